@@ -128,6 +128,11 @@ static void stats_row(const void* cur, const void* prev, int dtype, int64_t V, d
   *lse_out = lse;
   /* conf = max_v p_v = exp(m - lse) */
   *conf = exp(m - lse);
+  if (isnan(lse)) { /* no distribution: every statistic is NaN */
+    *entropy = NAN;
+    if (prev) *kl = NAN;
+    return;
+  }
   /* H = -sum_v p_v log p_v with log p_v = x_v - lse */
   double h = 0.0;
   for (int64_t v = 0; v < V; ++v) {

@@ -176,8 +176,10 @@ def test_non_finite_rows(oracle):
     assert np.isnan(out["conf"][0]) and np.isnan(out["entropy"][0]) and np.isnan(out["kl"][0])
     assert out["argmax"][0] == ref_arg0
     assert np.isnan(out["conf"][1]) and out["argmax"][1] == 0
+    assert np.isnan(out["entropy"][1]) and np.isnan(out["kl"][1]) and np.isnan(out["lse"][1])
     lp = torch.log_softmax(x[2, :100].double(), -1)
     assert abs(out["entropy"][2] - float(-(lp.exp() * lp).sum())) < 1e-13
     assert out["kl"][3] == float("inf")
     assert np.isnan(out["conf"][4]) and out["argmax"][4] == 5
     assert np.isnan(out["lse"][5]) and out["argmax"][5] == 0
+    assert np.isnan(out["entropy"][4]) and np.isnan(out["entropy"][5])
