@@ -1,0 +1,10 @@
+"""MI355X (gfx950) library for the per-denoising-step unmask decision of
+masked diffusion language models.
+
+The computation runs in hand-written HIP kernels behind the C ABI of
+``include/dlm.h`` (``libdlm.so`` in this directory); :mod:`.api` is the thin
+torch binding and :mod:`.synth` the seeded synthetic-input generators.
+"""
+from ._lib import DLMError  # noqa: F401
+from .api import (DEFAULTS, cap_select, dapd_select, dapd_workspace_bytes,  # noqa: F401
+                  depcap_boundary, fastdllm_select, step_stats)

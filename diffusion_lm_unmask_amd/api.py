@@ -1,0 +1,201 @@
+"""Thin torch-facing binding over the C ABI (include/dlm.h).
+
+Each function checks device, dtype, shape and contiguity, allocates its
+outputs as torch tensors on the input's device, and calls the library entry
+point of the same name on torch's current HIP stream.  Argument marshalling
+only: every step of the computation runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import DLMError
+
+DEFAULTS = dict(
+    fastdllm_tau=0.9, fastdllm_block=32,
+    depcap_lambda=1.2, depcap_l_min=8, depcap_l_max=128, depcap_radius=1, depcap_eps=1e-12,
+    cap_tau_low=0.8, cap_tau_high=0.95, cap_gamma=-16.0,
+    dapd_layer_frac=0.3, dapd_late_frac=0.5, dapd_late_tau=0.9,
+)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise DLMError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise DLMError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _vec(t, name, dtype, device):
+    _dev(t, name, dtype)
+    if t.device != device:
+        raise DLMError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise DLMError(f"{name} must be contiguous")
+    return t
+
+
+def _opt(t, name, dtype, device):
+    return None if t is None else _vec(t, name, dtype, device)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return _lib.BF16
+    if t.dtype == torch.float32:
+        return _lib.F32
+    raise DLMError(f"unsupported element type {t.dtype}")
+
+
+def _rows2d(logits, name):
+    _dev(logits, name)
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise DLMError(f"{name} must be 2-D [rows, ld] with unit column stride")
+    return logits.stride(0)
+
+
+def step_stats(logits: torch.Tensor, prev: torch.Tensor | None = None,
+               row_index: torch.Tensor | None = None, vocab: int | None = None):
+    """dlm_step_stats.  logits: [N, >=vocab] (bf16 or f32, unit column
+    stride); row_index: int64 rows to decide (default: all).  Returns a dict
+    with conf, argmax, entropy, kl (None without prev), lse."""
+    ld = _rows2d(logits, "logits")
+    dev = logits.device
+    vocab = logits.shape[1] if vocab is None else int(vocab)
+    if prev is not None:
+        _rows2d(prev, "prev")
+        if prev.dtype != logits.dtype or prev.stride(0) != ld or prev.shape != logits.shape:
+            raise DLMError("prev must match logits in dtype, shape and strides")
+    if row_index is None:
+        row_index = torch.arange(logits.shape[0], device=dev, dtype=torch.int64)
+    _vec(row_index, "row_index", torch.int64, dev)
+    n = row_index.numel()
+    f = dict(device=dev, dtype=torch.float32)
+    conf, ent, lse = torch.empty(n, **f), torch.empty(n, **f), torch.empty(n, **f)
+    kl = torch.empty(n, **f) if prev is not None else None
+    arg = torch.empty(n, device=dev, dtype=torch.int32)
+    st = _lib.lib().dlm_step_stats(logits.data_ptr(), _ptr(prev), _dtype_code(logits), vocab, ld,
+                                   row_index.data_ptr(), n, conf.data_ptr(), arg.data_ptr(),
+                                   ent.data_ptr(), _ptr(kl), lse.data_ptr(), _stream(logits))
+    _lib.check(st, "dlm_step_stats")
+    return {"conf": conf, "argmax": arg, "entropy": ent, "kl": kl, "lse": lse}
+
+
+def fastdllm_select(conf, seq_offsets, tau=DEFAULTS["fastdllm_tau"], eligible=None):
+    """dlm_fastdllm_select -> (commit u8 [rows], n_commit int32 [n_seq])."""
+    dev = _vec(conf, "conf", torch.float32, conf.device).device
+    _vec(seq_offsets, "seq_offsets", torch.int32, dev)
+    _opt(eligible, "eligible", torch.uint8, dev)
+    n_seq = seq_offsets.numel() - 1
+    commit = torch.empty(conf.numel(), device=dev, dtype=torch.uint8)
+    n_commit = torch.empty(max(n_seq, 0), device=dev, dtype=torch.int32)
+    st = _lib.lib().dlm_fastdllm_select(conf.data_ptr(), _ptr(eligible), seq_offsets.data_ptr(),
+                                        n_seq, float(tau), commit.data_ptr(), n_commit.data_ptr(),
+                                        _stream(conf))
+    _lib.check(st, "dlm_fastdllm_select")
+    return commit, n_commit
+
+
+def depcap_boundary(kl, entropy, seq_offsets, has_prev=None, lam=DEFAULTS["depcap_lambda"],
+                    l_min=DEFAULTS["depcap_l_min"], l_max=DEFAULTS["depcap_l_max"],
+                    radius=DEFAULTS["depcap_radius"], eps=DEFAULTS["depcap_eps"],
+                    want_score=True):
+    """dlm_depcap_boundary -> (block_len int32 [n_seq], score f32 [rows] or None)."""
+    dev = _vec(kl, "kl", torch.float32, kl.device).device
+    _vec(entropy, "entropy", torch.float32, dev)
+    _vec(seq_offsets, "seq_offsets", torch.int32, dev)
+    _opt(has_prev, "has_prev", torch.uint8, dev)
+    if entropy.numel() != kl.numel():
+        raise DLMError("kl and entropy must have the same length")
+    n_seq = seq_offsets.numel() - 1
+    block_len = torch.empty(max(n_seq, 0), device=dev, dtype=torch.int32)
+    score = torch.empty(kl.numel(), device=dev, dtype=torch.float32) if want_score else None
+    st = _lib.lib().dlm_depcap_boundary(kl.data_ptr(), entropy.data_ptr(), seq_offsets.data_ptr(),
+                                        n_seq, _ptr(has_prev), float(lam), int(l_min), int(l_max),
+                                        int(radius), float(eps), block_len.data_ptr(),
+                                        _ptr(score), _stream(kl))
+    _lib.check(st, "dlm_depcap_boundary")
+    return block_len, score
+
+
+def cap_select(logits, row_index, seq_offsets, conf, argmax, lse, eligible=None,
+               tau_low=DEFAULTS["cap_tau_low"], tau_high=DEFAULTS["cap_tau_high"],
+               gamma=DEFAULTS["cap_gamma"], k_max=64, vocab=None, want_cand=False,
+               want_dmat=False):
+    """dlm_cap_select -> dict(commit, n_commit, cand or None, dmat or None)."""
+    ld = _rows2d(logits, "logits")
+    dev = logits.device
+    vocab = logits.shape[1] if vocab is None else int(vocab)
+    _vec(row_index, "row_index", torch.int64, dev)
+    _vec(seq_offsets, "seq_offsets", torch.int32, dev)
+    _vec(conf, "conf", torch.float32, dev)
+    _vec(argmax, "argmax", torch.int32, dev)
+    _vec(lse, "lse", torch.float32, dev)
+    _opt(eligible, "eligible", torch.uint8, dev)
+    n_seq = seq_offsets.numel() - 1
+    k_max = int(k_max)
+    commit = torch.empty(conf.numel(), device=dev, dtype=torch.uint8)
+    n_commit = torch.empty(max(n_seq, 0), device=dev, dtype=torch.int32)
+    cand = torch.empty(max(n_seq, 0), k_max, device=dev, dtype=torch.int32) if want_cand else None
+    dmat = (torch.empty(max(n_seq, 0), k_max, k_max, device=dev, dtype=torch.float32)
+            if want_dmat else None)
+    st = _lib.lib().dlm_cap_select(logits.data_ptr(), _dtype_code(logits), vocab, ld,
+                                   row_index.data_ptr(), seq_offsets.data_ptr(), n_seq,
+                                   conf.data_ptr(), argmax.data_ptr(), lse.data_ptr(),
+                                   _ptr(eligible), float(tau_low), float(tau_high), float(gamma),
+                                   k_max, commit.data_ptr(), n_commit.data_ptr(), _ptr(cand),
+                                   _ptr(dmat), _stream(logits))
+    _lib.check(st, "dlm_cap_select")
+    return {"commit": commit, "n_commit": n_commit, "cand": cand, "dmat": dmat}
+
+
+def dapd_workspace_bytes(n_seq: int, m_max: int) -> int:
+    return int(_lib.lib().dlm_dapd_workspace_bytes(int(n_seq), int(m_max)))
+
+
+def dapd_select(attn, masked_pos, seq_offsets, conf, tau, m_max=None, workspace=None,
+                want_degree=False, want_key=False, want_sym=False):
+    """dlm_dapd_select.  attn: [B, n_lh, S, S] contiguous (bf16 or f32), the
+    maps to average; masked_pos int32 CSR by seq_offsets; conf f32 per row.
+    Returns dict(commit, n_commit, degree, key, sym)."""
+    _dev(attn, "attn")
+    if attn.dim() != 4 or not attn.is_contiguous() or attn.shape[2] != attn.shape[3]:
+        raise DLMError("attn must be a contiguous [B, n_lh, S, S] tensor")
+    dev = attn.device
+    B, n_lh, S, _ = attn.shape
+    _vec(masked_pos, "masked_pos", torch.int32, dev)
+    _vec(seq_offsets, "seq_offsets", torch.int32, dev)
+    _vec(conf, "conf", torch.float32, dev)
+    n_seq = seq_offsets.numel() - 1
+    if n_seq > B:
+        raise DLMError("more sequences than attention batches")
+    if m_max is None:
+        raise DLMError("m_max (an upper bound on masked positions per sequence) is required")
+    need = dapd_workspace_bytes(n_seq, m_max)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    _vec(workspace, "workspace", torch.uint8, dev)
+    n = conf.numel()
+    f = dict(device=dev, dtype=torch.float32)
+    commit = torch.empty(n, device=dev, dtype=torch.uint8)
+    n_commit = torch.empty(max(n_seq, 0), device=dev, dtype=torch.int32)
+    degree = torch.empty(n, **f) if want_degree else None
+    key = torch.empty(n, **f) if want_key else None
+    sym = torch.empty(max(n_seq, 0), m_max, m_max, **f) if want_sym else None
+    st = _lib.lib().dlm_dapd_select(attn.data_ptr(), _dtype_code(attn), n_lh, S, n_lh * S * S,
+                                    masked_pos.data_ptr(), seq_offsets.data_ptr(), n_seq,
+                                    int(m_max), conf.data_ptr(), float(tau), commit.data_ptr(),
+                                    n_commit.data_ptr(), _ptr(degree), _ptr(sym), _ptr(key),
+                                    workspace.data_ptr(), workspace.numel(), _stream(attn))
+    _lib.check(st, "dlm_dapd_select")
+    return {"commit": commit, "n_commit": n_commit, "degree": degree, "key": key, "sym": sym}

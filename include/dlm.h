@@ -1,0 +1,217 @@
+/*
+ * dlm.h — C ABI of the MI355X (gfx950) library for the per-denoising-step
+ * unmask decision of masked diffusion language models.
+ *
+ * One step of a masked diffusion LM produces a logits row for every masked
+ * position.  This library decides which of those positions to commit:
+ *   1. dlm_step_stats      — per-row confidence, argmax, entropy, KL to the
+ *                            previous step's row, log-normaliser (one pass
+ *                            over the vocabulary);
+ *   2. dlm_fastdllm_select — Fast-dLLM confidence threshold + top-1 fallback;
+ *   3. dlm_depcap_boundary — DepCap DepGA-Block boundary scan;
+ *   4. dlm_cap_select      — DepCap CAP-Decoding conflict-aware pick;
+ *   5. dlm_dapd_select     — DAPD attention graph + Welsh-Powell independent set.
+ *
+ * Conventions for every entry point
+ *   - Pointers marked (device) are device pointers owned by the caller; the
+ *     library never allocates, frees or retains memory and keeps no global
+ *     mutable state, so calls from several host threads are safe.
+ *   - Arguments are validated on the host before any HIP call.  On an
+ *     invalid argument nothing is enqueued and DLM_ERR_ARG or
+ *     DLM_ERR_UNSUPPORTED is returned.  Device-side data (offsets, indices)
+ *     cannot be read by the host; a violated device-side precondition is
+ *     reported per sequence where stated (n_commit[b] = -1), never by an
+ *     out-of-bounds access when the documented bounds are respected.
+ *   - Kernels are enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and the call returns without synchronising.  Asynchronous
+ *     device faults surface at the caller's next synchronisation.
+ *   - Outputs are fully overwritten (rows that are not eligible get 0).
+ *   - Rows of a sequence are given in CSR form by seq_offsets (device int32,
+ *     n_seq+1 entries, non-decreasing, seq_offsets[0] = 0), in position order.
+ *   - A NULL `eligible` means every row is eligible.
+ *
+ * Sources (page title, section) are cited per entry point:
+ *   [DepCap] "DepCap: Adaptive Block-Wise Parallel Decoding for Efficient
+ *            Diffusion LM Inference" (summary of arXiv 2604.15750);
+ *   [DAPD]   "DAPD: Dependency-Aware Parallel Decoding via Attention for
+ *            Diffusion LLMs" (ICML 2026 paper note);
+ *   [FastR]  "Fast-dLLM: Training-Free Acceleration of Diffusion LLMs via KV
+ *            Cache and Parallel Decoding" (review);
+ *   [FastN]  "Fast-dLLM: Training-free Acceleration of Diffusion LLM by
+ *            Enabling KV Cache and Parallel Decoding" (notes).
+ */
+#ifndef DLM_H
+#define DLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define DLM_OK 0
+#define DLM_ERR_ARG 1         /* NULL required pointer, size <= 0, NaN threshold, ...   */
+#define DLM_ERR_UNSUPPORTED 2 /* unknown dtype, a size above a documented limit         */
+#define DLM_ERR_HIP 3         /* a kernel launch failed (hipGetLastError)               */
+
+/* logits / attention element types */
+#define DLM_BF16 0
+#define DLM_F32 1
+
+/* limits */
+#define DLM_MAX_VOCAB 2147483647LL /* vocab < 2^31                                       */
+#define DLM_MAX_WINDOW 1024        /* DepCap l_max                                        */
+#define DLM_MAX_SEQ_ROWS 1024      /* CAP rows per sequence, DAPD masked positions (m_max)*/
+#define DLM_MAX_KMAX 128           /* CAP candidate cap                                   */
+
+/* default parameters quoted by the pages */
+#define DLM_FASTDLLM_TAU 0.9f      /* [FastR, Method]: default threshold                   */
+#define DLM_FASTDLLM_BLOCK 32      /* [FastN, Technical details]: block size               */
+#define DLM_DEPCAP_LAMBDA 1.2      /* [DepCap, Experiments]: defaults                      */
+#define DLM_DEPCAP_L_MIN 8
+#define DLM_DEPCAP_L_MAX 128
+#define DLM_DEPCAP_RADIUS 1        /* smoothing radius (a reading: the pages give none)   */
+#define DLM_DEPCAP_EPS 1e-12       /* normalisation guard (a reading)                     */
+#define DLM_CAP_TAU_LOW 0.8f       /* [DepCap, Experiments; AI Executive Summary]          */
+#define DLM_CAP_TAU_HIGH 0.95f
+#define DLM_CAP_GAMMA (-16.0f)
+#define DLM_DAPD_LAYER_FRAC 0.3    /* [DAPD, overall framework]: last ~30% of layers       */
+#define DLM_DAPD_LATE_FRAC 0.5     /* [DAPD, key design 3]: late-stage switch point       */
+#define DLM_DAPD_LATE_TAU 0.9f     /* [DAPD, key design 3]: late-stage threshold          */
+
+/*
+ * dlm_step_stats — [DepCap, Methodology] H_k = H(p_curr^k) and
+ * I_k = KL(p_curr^k || p_prev^k); [DepCap, Methodology] and [FastR, Method]
+ * confidence c = max_v p(v) and the argmax token.
+ *
+ * For r in [0, n_rows): row = logits + row_index[r]*ld elements (and the
+ * same offset into prev_logits).  With p = softmax(row) (natural log,
+ * temperature 1):
+ *   argmax[r]  = lowest index attaining the maximum over non-NaN entries
+ *                (0 if the row has none)
+ *   lse[r]     = log sum_v exp(row_v)
+ *   conf[r]    = max_v p_v = exp(max - lse)
+ *   entropy[r] = -sum_v p_v log p_v                       (0 log 0 = 0)
+ *   kl[r]      = sum_v p_v (log p_v - log q_v), q = softmax(prev row);
+ *                +inf if some p_v > 0 has q_v = 0.
+ * A row with a NaN or +inf entry, or with every entry -inf, gives NaN conf,
+ * entropy, kl and lse.
+ *
+ * logits, prev_logits (device): dtype elements (DLM_BF16 or DLM_F32), base
+ *   aligned to the element size; prev_logits may be NULL (then kl must be
+ *   NULL too).  Rows are streamed at full speed when both bases are 16-byte
+ *   aligned and ld*element_size is a multiple of 16; otherwise a slower
+ *   element-wise path is used.
+ * vocab: 1 <= vocab < 2^31; ld >= vocab.
+ * row_index (device int64 [n_rows]); n_rows >= 1.
+ * conf, entropy, kl, lse (device f32 [n_rows]); argmax (device int32 [n_rows]).
+ * Floating point: fp32 element arithmetic with fp64 cross-lane combination.
+ */
+int dlm_step_stats(const void* logits, const void* prev_logits, int dtype, int64_t vocab,
+                   int64_t ld, const int64_t* row_index, int64_t n_rows, float* conf,
+                   int32_t* argmax, float* entropy, float* kl, float* lse, void* stream);
+
+/*
+ * dlm_fastdllm_select — [FastR, Method]; [FastN, Key ideas, Technical details]:
+ * commit every eligible row whose confidence exceeds tau; if none does,
+ * commit the single highest-confidence eligible row (progress guarantee).
+ *   commit[r] = eligible[r] && conf[r] > tau   (strict; NaN never commits)
+ *   fallback ties go to the lowest row of the sequence.
+ * conf (device f32 [rows]); eligible (device u8 [rows] or NULL);
+ * seq_offsets (device int32 [n_seq+1]); n_seq >= 1; tau not NaN.
+ * commit (device u8 [rows]); n_commit (device int32 [n_seq]).
+ */
+int dlm_fastdllm_select(const float* conf, const uint8_t* eligible, const int32_t* seq_offsets,
+                        int32_t n_seq, float tau, uint8_t* commit, int32_t* n_commit,
+                        void* stream);
+
+/*
+ * dlm_depcap_boundary — [DepCap, Methodology bullets 1-3; Technical
+ * Contribution]: over the window W_b = min(l_max, rows of sequence b) of
+ * future positions right after the last decoded block, smooth and locally
+ * normalise I_k (= kl) and H_k (= entropy), form S_k = I~_k - lambda*H~_k,
+ * stop before the first S_k < 0 and clip the length to [l_min, W_b]; use
+ * l_min (clipped to W_b) on cold start (has_prev[b] == 0).
+ * Readings (the pages give no formula): I-bar_k = mean of I_j over
+ * j in [k-r, k+r] clipped to the window; I~_k = I-bar_k / (mean_k I-bar + eps);
+ * the same for H.  S_k is computed in fp64, rounded to f32, and the
+ * decision is taken on the f32 value (NaN is not negative).
+ * kl, entropy (device f32 [rows]); seq_offsets (device int32 [n_seq+1]);
+ * has_prev (device u8 [n_seq] or NULL = all warm); 0 <= l_min <= l_max <= 1024;
+ * smooth_radius >= 0; eps >= 0; lambda, eps not NaN.
+ * block_len (device int32 [n_seq]); score (device f32 [rows] or NULL):
+ * S_k for the first W_b rows of a warm sequence, NaN elsewhere.
+ */
+int dlm_depcap_boundary(const float* kl, const float* entropy, const int32_t* seq_offsets,
+                        int32_t n_seq, const uint8_t* has_prev, double lambda, int32_t l_min,
+                        int32_t l_max, int32_t smooth_radius, double eps, int32_t* block_len,
+                        float* score, void* stream);
+
+/*
+ * dlm_cap_select — [DepCap, Methodology bullets 4-6; Technical Contribution;
+ * AI Executive Summary]: candidate pool P = {eligible rows with conf >= tau_low},
+ * kept to the first k_max in (conf desc, row asc) order; if P is empty commit
+ * the top-1 eligible row.  Otherwise
+ *   D_ab = (logit_a[yhat_b] - lse_a) + (logit_b[yhat_a] - lse_b)
+ * (log p_a(yhat_b) + log p_b(yhat_a)), a conflict is D_ab > gamma (a reading);
+ * rows with conf > tau_high are committed first, then the rest in priority
+ * order are added when they conflict with nothing chosen.
+ * logits (device, dtype, same layout as dlm_step_stats) and row_index: only
+ * gathered at (candidate row, candidate argmax).  conf, argmax, lse: the
+ * outputs of dlm_step_stats for the same rows.
+ * Limits: rows per sequence <= 1024 (else n_commit[b] = -1 and no commit);
+ * 1 <= k_max <= 128.
+ * commit (device u8 [rows]); n_commit (device int32 [n_seq]);
+ * cand (device int32 [n_seq*k_max] or NULL): candidate rows in priority
+ * order, -1 pad; dmat (device f32 [n_seq*k_max*k_max] or NULL): D in
+ * candidate order, NaN on the diagonal and pad.
+ */
+int dlm_cap_select(const void* logits, int dtype, int64_t vocab, int64_t ld,
+                   const int64_t* row_index, const int32_t* seq_offsets, int32_t n_seq,
+                   const float* conf, const int32_t* argmax, const float* lse,
+                   const uint8_t* eligible, float tau_low, float tau_high, float gamma,
+                   int32_t k_max, uint8_t* commit, int32_t* n_commit, int32_t* cand,
+                   float* dmat, void* stream);
+
+/*
+ * dlm_dapd_workspace_bytes — device workspace that dlm_dapd_select needs for
+ * n_seq sequences of at most m_max masked positions (two fp32 m_max x m_max
+ * matrices per sequence).  Returns 0 for invalid sizes.
+ */
+size_t dlm_dapd_workspace_bytes(int32_t n_seq, int32_t m_max);
+
+/*
+ * dlm_dapd_select — [DAPD, overall framework; key designs 1-2]:
+ *   a_ij   = mean over the n_lh maps of attn[b][lh][pos_i][pos_j]
+ *            (the caller passes the maps of the last ~30% of layers, all heads;
+ *            probabilities used as given, no renormalisation)
+ *   s_ij   = (a_ij + a_ji)/2 ; edge (i,j) iff i != j and s_ij > tau
+ *   d~_i   = sum_{j != i} s_ij ; key_i = f32(f32(d~_i) * conf_i)
+ *   scan nodes by (key desc, position asc) and add each node with no edge
+ *   into the chosen set (Welsh-Powell order); NaN keys are never chosen.
+ * attn (device, dtype): sequence b's maps start at attn + b*batch_stride
+ * elements; map lh is the S x S row-major matrix at offset lh*S*S.
+ * masked_pos (device int32 [rows], CSR by seq_offsets): positions in [0, S).
+ * conf (device f32 [rows]) in the same row order.  1 <= m_max <= 1024 bounds
+ * the masked positions per sequence (a longer sequence gets n_commit = -1).
+ * workspace (device, >= dlm_dapd_workspace_bytes(n_seq, m_max) bytes, 256-byte
+ * aligned): scratch, overwritten.
+ * commit (device u8 [rows]); n_commit (device int32 [n_seq]); degree, key
+ * (device f32 [rows] or NULL); sym (device f32 [n_seq*m_max*m_max] or NULL):
+ * s_ij, NaN pad.
+ */
+int dlm_dapd_select(const void* attn, int dtype, int32_t n_lh, int64_t S, int64_t batch_stride,
+                    const int32_t* masked_pos, const int32_t* seq_offsets, int32_t n_seq,
+                    int32_t m_max, const float* conf, float tau, uint8_t* commit,
+                    int32_t* n_commit, float* degree, float* sym, float* key, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* dlm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLM_H */

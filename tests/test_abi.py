@@ -1,0 +1,106 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/dlm.h, and rejects bad arguments on the host (these
+calls return before any HIP call, so nothing is enqueued)."""
+import ctypes
+import math
+
+import pytest
+
+from diffusion_lm_unmask_amd import _lib
+
+FAKE = 0x100000  # a non-NULL, aligned pointer value; never dereferenced here
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _lib.header_symbols()
+    assert set(names) == set(_lib.SIGNATURES)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s, text in ((0, b"ok"), (1, b"invalid argument"), (3, b"HIP kernel launch failed")):
+        assert L.dlm_status_string(s) == text
+    assert L.dlm_status_string(99) == b"unknown status"
+
+
+def test_step_stats_validation(L):
+    f = L.dlm_step_stats
+    args = [FAKE, None, _lib.BF16, 1000, 1000, FAKE, 4, FAKE, FAKE, FAKE, None, FAKE, None]
+    bad = list(args)
+    bad[0] = None
+    assert f(*bad) == _lib.ERR_ARG                      # NULL logits
+    bad = list(args)
+    bad[2] = 5
+    assert f(*bad) == _lib.ERR_UNSUPPORTED              # unknown dtype
+    bad = list(args)
+    bad[4] = 999
+    assert f(*bad) == _lib.ERR_ARG                      # ld < vocab
+    bad = list(args)
+    bad[6] = 0
+    assert f(*bad) == _lib.ERR_ARG                      # no rows
+    bad = list(args)
+    bad[1] = FAKE
+    assert f(*bad) == _lib.ERR_ARG                      # prev without kl
+    bad = list(args)
+    bad[0] = FAKE + 1
+    assert f(*bad) == _lib.ERR_ARG                      # misaligned bf16 base
+    bad = list(args)
+    bad[3] = 2**31
+    bad[4] = 2**31
+    assert f(*bad) == _lib.ERR_UNSUPPORTED              # vocab >= 2^31
+
+
+def test_rule_validation(L):
+    assert L.dlm_fastdllm_select(FAKE, None, FAKE, 1, math.nan, FAKE, FAKE, None) == _lib.ERR_ARG
+    assert L.dlm_fastdllm_select(None, None, FAKE, 1, 0.9, FAKE, FAKE, None) == _lib.ERR_ARG
+    assert L.dlm_fastdllm_select(FAKE, None, FAKE, 0, 0.9, FAKE, FAKE, None) == _lib.ERR_ARG
+    d = L.dlm_depcap_boundary
+    ok = [FAKE, FAKE, FAKE, 1, None, 1.2, 8, 128, 1, 1e-12, FAKE, None, None]
+    for i, v, code in ((6, 9, _lib.ERR_ARG), (7, 4, _lib.ERR_ARG), (7, 2048, _lib.ERR_UNSUPPORTED),
+                       (8, -1, _lib.ERR_ARG), (5, math.nan, _lib.ERR_ARG), (9, -1.0, _lib.ERR_ARG),
+                       (10, None, _lib.ERR_ARG)):
+        bad = list(ok)
+        bad[7] = 128
+        bad[i] = v
+        if i == 6:
+            bad[7] = 8           # l_min > l_max
+        assert d(*bad) == code, (i, v)
+    c = L.dlm_cap_select
+    ok = [FAKE, _lib.BF16, 1000, 1000, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, 0.8, 0.95, -16.0, 64,
+          FAKE, FAKE, None, None, None]
+    for i, v, code in ((14, 129, _lib.ERR_UNSUPPORTED), (14, 0, _lib.ERR_ARG),
+                       (1, 3, _lib.ERR_UNSUPPORTED), (13, math.nan, _lib.ERR_ARG),
+                       (9, None, _lib.ERR_ARG), (6, 0, _lib.ERR_ARG)):
+        bad = list(ok)
+        bad[i] = v
+        assert c(*bad) == code, (i, v)
+
+
+def test_dapd_validation(L):
+    assert L.dlm_dapd_workspace_bytes(8, 256) == 2 * 8 * 256 * 256 * 4
+    assert L.dlm_dapd_workspace_bytes(1, 1025) == 0
+    assert L.dlm_dapd_workspace_bytes(0, 10) == 0
+    f = L.dlm_dapd_select
+    need = L.dlm_dapd_workspace_bytes(2, 64)
+    ok = [FAKE, _lib.BF16, 4, 96, 4 * 96 * 96, FAKE, FAKE, 2, 64, FAKE, 0.01, FAKE, FAKE, None,
+          None, None, FAKE, need, None]
+    for i, v, code in ((17, need - 1, _lib.ERR_ARG), (8, 1025, _lib.ERR_UNSUPPORTED),
+                       (10, math.nan, _lib.ERR_ARG), (4, 10, _lib.ERR_ARG),
+                       (16, None, _lib.ERR_ARG), (16, FAKE + 4, _lib.ERR_ARG),
+                       (1, 9, _lib.ERR_UNSUPPORTED), (2, 0, _lib.ERR_ARG)):
+        bad = list(ok)
+        bad[i] = v
+        assert f(*bad) == code, (i, v)
+
+
+def test_binding_fails_loudly_without_device_tensors():
+    torch = pytest.importorskip("torch")
+    import diffusion_lm_unmask_amd as d
+    with pytest.raises(d.DLMError):
+        d.step_stats(torch.zeros(2, 8))             # host tensor: refused, no CPU fallback

@@ -1,0 +1,328 @@
+"""GPU parity of the four selection rules (marked gpu).
+
+Each rule is checked decision-only (oracle rule on the GPU's exported fp32
+scores must equal the GPU decision bit for bit) and end-to-end (GPU decisions
+from GPU statistics vs oracle decisions from oracle statistics, differences
+allowed only at near-threshold quantities, counted as flagged).  Exported
+scores (S_k, D_ij, s_ij, degree) are compared within 1e-5 of the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _parity import Flags, assert_close, f64, host, near_any, near_tie
+from diffusion_lm_unmask_amd import api, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+# The stress workload's rule tests use its first 4 sequences (same per-row
+# launch configuration as the full 64); the full 64-sequence launch is
+# compared on sampled sequences in test_cap_stress_sampled_sequences.
+BATCH = {"stress": 4}
+
+
+def _stats(name, variant="peak", **kw):
+    kw.setdefault("batch", BATCH.get(name))
+    cur, prev, so, ri = synth.logits(name, DEV, variant=variant, **kw)
+    g = api.step_stats(cur, prev)
+    torch.cuda.synchronize()
+    o = oracle.step_stats(host(cur), host(prev) if prev is not None else None)
+    return cur, prev, so, ri, g, o
+
+
+# ---------------------------------------------------------------- Fast-dLLM
+
+def _fastdllm_case(conf_g, conf_o, so, tau, eligible, tag):
+    commit, n = api.fastdllm_select(conf_g, so, tau, eligible)
+    torch.cuda.synchronize()
+    el = None if eligible is None else host(eligible).numpy()
+    so_h = host(so).numpy()
+    dec_only, _ = oracle.fastdllm_select(f64(conf_g), so_h, np.float32(tau), el)
+    assert np.array_equal(host(commit).numpy(), dec_only), f"{tag}: decision-only"
+    e2e, n_o = oracle.fastdllm_select(conf_o, so_h, np.float32(tau), el)
+    fl = Flags(f"fastdllm {tag}")
+    for b in range(len(so_h) - 1):
+        lo, hi = so_h[b], so_h[b + 1]
+        same = np.array_equal(host(commit).numpy()[lo:hi], e2e[lo:hi])
+        elig = slice(lo, hi) if el is None else np.where(el[lo:hi])[0] + lo
+        c = conf_o[elig]
+        fl.check(same, True, near_any(c, [float(np.float32(tau))]) or near_tie(c), f"seq {b}")
+    fl.report()
+    per_seq = [int(dec_only[so_h[b]:so_h[b + 1]].sum()) for b in range(len(so_h) - 1)]
+    assert host(n).tolist() == per_seq
+
+
+@pytest.mark.parametrize("name", ["tiny", "llada", "stress"])
+def test_fastdllm(name):
+    cur, prev, so, ri, g, o = _stats(name)
+    n = cur.shape[0]
+    for tau in (0.9, 0.5, 0.99, 1.5):
+        el = torch.zeros(n, dtype=torch.uint8, device=DEV)
+        rows = synth.SPECS[name].rows
+        for b in range(so.numel() - 1):                    # block 0 of every sequence
+            el[b * rows:b * rows + 32] = 1
+        _fastdllm_case(g["conf"], o["conf"], so, tau, el, f"{name} tau={tau} block0")
+        _fastdllm_case(g["conf"], o["conf"], so, tau, None, f"{name} tau={tau} all")
+
+
+def test_fastdllm_edges():
+    conf = torch.tensor([0.1, float("nan"), 0.95, 0.2, 0.2, float("nan")], device=DEV)
+    so = torch.tensor([0, 0, 2, 5, 6, 6], device=DEV, dtype=torch.int32)
+    commit, n = api.fastdllm_select(conf, so, 0.9)
+    # seq 0 empty; seq 1 {0.1, NaN} falls back to row 0; seq 2 commits 0.95;
+    # seq 3 is only NaN (nothing); seq 4 empty
+    assert host(commit).tolist() == [1, 0, 1, 0, 0, 0] and host(n).tolist() == [0, 1, 1, 0, 0]
+    el = torch.tensor([1, 1, 0, 1, 1, 1], device=DEV, dtype=torch.uint8)
+    commit, n = api.fastdllm_select(conf, so, 0.9, el)
+    assert host(commit).tolist() == [1, 0, 0, 1, 0, 0] and host(n).tolist() == [0, 1, 1, 0, 0]
+
+
+# --------------------------------------------------------------- DepGA-Block
+
+def _depcap_case(g, o, so, R, tag, has_prev=None):
+    kl_g, h_g = g["kl"], g["entropy"]
+    L_g, S_g = api.depcap_boundary(kl_g, h_g, so, has_prev=has_prev, lam=R["lam"],
+                                   l_min=R["l_min"], l_max=R["l_max"])
+    torch.cuda.synchronize()
+    so_h = host(so).numpy()
+    hp = None if has_prev is None else host(has_prev).numpy()
+    # scores from the GPU's own KL/H, in fp64: within 1e-5
+    S_from_g = oracle.depcap_scores(f64(kl_g), f64(h_g), so_h, R["l_max"], R["lam"], 1, 1e-12, hp)
+    assert_close(S_g, S_from_g, f"{tag} S (gpu stats)")
+    # decision-only: oracle's boundary rule on the GPU's f32 scores
+    dec = oracle.depcap_decide(f64(S_g), so_h, R["l_max"], R["l_min"], hp)
+    assert np.array_equal(host(L_g).numpy(), dec), f"{tag}: decision-only"
+    # end-to-end
+    L_o, S_o = oracle.depcap_boundary(o["kl"], o["entropy"], so_h, R["l_max"], R["l_min"],
+                                      R["lam"], 1, 1e-12, hp)
+    w = assert_close(S_g, S_o, f"{tag} S (oracle stats)")
+    print(f"[depcap] {tag} S max err {w:.2e}")
+    fl = Flags(f"depcap {tag}")
+    L_gh = host(L_g).numpy()
+    for b in range(len(so_h) - 1):
+        lo = so_h[b]
+        kk = max(L_gh[b], L_o[b]) + 1
+        fl.check(L_gh[b] == L_o[b], True, near_any(S_o[lo:lo + kk], [0.0]), f"seq {b}")
+    fl.report()
+    return L_g
+
+
+@pytest.mark.parametrize("name", ["tiny", "llada", "stress"])
+def test_depcap(name):
+    cur, prev, so, ri, g, o = _stats(name)
+    R = synth.RULES[name]
+    _depcap_case(g, o, so, R, name)
+    B = so.numel() - 1
+    hp = torch.tensor([(b + 1) % 3 != 0 for b in range(B)], device=DEV, dtype=torch.uint8)
+    _depcap_case(g, o, so, R, name + " mixed-cold", has_prev=hp)
+    for lam, lmin in ((0.0, 4), (3.0, 16), (1.2, 0)):
+        _depcap_case(g, o, so, dict(R, lam=lam, l_min=lmin), f"{name} lam={lam} lmin={lmin}")
+
+
+def test_depcap_edges():
+    kl = torch.tensor([0.1, 0.2, 0.0, 0.3, 0.4], device=DEV)
+    h = torch.tensor([1.0, 0.5, 2.0, 1.0, 0.1], device=DEV)
+    so = torch.tensor([0, 0, 3, 5], device=DEV, dtype=torch.int32)    # empty, 3 rows, 2 rows
+    L, S = api.depcap_boundary(kl, h, so, lam=1.2, l_min=4, l_max=128)
+    assert host(L).tolist()[0] == 0
+    ref, Sref = oracle.depcap_boundary(f64(kl), f64(h), host(so).numpy(), 128, 4, 1.2)
+    assert host(L).tolist() == list(ref)
+    assert_close(S, Sref, "edge S")
+
+
+# -------------------------------------------------------------- CAP-Decoding
+
+def _cap_case(cur, ri, so, g, o, R, eligible, tag):
+    out = api.cap_select(cur, ri, so, g["conf"], g["argmax"], g["lse"], eligible,
+                         tau_low=R["tau_low"], tau_high=R["tau_high"], gamma=R["gamma"],
+                         k_max=R["k_max"], want_cand=True, want_dmat=True)
+    torch.cuda.synchronize()
+    so_h = host(so).numpy()
+    el = None if eligible is None else host(eligible).numpy()
+    conf_g = f64(g["conf"])
+    commit_g = host(out["commit"]).numpy()
+    cand_g = host(out["cand"]).numpy()
+    dmat_g = f64(out["dmat"])
+    K = R["k_max"]
+    t_low, t_high = float(np.float32(R["tau_low"])), float(np.float32(R["tau_high"]))
+    gam = float(np.float32(R["gamma"]))
+    o_all = oracle.cap_select(host(cur), host(ri).numpy(), so_h, o["conf"], o["argmax"], o["lse"],
+                              t_low, t_high, gam, K, eligible=el)
+    fl = Flags(f"cap {tag}")
+    n_cmp = 0
+    worst = 0.0
+    for b in range(len(so_h) - 1):
+        lo, hi = so_h[b], so_h[b + 1]
+        e = None if el is None else el[lo:hi]
+        # decision-only: pool + cap from GPU conf, greedy on GPU D
+        pool, fb = oracle.cap_pool(conf_g[lo:hi], t_low, K, e)
+        nc = len(pool)
+        assert list(cand_g[b][:nc]) == list(pool + lo) and np.all(cand_g[b][nc:] == -1), \
+            f"{tag} seq {b}: candidate list"
+        if nc == 0:
+            want = np.zeros(hi - lo, np.uint8)
+            if fb >= 0:
+                want[fb] = 1
+        else:
+            take = oracle.cap_greedy(conf_g[lo:hi][pool], dmat_g[b][:nc, :nc], t_high, gam)
+            want = np.zeros(hi - lo, np.uint8)
+            want[pool[take == 1]] = 1
+            D = dmat_g[b][:nc, :nc]
+            assert np.array_equal(np.nan_to_num(D, nan=7.0), np.nan_to_num(D.T, nan=7.0)), \
+                "D not bit-symmetric"
+        dec_ok = np.array_equal(commit_g[lo:hi], want)
+        assert dec_ok, f"{tag} seq {b}: decision-only"
+        # D within 1e-5 of the oracle's D where the candidate lists agree
+        cand_o = o_all["cand"][b]
+        if nc and np.array_equal(cand_o[:nc], cand_g[b][:nc]):
+            worst = max(worst, assert_close(dmat_g[b][:nc, :nc], o_all["dmat"][b][:nc, :nc],
+                                            f"{tag} D seq {b}"))
+            n_cmp += 1
+        same = np.array_equal(commit_g[lo:hi], o_all["commit"][lo:hi])
+        co = o["conf"][lo:hi] if e is None else o["conf"][lo:hi][e == 1]
+        Do = o_all["dmat"][b]
+        near = (near_any(co, [t_low, t_high]) or near_tie(co[co >= t_low - 1e-5]) or
+                near_any(Do[np.isfinite(Do)], [gam]))
+        fl.check(same, dec_ok, near, f"seq {b}")
+    fl.report()
+    print(f"[cap] {tag}: D compared on {n_cmp} sequences, max err {worst:.2e}")
+    return out
+
+
+@pytest.mark.parametrize("name,variant", [("tiny", "peak"), ("llada", "peak"), ("llada", "cov"),
+                                          ("dream", "peak"), ("dream", "cov"), ("dream", "lit")])
+def test_cap(name, variant):
+    cur, prev, so, ri, g, o = _stats(name, variant)
+    R = dict(synth.RULES[name])
+    R.setdefault("k_max", 64)
+    el = None
+    if "cap_block" in R:
+        el = torch.zeros(cur.shape[0], dtype=torch.uint8, device=DEV)
+        el[R["cap_block"][0]:R["cap_block"][1]] = 1
+    _cap_case(cur, ri, so, g, o, R, el, f"{name}/{variant}")
+    if name == "llada":   # the whole generation as one pool, cap binding
+        _cap_case(cur, ri, so, g, o, dict(R, k_max=128, tau_low=0.5), None, f"{name}/{variant} all")
+        _cap_case(cur, ri, so, g, o, dict(R, k_max=16, tau_high=1.5), None, f"{name}/{variant} k16")
+
+
+def test_cap_stress_sampled_sequences():
+    spec = synth.SPECS["stress"]
+    R = synth.RULES["stress"]
+    cur, prev, so, ri = synth.logits("stress", DEV)
+    g = api.step_stats(cur, prev)
+    out = api.cap_select(cur, ri, so, g["conf"], g["argmax"], g["lse"], tau_low=R["tau_low"],
+                         tau_high=R["tau_high"], gamma=R["gamma"], k_max=R["k_max"],
+                         want_cand=True, want_dmat=True)
+    torch.cuda.synchronize()
+    for b in (0, 17, 63):                              # sampled sequences, full launch
+        lo, hi = b * spec.rows, (b + 1) * spec.rows
+        sub = cur[lo:hi]
+        o = oracle.step_stats(host(sub), host(prev[lo:hi]))
+        so1 = torch.tensor([0, spec.rows], device=DEV, dtype=torch.int32)
+        gsub = {k: (None if v is None else v[lo:hi].contiguous()) for k, v in g.items()}
+        ri1 = torch.arange(spec.rows, device=DEV, dtype=torch.int64)
+        res = _cap_case(sub.contiguous(), ri1, so1, gsub, o, R, None, f"stress seq {b}")
+        assert torch.equal(res["commit"], out["commit"][lo:hi])
+        assert torch.equal(res["cand"][0][res["cand"][0] >= 0] + lo,
+                           out["cand"][b][out["cand"][b] >= 0])
+        n_pool = int((g["conf"][lo:hi] >= R["tau_low"]).sum())
+        print(f"[cap] stress seq {b}: pool {n_pool}, committed {int(out['n_commit'][b])}")
+
+
+def test_cap_edges():
+    V = 64
+    x = torch.randn(6, V, device=DEV).to(torch.bfloat16)
+    x[0, 3] = 40.0
+    ri = torch.arange(6, device=DEV, dtype=torch.int64)
+    g = api.step_stats(x)
+    so = torch.tensor([0, 0, 2, 6], device=DEV, dtype=torch.int32)
+    el = torch.tensor([1, 1, 0, 0, 0, 0], device=DEV, dtype=torch.uint8)
+    out = api.cap_select(x, ri, so, g["conf"], g["argmax"], g["lse"], el, k_max=4,
+                         want_cand=True, want_dmat=True)
+    n = host(out["n_commit"]).tolist()
+    assert n[0] == 0 and n[2] == 0 and n[1] >= 1
+    assert host(out["commit"]).tolist()[2:] == [0, 0, 0, 0]
+    # a sequence above the 1024-row limit is reported, not processed
+    big = torch.randn(1100, V, device=DEV).to(torch.bfloat16)
+    gb = api.step_stats(big)
+    so2 = torch.tensor([0, 1100], device=DEV, dtype=torch.int32)
+    out = api.cap_select(big, torch.arange(1100, device=DEV), so2, gb["conf"], gb["argmax"],
+                         gb["lse"], k_max=8)
+    assert host(out["n_commit"]).tolist() == [-1] and int(out["commit"].sum()) == 0
+
+
+# ----------------------------------------------------------------------- DAPD
+
+def _dapd_case(attn, pos, so, conf_g, conf_o, tau, m_max, tag):
+    out = api.dapd_select(attn, pos, so, conf_g, tau, m_max=m_max, want_degree=True,
+                          want_key=True, want_sym=True)
+    torch.cuda.synchronize()
+    so_h = host(so).numpy()
+    ref = oracle.dapd_select(host(attn), host(pos).numpy(), so_h, conf_o, float(np.float32(tau)),
+                             m_max=m_max)
+    ws = assert_close(out["sym"], ref["sym"], f"{tag} sym")
+    wd = assert_close(out["degree"], ref["degree"], f"{tag} degree")
+    print(f"[dapd] {tag}: sym err {ws:.2e} degree err {wd:.2e}")
+    sym = f64(out["sym"])
+    key = f64(out["key"])
+    commit = host(out["commit"]).numpy()
+    fl = Flags(f"dapd {tag}")
+    t32 = float(np.float32(tau))
+    n_edges = 0
+    for b in range(len(so_h) - 1):
+        lo, hi = so_h[b], so_h[b + 1]
+        M = hi - lo
+        s = sym[b][:M, :M]
+        assert np.array_equal(np.nan_to_num(s), np.nan_to_num(s.T)), "s not bit-symmetric"
+        take = oracle.dapd_greedy(s, t32, key[lo:hi])
+        dec_ok = np.array_equal(commit[lo:hi], take)
+        assert dec_ok, f"{tag} seq {b}: decision-only"
+        so_ = ref["sym"][b][:M, :M]
+        n_edges += int(((so_ > t32) & ~np.eye(M, dtype=bool)).sum()) // 2
+        near = near_any(so_[~np.eye(M, dtype=bool)], [t32]) or near_tie(ref["key"][lo:hi])
+        fl.check(np.array_equal(commit[lo:hi], ref["commit"][lo:hi]), dec_ok, near, f"seq {b}")
+        assert int(host(out["n_commit"])[b]) == int(commit[lo:hi].sum())
+    fl.report()
+    print(f"[dapd] {tag}: {n_edges} edges, {int(commit.sum())} committed")
+    return out
+
+
+@pytest.mark.parametrize("tau", [0.01, 0.03, 0.05])
+def test_dapd_tiny(tau):
+    cur, prev, so, ri, g, o = _stats("tiny")
+    attn = synth.attention("tiny", DEV)
+    pos, offs = synth.gen_positions("tiny", DEV)
+    _dapd_case(attn, pos, offs, g["conf"], o["conf"], tau, 32, f"tiny tau={tau}")
+
+
+@pytest.mark.parametrize("variant", ["peak", "cov"])
+def test_dapd_full(variant):
+    spec = synth.SPECS["dapd"]
+    cur, prev, so, ri, g, o = _stats("dapd")
+    pos, offs = synth.gen_positions("dapd", DEV)
+    attn = synth.attention("dapd", DEV, variant=variant, masked_pos=pos[:spec.rows])
+    _dapd_case(attn, pos, offs, g["conf"], o["conf"], 0.01, 256, f"dapd/{variant}")
+
+
+def test_dapd_scattered_positions_and_edges():
+    spec = synth.Spec("scat", 11, 3, 40, 512, torch.bfloat16, 2.0, 0.6, 12.0, None,
+                      n_lh=6, seq_len=100, attn_sigma=3.0)
+    cur, prev, so, ri = synth.logits(spec, DEV)
+    g = api.step_stats(cur)
+    o = oracle.step_stats(host(cur))
+    gen = torch.Generator().manual_seed(3)
+    pos = torch.cat([torch.randperm(100, generator=gen)[:40].sort().values for _ in range(3)])
+    pos = pos.to(device=DEV, dtype=torch.int32)
+    attn = synth.attention(spec, DEV)
+    # sequence 1 empty, sequence 2 short, m_max not a multiple of 64 or 8
+    so2 = torch.tensor([0, 40, 40, 77], device=DEV, dtype=torch.int32)
+    conf_g = g["conf"][:77].contiguous()
+    for tau in (0.01, 0.02):
+        _dapd_case(attn, pos[:77].contiguous(), so2, conf_g, o["conf"][:77], tau, 45,
+                   f"scattered tau={tau}")
+    # a sequence longer than m_max is reported
+    out = api.dapd_select(attn, pos, so, g["conf"], 0.01, m_max=30)
+    assert host(out["n_commit"]).tolist() == [-1, -1, -1]
