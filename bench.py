@@ -60,6 +60,11 @@ def measured_traffic(nbytes_alg: int):
     return t.get("hbm_bytes_per_launch")
 
 
+def torch_int_view(t):
+    import torch
+    return {torch.float32: torch.int32}.get(t.dtype, t.dtype)
+
+
 class LladaStep:
     """Preallocated buffers and ctypes argument lists for the LLaDA-shaped step."""
 
@@ -92,17 +97,30 @@ class LladaStep:
         self.commit_f, self.commit_c, self.commit_d = (torch.empty(n, **u8) for _ in range(3))
         self.nf, self.nc, self.nd, self.blen = (torch.empty(1, **i32) for _ in range(4))
         self.score = torch.empty(n, **f32)
+        self.sws_bytes = int(self.L.dlm_step_stats_workspace_bytes(n))
+        self.sws = torch.zeros(self.sws_bytes, **u8)     # zero-filled once; kept zero by the library
         self.ws_bytes = int(self.L.dlm_dapd_workspace_bytes(1, n))
         self.ws = torch.empty(self.ws_bytes, **u8)
-        self.stream = torch.cuda.current_stream().cuda_stream
+        # every call goes to this stream (default priority), eager or captured
+        self.torch_stream = torch.cuda.Stream(device=dev)
+        self.stream = self.torch_stream.cuda_stream
         self.n_lh, self.S = attn.shape[1], attn.shape[2]
         self.bytes_stats = n * self.V * 2 * 2          # cur + prev rows, bf16
+
+    def outputs(self):
+        """Copies of every output, as raw bits (so NaN compares equal to NaN)."""
+        out = []
+        for t in (self.conf, self.arg, self.ent, self.kl, self.lse, self.commit_f, self.nf,
+                  self.blen, self.score, self.commit_c, self.nc, self.commit_d, self.nd):
+            out.append(t.view(torch_int_view(t)).clone())
+        return out
 
     def stats(self, r):
         st = self.L.dlm_step_stats(self.cur[r].data_ptr(), self.prev[r].data_ptr(), 0, self.V,
                                    self.V, self.ri.data_ptr(), self.rows, self.conf.data_ptr(),
                                    self.arg.data_ptr(), self.ent.data_ptr(), self.kl.data_ptr(),
-                                   self.lse.data_ptr(), self.stream)
+                                   self.lse.data_ptr(), self.sws.data_ptr(), self.sws_bytes,
+                                   self.stream)
         if st:
             self.check(st, "dlm_step_stats")
 
@@ -212,6 +230,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-iters", type=int, default=200)
+    ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
+                    help="graph: the step is captured once per input replica and replayed")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -226,42 +246,87 @@ def main() -> int:
     dev = "cuda:0"
     torch.cuda.set_device(0)
     step = LladaStep(args.replicas, dev)
+    R = args.replicas
+    sm = step.torch_stream
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        step.step(i % args.replicas)
+    def timed_eager(n_steps, with_stats_events):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_steps)] if with_stats_events else None
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(sm):
+            t0.record()
+            for i in range(n_steps):
+                step.step(i % R, ev[i] if ev else None)
+            t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / n_steps
+        st_us = (sum(a.elapsed_time(b) for a, b in ev) / n_steps * 1000.0) if ev else None
+        return ms, st_us
+
+    with torch.cuda.stream(sm):
+        for i in range(args.warmup):
+            step.step(i % R)
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        step.step(i % args.replicas, ev[i])
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    stats_us = sum(a.elapsed_time(b) for a, b in ev) / args.steps * 1000.0
+    graph_ok = None
+    if args.mode == "graph":
+        # one captured step per input replica; replays run the seven kernels
+        # back to back without host launch overhead
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=sm):
+                step.step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        # replay correctness: each replica's replay equals its eager step
+        graph_ok = True
+        for r in range(R):
+            with torch.cuda.stream(sm):
+                step.step(r)
+            torch.cuda.synchronize()
+            want = step.outputs()
+            graphs[r].replay()
+            torch.cuda.synchronize()
+            got = step.outputs()
+            graph_ok = graph_ok and all(torch.equal(a, b) for a, b in zip(want, got))
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(sm):
+            t0.record()
+            for i in range(args.steps):
+                graphs[i % R].replay()
+            t1.record()
+        torch.cuda.synchronize()
+        ms_per_step = t0.elapsed_time(t1) / args.steps
+        # the stats kernel's live duration: HIP events on its launch stream over
+        # an eager run of the same steps (events cannot sit inside the graphs)
+        eager_ms, stats_us = timed_eager(args.steps, True)
+    else:
+        ms_per_step, stats_us = timed_eager(args.steps, True)
+        eager_ms = ms_per_step
 
     # per-call breakdown (untimed region, same rotation)
     breakdown = {}
     for name in ("stats", "fastdllm", "depcap", "cap", "dapd"):
         fn = getattr(step, name)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for i in range(10):
-            step.step(i % args.replicas)
-        torch.cuda.synchronize()
-        acc = 0.0
-        for i in range(args.breakdown_iters):
-            r = i % args.replicas
-            e0.record()
-            fn(r)
-            e1.record()
-            e1.synchronize()
-            acc += e0.elapsed_time(e1)
-            step.step((i + 1) % args.replicas)          # keep the inputs cold in cache
+        with torch.cuda.stream(sm):
+            for i in range(10):
+                step.step(i % R)
+            torch.cuda.synchronize()
+            acc = 0.0
+            for i in range(args.breakdown_iters):
+                e0.record()
+                fn(i % R)
+                e1.record()
+                e1.synchronize()
+                acc += e0.elapsed_time(e1)
+                step.step((i + 1) % R)          # keep the inputs cold in cache
         breakdown[name] = round(acc / args.breakdown_iters * 1000.0, 2)
 
     achieved = step.bytes_stats / (stats_us * 1e-6) / 1e9
@@ -285,8 +350,10 @@ def main() -> int:
             "workload": "llada-step: 1 seq x 256 masked rows, V=126464 bf16 cur+prev logits; "
                         "Fast-dLLM + DepCap boundary + CAP on block 0 + DAPD over 256 rows",
             "rows": step.rows, "vocab": step.V, "attention": [1, step.n_lh, step.S, step.S],
-            "replicas": args.replicas,
+            "replicas": args.replicas, "mode": args.mode,
         },
+        "eager_ms_per_step": round(eager_ms, 5),
+        "graph_replay_matches_eager": graph_ok,
         "roofline": {
             "bound": "hbm", "kernel": "dlm_step_stats (k_stats)",
             "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

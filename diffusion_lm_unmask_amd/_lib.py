@@ -25,7 +25,9 @@ _INT = ctypes.c_int
 _SZ = ctypes.c_size_t
 
 SIGNATURES = {
-    "dlm_step_stats": (_INT, [_P, _P, _INT, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P]),
+    "dlm_step_stats": (_INT, [_P, _P, _INT, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ,
+                              _P]),
+    "dlm_step_stats_workspace_bytes": (_SZ, [_I64]),
     "dlm_fastdllm_select": (_INT, [_P, _P, _P, _I32, _F, _P, _P, _P]),
     "dlm_depcap_boundary": (_INT, [_P, _P, _P, _I32, _P, _D, _I32, _I32, _I32, _D, _P, _P, _P]),
     "dlm_cap_select": (_INT, [_P, _INT, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P, _F, _F, _F,

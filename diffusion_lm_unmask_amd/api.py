@@ -64,11 +64,30 @@ def _rows2d(logits, name):
     return logits.stride(0)
 
 
+_WORKSPACES: dict = {}
+
+
+def stats_workspace(n_rows: int, device) -> torch.Tensor:
+    """Zero-filled dlm_step_stats workspace for `n_rows` rows, cached per
+    (device, current stream): the library leaves it zero-filled after every
+    call, and calls on one stream never overlap."""
+    dev = torch.device(device)
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    need = int(_lib.lib().dlm_step_stats_workspace_bytes(int(n_rows)))
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 256), device=dev, dtype=torch.uint8)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def step_stats(logits: torch.Tensor, prev: torch.Tensor | None = None,
-               row_index: torch.Tensor | None = None, vocab: int | None = None):
+               row_index: torch.Tensor | None = None, vocab: int | None = None,
+               split: bool = True):
     """dlm_step_stats.  logits: [N, >=vocab] (bf16 or f32, unit column
     stride); row_index: int64 rows to decide (default: all).  Returns a dict
-    with conf, argmax, entropy, kl (None without prev), lse."""
+    with conf, argmax, entropy, kl (None without prev), lse.  split=False
+    runs one workgroup per row (no workspace)."""
     ld = _rows2d(logits, "logits")
     dev = logits.device
     vocab = logits.shape[1] if vocab is None else int(vocab)
@@ -84,9 +103,11 @@ def step_stats(logits: torch.Tensor, prev: torch.Tensor | None = None,
     conf, ent, lse = torch.empty(n, **f), torch.empty(n, **f), torch.empty(n, **f)
     kl = torch.empty(n, **f) if prev is not None else None
     arg = torch.empty(n, device=dev, dtype=torch.int32)
+    ws = stats_workspace(n, dev) if split else None
     st = _lib.lib().dlm_step_stats(logits.data_ptr(), _ptr(prev), _dtype_code(logits), vocab, ld,
                                    row_index.data_ptr(), n, conf.data_ptr(), arg.data_ptr(),
-                                   ent.data_ptr(), _ptr(kl), lse.data_ptr(), _stream(logits))
+                                   ent.data_ptr(), _ptr(kl), lse.data_ptr(), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(logits))
     _lib.check(st, "dlm_step_stats")
     return {"conf": conf, "argmax": arg, "entropy": ent, "kl": kl, "lse": lse}
 

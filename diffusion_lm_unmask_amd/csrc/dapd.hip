@@ -3,30 +3,42 @@
 // (s_ij = (a_ij + a_ji)/2, edge iff s_ij > tau); key design 2 (proxy degree,
 // order by degree x confidence, maximal independent set)).
 //
-// Two kernels:
-//  k_dapd_avg   grid-wide, HBM-bound.  Streams only the masked x masked
-//               sub-blocks of the n_lh attention maps (fp32 accumulation) and
-//               writes a and its transpose to the workspace.  A workgroup owns a
-//               tile of 8 rows x 64 columns; its 4 waves take every 4th map and
-//               are summed in LDS in a fixed order.  The 8-row tile makes the
-//               transposed writes 32-byte runs.
-//  k_dapd_select one workgroup (1024 threads) per sequence: s = (a + aT)/2
-//               (computed once per unordered pair value, so bit-symmetric),
-//               adjacency bitset in LDS, fp64 proxy degree, key, bitonic sort,
-//               and the sequential greedy on one wave with the chosen-set
-//               bitset spread over its lanes.
+// Three kernels:
+//  k_dapd_avg    grid-wide, HBM-bound.  Streams only the masked x masked
+//                sub-blocks of the n_lh attention maps (fp32 accumulation) and
+//                writes a and its transpose to the workspace.  A workgroup owns
+//                32 (row, 8-column chunk) items = one row x 256 columns, so each
+//                wave reads whole 512-byte row segments of two maps; its 1024
+//                lanes are 32 map groups x 32 items, so a single sequence already
+//                fills every CU.  Map groups are summed in LDS in a fixed order.
+//  k_dapd_sym    grid-wide: s = (a + aT)/2 for 16 rows per workgroup, one
+//                16-lane team per row with float4 loads; each lane turns its 16
+//                columns into a 16-bit slice of the row's adjacency bitset;
+//                fp64 proxy degree and the ordering key.
+//  k_dapd_select one workgroup (1024 threads) per sequence:
+//                1. the adjacency bitset and keys into LDS;
+//                2. rank sort of the 64-bit keys (key desc, position asc);
+//                3. greedy over blocks of 64 nodes in that order: a node is
+//                   blocked by an earlier block's chosen node (bitset AND) or by
+//                   an earlier node of its own block (ballots), which gives the
+//                   same set as the one-node-at-a-time scan.
 #include <math.h>
 
 #include "dlm_device.h"
 
 namespace {
 
-constexpr int kAvgNT = 256;  // 4 waves = 4 map groups
-constexpr int kTileRows = 8;
-constexpr int kTileChunks = 8;  // 8 chunks of 8 columns = 64 columns
+constexpr int kGroups = 32;          // map groups per workgroup
+constexpr int kItems = 32;           // (row, chunk) items per workgroup
+constexpr int kAvgNT = kGroups * kItems;
+constexpr int kTileRows = 1;
+constexpr int kTileChunks = kItems / kTileRows;  // 32 chunks of 8 columns = 256 columns
 constexpr int kSelNT = 1024;
 constexpr int kMaxM = DLM_MAX_SEQ_ROWS;
 constexpr int kWords = kMaxM / 64;
+
+// Row stride (floats) of the workspace matrices: 16-float aligned rows.
+__host__ __device__ inline int ws_ld(int m_max) { return (m_max + 15) & ~15; }
 
 template <bool BF16>
 __device__ __forceinline__ float ld1(const void* base, int64_t idx) {
@@ -42,24 +54,24 @@ __global__ __launch_bounds__(kAvgNT) void k_dapd_avg(const void* __restrict__ at
                                                      int m_max, int n_tc, int vec_ok,
                                                      float* __restrict__ ws_a,
                                                      float* __restrict__ ws_at) {
-  __shared__ float red[4][64][9];
+  __shared__ float red[kGroups][kItems][9];
   const int b = blockIdx.y;
   const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
   if (M > m_max || M <= 0) return;
   const int ti = blockIdx.x / n_tc, tc = blockIdx.x % n_tc;
   const int i0 = ti * kTileRows, c0 = tc * kTileChunks;
   if (i0 >= M || c0 * 8 >= M) return;  // whole workgroup idle (uniform)
-  const int wv = threadIdx.x / DLM_WAVE, ln = threadIdx.x % DLM_WAVE;
-  const int i = i0 + ln / kTileChunks, c = c0 + ln % kTileChunks;
+  const int g = threadIdx.x / kItems, it = threadIdx.x % kItems;
+  const int i = i0 + it / kTileChunks, c = c0 + it % kTileChunks;
   const int j0 = c * 8;
-  const bool row_ok = i < M;
+  const bool item_ok = i < M && j0 < M;
   const int* pos = masked_pos + lo;
 
   float acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
 
-  if (row_ok && j0 < M) {
+  if (item_ok) {
     const int64_t prow = static_cast<int64_t>(pos[i]) * S;
     int pj[8];
     bool contig = vec_ok && (j0 + 8 <= M);
@@ -73,22 +85,28 @@ __global__ __launch_bounds__(kAvgNT) void k_dapd_avg(const void* __restrict__ at
                        static_cast<int64_t>(b) * batch_stride * (BF16 ? 2 : 4);
     const int64_t map_stride = S * S;
     if (contig) {
-      constexpr int UNR = 4;
-      int lh = wv;
-      for (; lh + 4 * (UNR - 1) < n_lh; lh += 4 * UNR) {
+      // every map this lane owns is loaded before any is summed (one round
+      // trip for up to UNR * kGroups maps)
+      constexpr int UNR = BF16 ? 12 : 6;
+      for (int lh0 = g; lh0 < n_lh; lh0 += kGroups * UNR) {
         uint4 q[UNR][BF16 ? 1 : 2];
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
-          const int64_t e = static_cast<int64_t>(lh + 4 * u) * map_stride + prow + pj[0];
+          const int lh = lh0 + kGroups * u;
+          const int64_t e = static_cast<int64_t>(lh) * map_stride + prow + pj[0];
           if constexpr (BF16) {
-            q[u][0] = *reinterpret_cast<const uint4*>(base + e * 2);
+            q[u][0] = lh < n_lh ? *reinterpret_cast<const uint4*>(base + e * 2)
+                                : make_uint4(0u, 0u, 0u, 0u);
           } else {
-            q[u][0] = *reinterpret_cast<const uint4*>(base + e * 4);
-            q[u][1] = *reinterpret_cast<const uint4*>(base + e * 4 + 16);
+            q[u][0] = lh < n_lh ? *reinterpret_cast<const uint4*>(base + e * 4)
+                                : make_uint4(0u, 0u, 0u, 0u);
+            q[u][1] = lh < n_lh ? *reinterpret_cast<const uint4*>(base + e * 4 + 16)
+                                : make_uint4(0u, 0u, 0u, 0u);
           }
         }
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
+          if (lh0 + kGroups * u >= n_lh) break;
           if constexpr (BF16) {
             acc[0] += dlm::bf16_lo(q[u][0].x);
             acc[1] += dlm::bf16_hi(q[u][0].x);
@@ -110,13 +128,8 @@ __global__ __launch_bounds__(kAvgNT) void k_dapd_avg(const void* __restrict__ at
           }
         }
       }
-      for (; lh < n_lh; lh += 4) {
-        const int64_t e = static_cast<int64_t>(lh) * map_stride + prow + pj[0];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] += ld1<BF16>(base, e + k);
-      }
     } else {
-      for (int lh = wv; lh < n_lh; lh += 4) {
+      for (int lh = g; lh < n_lh; lh += kGroups) {
         const int64_t e = static_cast<int64_t>(lh) * map_stride + prow;
 #pragma unroll
         for (int k = 0; k < 8; ++k)
@@ -125,20 +138,20 @@ __global__ __launch_bounds__(kAvgNT) void k_dapd_avg(const void* __restrict__ at
     }
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) red[wv][ln][k] = acc[k];
+  for (int k = 0; k < 8; ++k) red[g][it][k] = acc[k];
   __syncthreads();
-  if (wv == 0 && row_ok && j0 < M) {
-    const float fn = static_cast<float>(n_lh);
-    float* arow = ws_a + (static_cast<int64_t>(b) * m_max + i) * m_max;
+  // 32 items x 8 columns = 256 outputs; thread t < 256 finishes one
+  if (threadIdx.x < kItems * 8) {
+    const int oi = threadIdx.x / 8, k = threadIdx.x % 8;
+    const int ri = i0 + oi / kTileChunks, rj = (c0 + oi % kTileChunks) * 8 + k;
+    if (ri < M && rj < M) {
+      float s = red[0][oi][k];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int j = j0 + k;
-      if (j < M) {
-        const float s = ((red[0][ln][k] + red[1][ln][k]) + red[2][ln][k]) + red[3][ln][k];
-        const float a = s / fn;
-        arow[j] = a;
-        ws_at[(static_cast<int64_t>(b) * m_max + j) * m_max + i] = a;
-      }
+      for (int q = 1; q < kGroups; ++q) s += red[q][oi][k];  // fixed order
+      const float a = s / static_cast<float>(n_lh);
+      const int ld = ws_ld(m_max);
+      ws_a[(static_cast<int64_t>(b) * m_max + ri) * ld + rj] = a;
+      ws_at[(static_cast<int64_t>(b) * m_max + rj) * ld + ri] = a;
     }
   }
 }
@@ -149,17 +162,131 @@ __device__ __forceinline__ uint32_t desc_bits(float f) {
   return ~asc;
 }
 
-__global__ __launch_bounds__(kSelNT) void k_dapd_select(
+// Workspace layout (every region 256-byte aligned), for n_seq x m_max:
+//   a, aT      f32 [n_seq][m_max][ws_ld]     averaged maps and transpose
+//   adj        u64 [n_seq][m_max][words]     adjacency bitsets, words = ceil(m_max/64)
+//   keys       u64 [n_seq][m_max]            (order key, position)
+//   has_edge   u8  [n_seq][m_max]
+struct Layout {
+  size_t a, at, adj, keys, has_edge, total;
+  int ld, words;
+};
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+__host__ __device__ inline Layout layout(int n_seq, int m_max) {
+  Layout L;
+  L.ld = ws_ld(m_max);
+  L.words = (m_max + 63) / 64;
+  const size_t nm = static_cast<size_t>(n_seq) * m_max;
+  L.a = 0;
+  L.at = align256(nm * L.ld * sizeof(float));
+  L.adj = L.at + align256(nm * L.ld * sizeof(float));
+  L.keys = L.adj + align256(nm * L.words * sizeof(uint64_t));
+  L.has_edge = L.keys + align256(nm * sizeof(uint64_t));
+  L.total = L.has_edge + align256(nm);
+  return L;
+}
+
+constexpr int kSymRows = 16;           // rows per k_dapd_sym workgroup (16 lanes each)
+constexpr int kSymNT = kSymRows * 16;
+
+// s = (a + aT)/2 for 16 rows per workgroup: adjacency bits (16-bit slices
+// per lane), fp64 proxy degree (fixed-pattern 16-lane reduction), ordering key.
+__global__ __launch_bounds__(kSymNT) void k_dapd_sym(
     const int32_t* __restrict__ seq_offsets, int m_max, const float* __restrict__ conf,
-    float tau, const float* __restrict__ ws_a, const float* __restrict__ ws_at,
+    float tau, const char* __restrict__ ws, Layout L, float* __restrict__ degree,
+    float* __restrict__ sym, float* __restrict__ key_out) {
+  const int b = blockIdx.y;
+  const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
+  const int team = threadIdx.x / 16, tl = threadIdx.x % 16;
+  const int i = blockIdx.x * kSymRows + team;
+  const int64_t sbase = static_cast<int64_t>(b) * m_max * m_max;
+  if (M > m_max || M < 0 || i >= m_max) return;  // over-long sequences: k_dapd_select reports
+  if (i >= M) {  // pad rows of the optional sym output
+    if (sym)
+      for (int j = tl; j < m_max; j += 16) sym[sbase + static_cast<int64_t>(i) * m_max + j] = NAN;
+    return;
+  }
+  const float* ar = reinterpret_cast<const float*>(ws + L.a) +
+                    (static_cast<int64_t>(b) * m_max + i) * L.ld;
+  const float* tr = reinterpret_cast<const float*>(ws + L.at) +
+                    (static_cast<int64_t>(b) * m_max + i) * L.ld;
+  uint16_t* adj16 = reinterpret_cast<uint16_t*>(
+      const_cast<char*>(ws) + L.adj + (static_cast<int64_t>(b) * m_max + i) * L.words * 8);
+  const int nw = (M + 63) / 64;
+  float* so = sym ? sym + sbase + static_cast<int64_t>(i) * m_max : nullptr;
+  double dsum = 0.0;
+  bool any = false;
+  for (int c0 = 0; c0 < 64 * nw; c0 += 256) {
+    const int j0 = c0 + tl * 16;
+    float va[16], vt[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float4 xa = make_float4(0.f, 0.f, 0.f, 0.f), xt = xa;
+      if (j0 + 4 * q < M) {  // stays inside the 16-float padded row
+        xa = reinterpret_cast<const float4*>(ar + j0)[q];
+        xt = reinterpret_cast<const float4*>(tr + j0)[q];
+      }
+      va[4 * q + 0] = xa.x;
+      va[4 * q + 1] = xa.y;
+      va[4 * q + 2] = xa.z;
+      va[4 * q + 3] = xa.w;
+      vt[4 * q + 0] = xt.x;
+      vt[4 * q + 1] = xt.y;
+      vt[4 * q + 2] = xt.z;
+      vt[4 * q + 3] = xt.w;
+    }
+    if (j0 >= 64 * nw) continue;
+    uint32_t bits = 0u;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int j = j0 + e;
+      float sv = NAN;
+      if (j < M) {
+        sv = 0.5f * (va[e] + vt[e]);
+        if (j != i) {
+          dsum += static_cast<double>(sv);
+          bits |= static_cast<uint32_t>(sv > tau) << e;
+        }
+      }
+      if (so && j < m_max) so[j] = sv;
+    }
+    adj16[j0 / 16] = static_cast<uint16_t>(bits);  // zero past M, up to the last word
+    any = any || bits != 0u;
+  }
+  if (so)
+    for (int j = 64 * nw + tl; j < m_max; j += 16) so[j] = NAN;
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) dsum += __shfl_xor(dsum, o, 16);  // fixed pattern
+  uint32_t anyb = any ? 1u : 0u;
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) anyb |= __shfl_xor(anyb, o, 16);
+  if (tl == 0) {
+    const float df = static_cast<float>(dsum);
+    const float kk = df * conf[lo + i];
+    if (degree) degree[lo + i] = df;
+    if (key_out) key_out[lo + i] = kk;
+    const uint64_t hi = (kk != kk) ? 0xffffffffull : static_cast<uint64_t>(desc_bits(kk));
+    // NaN keys sort last; every other key maps below 0xffffffff
+    reinterpret_cast<uint64_t*>(const_cast<char*>(ws) + L.keys)[static_cast<int64_t>(b) * m_max + i] =
+        (hi << 32) | static_cast<uint32_t>(i);
+    reinterpret_cast<uint8_t*>(const_cast<char*>(ws) + L.has_edge)[static_cast<int64_t>(b) * m_max + i] =
+        static_cast<uint8_t>(anyb);
+  }
+}
+
+// Per sequence: load the graph into LDS, order the nodes, run the greedy.
+__global__ __launch_bounds__(kSelNT) void k_dapd_select(
+    const int32_t* __restrict__ seq_offsets, int m_max, const char* __restrict__ ws, Layout L,
     uint8_t* __restrict__ commit, int32_t* __restrict__ n_commit, float* __restrict__ degree,
     float* __restrict__ sym, float* __restrict__ key_out) {
-  __shared__ uint64_t adj[kMaxM][kWords];  // 128 KiB
+  __shared__ uint64_t adj[kMaxM][kWords];  // 128 KiB; row i = neighbours of node i
   __shared__ uint64_t keys[kMaxM];
+  __shared__ int16_t order[kMaxM];
   __shared__ uint64_t chosen[kWords];
+  __shared__ uint8_t has_edge[kMaxM];
+  __shared__ int shi[kSelNT / DLM_WAVE];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int wv = tid / DLM_WAVE, ln = tid % DLM_WAVE;
-  constexpr int NW = kSelNT / DLM_WAVE;
   const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
   const int64_t sbase = static_cast<int64_t>(b) * m_max * m_max;
 
@@ -175,84 +302,82 @@ __global__ __launch_bounds__(kSelNT) void k_dapd_select(
     if (tid == 0) n_commit[b] = -1;
     return;
   }
-  const int nw = (M + 63) / 64;       // adjacency words in use
-  const int wm = (m_max + 63) / 64;   // words spanned by a sym row
-
-  // phase 1: s, adjacency words, proxy degree, key.  Wave w owns rows w, w+16, ...
-  for (int i = wv; i < m_max; i += NW) {
-    if (i >= M) {  // pad rows of the optional sym output
-      if (sym)
-        for (int j = ln; j < m_max; j += DLM_WAVE) sym[sbase + static_cast<int64_t>(i) * m_max + j] = NAN;
-      continue;
-    }
-    const float* ar = ws_a + sbase + static_cast<int64_t>(i) * m_max;
-    const float* tr = ws_at + sbase + static_cast<int64_t>(i) * m_max;
-    double dsum = 0.0;
-    for (int w = 0; w < wm; ++w) {
-      const int j = w * 64 + ln;
-      bool edge = false;
-      float s = NAN;
-      if (j < M) {
-        s = 0.5f * (ar[j] + tr[j]);
-        if (j != i) {
-          dsum += static_cast<double>(s);
-          edge = s > tau;
-        }
-      }
-      if (sym && j < m_max) sym[sbase + static_cast<int64_t>(i) * m_max + j] = s;
-      if (w < nw) {  // w is wave-uniform
-        const uint64_t bits = __ballot(edge);
-        if (ln == 0) adj[i][w] = bits;
-      }
-    }
-    dsum = dlm::wave_sum(dsum);
-    if (ln == 0) {
-      const float d = static_cast<float>(dsum);
-      const float kk = d * conf[lo + i];
-      if (degree) degree[lo + i] = d;
-      if (key_out) key_out[lo + i] = kk;
-      const uint64_t hi = (kk != kk) ? 0xffffffffull : static_cast<uint64_t>(desc_bits(kk));
-      // NaN keys sort last; every finite key maps below 0xffffffff
-      keys[i] = (hi << 32) | static_cast<uint32_t>(i);
-    }
+  const int nw = (M + 63) / 64;  // adjacency words in use
+  const uint64_t* gadj = reinterpret_cast<const uint64_t*>(ws + L.adj) +
+                         static_cast<int64_t>(b) * m_max * L.words;
+  for (int e = tid; e < M * nw; e += kSelNT) {
+    const int i = e / nw, w = e - i * nw;
+    adj[i][w] = gadj[static_cast<int64_t>(i) * L.words + w];
   }
-  int n2 = 1;
-  while (n2 < M) n2 <<= 1;
-  for (int i = M + tid; i < n2; i += kSelNT) keys[i] = ~0ull;
+  const uint64_t* gkeys = reinterpret_cast<const uint64_t*>(ws + L.keys) +
+                          static_cast<int64_t>(b) * m_max;
+  const uint8_t* gedge = reinterpret_cast<const uint8_t*>(ws + L.has_edge) +
+                         static_cast<int64_t>(b) * m_max;
+  for (int e = tid; e < M; e += kSelNT) {
+    keys[e] = gkeys[e];
+    has_edge[e] = gedge[e];
+  }
   if (tid < kWords) chosen[tid] = 0ull;
   __syncthreads();
 
-  // phase 2: order by (key desc, position asc)
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int t = tid; t < n2 / 2; t += kSelNT) {
-        const int i = 2 * j * (t / j) + (t % j);
-        const int p = i + j;
-        const bool up = (i & k) == 0;
-        const uint64_t x = keys[i], y = keys[p];
-        if ((x > y) == up) {
-          keys[i] = y;
-          keys[p] = x;
+  // ---- rank sort, 4 threads per key (keys are unique: they carry the position)
+  for (int i0 = 0; i0 < M; i0 += kSelNT / 4) {
+    const int i = i0 + tid / 4, part = tid % 4;
+    int rank = 0;
+    if (i < M) {
+      const uint64_t k = keys[i];
+      const int j0 = part * ((M + 3) / 4), j1 = min(M, j0 + (M + 3) / 4);
+#pragma unroll 8
+      for (int j = j0; j < j1; ++j) rank += keys[j] < k;
+    }
+    rank += __shfl_xor(rank, 1, 4);
+    rank += __shfl_xor(rank, 2, 4);
+    if (i < M && part == 0) order[rank] = static_cast<int16_t>(i);
+  }
+  __syncthreads();
+
+  // ---- greedy on wave 0, 64 nodes of the order at a time
+  if (wv == 0) {
+    for (int base = 0; base < M; base += 64) {
+      const int t = base + ln;
+      int v = -1;
+      if (t < M) {
+        const int cand = order[t];
+        if ((keys[cand] >> 32) != 0xffffffffull) v = cand;  // NaN keys never chosen
+      }
+      uint64_t sel;
+      if (__ballot(v >= 0 && has_edge[v]) == 0ull) {
+        sel = __ballot(v >= 0);  // no node of this block has an edge: all chosen
+      } else {
+        // blocked by a node chosen in an earlier block
+        bool blocked = false;
+        if (v >= 0)
+          for (int w = 0; w < nw; ++w) blocked |= (adj[v][w] & chosen[w]) != 0ull;
+        // conflicts with earlier nodes of this block: bit q set when node q < ln
+        // is adjacent (reads unrolled so that they are in flight together)
+        uint64_t local = 0ull;
+#pragma unroll 16
+        for (int q = 0; q < 64; ++q) {
+          const int vq = __builtin_amdgcn_readlane(v, q);
+          const uint64_t word = (v >= 0 && vq >= 0) ? adj[v][vq >> 6] : 0ull;
+          if (q < ln && vq >= 0) local |= ((word >> (vq & 63)) & 1ull) << q;
+        }
+        uint64_t cand = __ballot(v >= 0 && !blocked);
+        if (__ballot(local != 0ull) == 0ull) {
+          sel = cand;  // no conflicts inside the block
+        } else {
+          sel = 0ull;
+          while (cand) {
+            const int p = __builtin_ctzll(cand);
+            sel |= 1ull << p;
+            cand &= ~(1ull << p);
+            cand &= ~__ballot(((local >> p) & 1ull) != 0ull);  // later nodes adjacent to p
+          }
         }
       }
-      __syncthreads();
+      if ((sel >> ln) & 1ull)
+        atomicOr(reinterpret_cast<unsigned long long*>(&chosen[v >> 6]), 1ull << (v & 63));
     }
-  }
-
-  // phase 3: greedy on wave 0; lane w < nw holds word w of the excluded set
-  if (wv == 0) {
-    uint64_t excl = 0ull, mine = 0ull;
-    for (int t = 0; t < M; ++t) {
-      const uint64_t kv = keys[t];
-      if ((kv >> 32) == 0xffffffffull) break;  // NaN keys: never chosen
-      const int v = static_cast<int>(kv & 0xffffffffu);
-      const uint64_t word = __shfl(excl, v >> 6, DLM_WAVE);
-      if (((word >> (v & 63)) & 1ull) == 0ull) {
-        if (ln < nw) excl |= adj[v][ln];
-        if (ln == (v >> 6)) mine |= 1ull << (v & 63);
-      }
-    }
-    if (ln < kWords) chosen[ln] = mine;
   }
   __syncthreads();
   int cnt = 0;
@@ -261,7 +386,6 @@ __global__ __launch_bounds__(kSelNT) void k_dapd_select(
     commit[lo + r] = static_cast<uint8_t>(c);
     cnt += c;
   }
-  __shared__ int shi[NW];
   cnt = dlm::block_sum<kSelNT>(cnt, shi);
   if (tid == 0) n_commit[b] = cnt;
 }
@@ -270,8 +394,7 @@ __global__ __launch_bounds__(kSelNT) void k_dapd_select(
 
 extern "C" size_t dlm_dapd_workspace_bytes(int32_t n_seq, int32_t m_max) {
   if (n_seq <= 0 || m_max <= 0 || m_max > DLM_MAX_SEQ_ROWS) return 0;
-  return static_cast<size_t>(2) * static_cast<size_t>(n_seq) * static_cast<size_t>(m_max) *
-         static_cast<size_t>(m_max) * sizeof(float);
+  return layout(n_seq, m_max).total;
 }
 
 extern "C" int dlm_dapd_select(const void* attn, int dtype, int32_t n_lh, int64_t S,
@@ -293,8 +416,10 @@ extern "C" int dlm_dapd_select(const void* attn, int dtype, int32_t n_lh, int64_
   if (reinterpret_cast<uintptr_t>(workspace) % 16) return DLM_ERR_ARG;
   if (workspace_bytes < dlm_dapd_workspace_bytes(n_seq, m_max)) return DLM_ERR_ARG;
   const int vec_ok = (ab % 16 == 0) && (S % 8 == 0) && (batch_stride % 8 == 0);
-  float* ws_a = static_cast<float*>(workspace);
-  float* ws_at = ws_a + static_cast<size_t>(n_seq) * m_max * m_max;
+  const Layout L = layout(n_seq, m_max);
+  char* ws = static_cast<char*>(workspace);
+  float* ws_a = reinterpret_cast<float*>(ws + L.a);
+  float* ws_at = reinterpret_cast<float*>(ws + L.at);
   const int n_ti = (m_max + kTileRows - 1) / kTileRows;
   const int n_tc = (m_max + 8 * kTileChunks - 1) / (8 * kTileChunks);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -306,8 +431,11 @@ extern "C" int dlm_dapd_select(const void* attn, int dtype, int32_t n_lh, int64_
     hipLaunchKernelGGL(k_dapd_avg<false>, grid, dim3(kAvgNT), 0, s, attn, n_lh, S, batch_stride,
                        masked_pos, seq_offsets, m_max, n_tc, vec_ok, ws_a, ws_at);
   DLM_CHECK_LAUNCH();
-  hipLaunchKernelGGL(k_dapd_select, dim3(n_seq), dim3(kSelNT), 0, s, seq_offsets, m_max, conf,
-                     tau, ws_a, ws_at, commit, n_commit, degree, sym, key);
+  hipLaunchKernelGGL(k_dapd_sym, dim3((m_max + kSymRows - 1) / kSymRows, n_seq), dim3(kSymNT), 0,
+                     s, seq_offsets, m_max, conf, tau, ws, L, degree, sym, key);
+  DLM_CHECK_LAUNCH();
+  hipLaunchKernelGGL(k_dapd_select, dim3(n_seq), dim3(kSelNT), 0, s, seq_offsets, m_max, ws, L,
+                     commit, n_commit, degree, sym, key);
   DLM_CHECK_LAUNCH();
   return DLM_OK;
 }

@@ -13,6 +13,8 @@
 //    exp2 per element, t = x*log2(e) - h, with the lane reference
 //    h = ceil(max*log2(e)) an integer, so a rescale of the running sums when
 //    the max grows is an exact power of two (ldexp) and adds no rounding;
+//  * the previous step's row is summed against the same reference, so KL
+//    needs no second maximum: KL = B/Z + log(Z2/Z);
 //  * sums are fp32 per segment and per lane; lanes are combined exactly
 //    (ldexp) in fp64 relative to the row's integer reference, and the
 //    fractional offset between that reference and the row max is applied
@@ -33,6 +35,25 @@ constexpr double kLN2 = 0.6931471805599453;
 constexpr float kLow = -1e30f;  // running-max sentinel: no finite data seen yet
 
 __device__ __forceinline__ float ex2(float t) { return __builtin_amdgcn_exp2f(t); }
+
+// Tuning: 16-byte chunks per lane per segment, and whether row loads carry the
+// non-temporal hint (streamed once, not worth caching).
+#ifndef DLM_STATS_U_BF16
+#define DLM_STATS_U_BF16 2
+#endif
+#ifndef DLM_STATS_NT_LOADS
+#define DLM_STATS_NT_LOADS 1
+#endif
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16(const uint4* p) {
+#if DLM_STATS_NT_LOADS
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
+}
 
 template <bool BF16>
 __device__ __forceinline__ void unpack(const uint4 q, float* x) {
@@ -59,22 +80,36 @@ __device__ __forceinline__ float load_elem(const char* row, int64_t v) {
   return reinterpret_cast<const float*>(row)[v];
 }
 
-// Per-lane running state for the current (cur) and previous (prv) rows.
-struct CurState {
-  float m, h, Z, A, B;  // max, ceil(m*log2e), sum e, sum e*t (log2 units), sum e*(x-y)
-  int64_t best;         // first element index of the chunk holding the lane max
-  int bestw;            // width of that chunk (VEC, or 1 for a tail element)
-};
-struct PrvState {
-  float m, h, Z;
+// Element k of a 16-byte chunk (k is a compile-time constant after unrolling).
+template <bool BF16>
+__device__ __forceinline__ float elem_of(const uint4 q, int k) {
+  if constexpr (BF16) {
+    const uint32_t w = (k >> 1) == 0 ? q.x : (k >> 1) == 1 ? q.y : (k >> 1) == 2 ? q.z : q.w;
+    return (k & 1) ? dlm::bf16_hi(w) : dlm::bf16_lo(w);
+  } else {
+    return __uint_as_float(k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w);
+  }
+}
+
+// Per-lane running state.  Both rows' sums use the current row's reference
+// h = ceil(m * log2 e) (m = the lane's running max of the current row): the
+// previous row only needs sum 2^(y*log2e - h), and KL = B/Z + log(Z2/Z) then
+// involves no reference at all.  A previous row far above or below the
+// current one overflows or underflows Z2 and is sent to the element-wise path.
+struct LaneState {
+  float m, h;       // running max of the current row, integer reference
+  float Z, A, B;    // sum e, sum e*t (log2 units), sum e*(x - y)
+  float Z2;         // sum 2^(y*log2e - h)
+  int64_t best;     // first element index of the chunk holding the lane max
+  int bestw;        // width of that chunk (VEC, or 1 for a tail element)
 };
 
-// Fold a block of N values (x: current, y: previous) into the lane state.
-// `valid` masks whole sub-blocks of W values (chunks); start[u] is the
-// element index of sub-block u (for the argmax record).
-template <int NSUB, int W, bool PREV>
-__device__ __forceinline__ void fold(CurState& c, PrvState& p, const float (*x)[W],
-                                     const float (*y)[W], const bool* valid,
+// Fold NSUB sub-blocks of W values into the lane state.  qc/qp hold the raw
+// chunks (W values each); x is the unpacked current row; `valid` masks whole
+// sub-blocks; start[u] is the element index of sub-block u (argmax record).
+template <int NSUB, int W, bool BF16, bool PREV>
+__device__ __forceinline__ void fold(LaneState& c, const float (*x)[W], const uint4* qp,
+                                     const float* ys, const bool* valid,
                                      const int64_t* start) {
   // segment maxima and the first-strict-increase chunk record
   float mr = c.m;
@@ -97,11 +132,14 @@ __device__ __forceinline__ void fold(CurState& c, PrvState& p, const float (*x)[
     const int di = static_cast<int>(fmaxf(dh, -256.f));
     c.A = ldexpf(fmaf(dh, c.Z, c.A), di);
     c.Z = ldexpf(c.Z, di);
-    if constexpr (PREV) c.B = ldexpf(c.B, di);
+    if constexpr (PREV) {
+      c.B = ldexpf(c.B, di);
+      c.Z2 = ldexpf(c.Z2, di);
+    }
     c.h = hn;
     c.m = mr;
   }
-  float z = 0.f, a = 0.f, b = 0.f;
+  float z = 0.f, a = 0.f, b = 0.f, z2 = 0.f;
 #pragma unroll
   for (int u = 0; u < NSUB; ++u) {
     if (!valid[u]) continue;
@@ -111,39 +149,28 @@ __device__ __forceinline__ void fold(CurState& c, PrvState& p, const float (*x)[
       const float e = ex2(t);
       z += e;
       a = fmaf(e, t, a);
-      if constexpr (PREV) b = fmaf(e, x[u][k] - y[u][k], b);
+      if constexpr (PREV) {
+        const float y = ys ? ys[u * W + k] : elem_of<BF16>(qp[u], k);
+        b = fmaf(e, x[u][k] - y, b);
+        z2 += ex2(fmaf(y, kL2E, -c.h));
+      }
     }
   }
   c.Z += z;
   c.A += a;
   if constexpr (PREV) {
     c.B += b;
-    float mq = p.m;
-#pragma unroll
-    for (int u = 0; u < NSUB; ++u) {
-      if (!valid[u]) continue;
-#pragma unroll
-      for (int k = 0; k < W; ++k) mq = fmaxf(mq, y[u][k]);
-    }
-    const float hn = ceilf(mq * kL2E);
-    p.Z = ldexpf(p.Z, static_cast<int>(fmaxf(p.h - hn, -256.f)));
-    p.h = hn;
-    p.m = mq;
-    float z2 = 0.f;
-#pragma unroll
-    for (int u = 0; u < NSUB; ++u) {
-      if (!valid[u]) continue;
-#pragma unroll
-      for (int k = 0; k < W; ++k) z2 += ex2(fmaf(y[u][k], kL2E, -p.h));
-    }
-    p.Z += z2;
+    c.Z2 += z2;
   }
 }
 
-// Sum four doubles over the workgroup in a fixed order.
+// Sum four doubles over the workgroup in a fixed order.  Only thread 0
+// receives the totals (the only consumer); its loop over the per-wave
+// partials is kept rolled so the other waves' partials are not all held in
+// registers at once.
 template <int NT>
-__device__ __forceinline__ void block_sum4(double& a, double& b, double& c, double& d,
-                                           double (*sh)[NT / DLM_WAVE]) {
+__device__ __forceinline__ void block_sum4_to0(double& a, double& b, double& c, double& d,
+                                               double (*sh)[NT / DLM_WAVE]) {
   constexpr int NW = NT / DLM_WAVE;
   a = dlm::wave_sum(a);
   b = dlm::wave_sum(b);
@@ -158,16 +185,18 @@ __device__ __forceinline__ void block_sum4(double& a, double& b, double& c, doub
     sh[3][w] = d;
   }
   __syncthreads();
-  a = sh[0][0];
-  b = sh[1][0];
-  c = sh[2][0];
-  d = sh[3][0];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) {
-    a += sh[0][i];
-    b += sh[1][i];
-    c += sh[2][i];
-    d += sh[3][i];
+  if (threadIdx.x == 0) {
+    a = sh[0][0];
+    b = sh[1][0];
+    c = sh[2][0];
+    d = sh[3][0];
+#pragma unroll 1
+    for (int i = 1; i < NW; ++i) {
+      a += sh[0][i];
+      b += sh[1][i];
+      c += sh[2][i];
+      d += sh[3][i];
+    }
   }
 }
 
@@ -244,7 +273,7 @@ __device__ void careful_row(const char* cur, const char* prv, int64_t V, Shared<
     }
   }
   double Z = z, A = a, B = b, Z2 = z2;
-  block_sum4<NT>(Z, A, B, Z2, sh.d);
+  block_sum4_to0<NT>(Z, A, B, Z2, sh.d);
   if constexpr (PREV) inf_kl = dlm::block_max_i<NT>(inf_kl, sh.i);
   if (tid == 0) {
     const double lz = log(Z);
@@ -262,27 +291,82 @@ __device__ void careful_row(const char* cur, const char* prv, int64_t V, Shared<
   }
 }
 
+// Partial statistics of one split of a row: sums relative to the split's
+// integer reference h = ceil(m * log2 e), its max m and lowest argmax index.
+struct Partial {
+  double Z, A, B, Z2;
+  float m, h;
+  int cand, pad;
+};
+
+struct StatsArgs {
+  const void* logits;
+  const void* prev;
+  int64_t V, ld;
+  const int64_t* row_index;
+  float *conf, *ent, *kl, *lse;
+  int32_t* argmax;
+  int aligned, splits;
+  int* counters;     // [rows], zero between calls
+  Partial* parts;    // [rows][splits]
+};
+
+// Turn row totals (relative to the integer reference hM) into the outputs.
+// Returns false when a total is not finite (or the previous row's mass is out
+// of the reference's range): the caller then runs the element-wise path.
+template <bool PREV>
+__device__ __forceinline__ bool finalize(const StatsArgs& p, int64_t r, float M, float hM,
+                                         int yhat, double Z, double A, double B, double Z2) {
+  bool ok = isfinite(Z) && Z > 0.0 && isfinite(A) && M > kLow && isfinite(M) && yhat >= 0 &&
+            yhat != INT32_MAX;
+  // Z2 below 2^-60 would mean the previous row's mass sits far below the
+  // current row's reference, where fp32 terms lose precision: exact path.
+  if constexpr (PREV) ok = ok && isfinite(B) && isfinite(Z2) && Z2 >= 0x1p-60;
+  if (!ok) return false;
+  // Z_true = Z * 2^cM with cM = hM - M*log2e in [0, 1]: conf and lse need it;
+  // entropy does not (it cancels) and KL uses a common reference.
+  const double cM = static_cast<double>(hM) - static_cast<double>(M) * kL2Ed;
+  const double lz = log(Z);
+  p.argmax[r] = yhat;
+  p.lse[r] = static_cast<float>(static_cast<double>(M) + lz + kLN2 * cM);
+  p.conf[r] = static_cast<float>(exp2(-cM) / Z);
+  p.ent[r] = static_cast<float>(lz - kLN2 * (A / Z));
+  if constexpr (PREV) p.kl[r] = static_cast<float>(B / Z + log(Z2 / Z));
+  return true;
+}
+
+template <typename T>
+__device__ __forceinline__ void st_agent(T* a, T v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_agent(T* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One workgroup per (row, split).  With splits == 1 the workgroup owns the
+// whole row.  Otherwise each split streams a contiguous range of the row's
+// chunks and publishes a Partial; the row's last-arriving workgroup (atomic
+// counter) merges the partials in split order — the same order whichever
+// workgroup arrives last — and resets the counter to zero.
 template <int NT, bool BF16, bool PREV>
-__global__ __launch_bounds__(NT) void k_stats(const void* __restrict__ logits,
-                                              const void* __restrict__ prev, int64_t V,
-                                              int64_t ld, const int64_t* __restrict__ row_index,
-                                              float* __restrict__ conf,
-                                              int32_t* __restrict__ argmax,
-                                              float* __restrict__ ent, float* __restrict__ kl,
-                                              float* __restrict__ lse, int aligned) {
+__global__ __launch_bounds__(NT) void k_stats(const StatsArgs p) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int VEC = 16 / ES;          // elements per 16-byte chunk
-  constexpr int U = BF16 ? 2 : 4;       // chunks per lane per segment
+  constexpr int U = BF16 ? DLM_STATS_U_BF16 : 4;  // chunks per lane per segment
   __shared__ Shared<NT> sh;
 
-  const int64_t r = blockIdx.x;
-  const int64_t off = row_index[r] * ld;
-  const char* cur = static_cast<const char*>(logits) + off * ES;
-  const char* prv = PREV ? static_cast<const char*>(prev) + off * ES : nullptr;
+  const int S = p.splits;
+  const int64_t r = blockIdx.x / S;
+  const int s = static_cast<int>(blockIdx.x % S);
+  const int64_t V = p.V;
+  const int64_t off = p.row_index[r] * p.ld;
+  const char* cur = static_cast<const char*>(p.logits) + off * ES;
+  const char* prv = PREV ? static_cast<const char*>(p.prev) + off * ES : nullptr;
   const int tid = threadIdx.x;
 
-  if (!aligned) {
-    careful_row<NT, BF16, PREV>(cur, prv, V, sh, r, conf, argmax, ent, kl, lse);
+  if (!p.aligned) {  // the host never splits unaligned rows
+    careful_row<NT, BF16, PREV>(cur, prv, V, sh, r, p.conf, p.argmax, p.ent, p.kl, p.lse);
     return;
   }
 
@@ -290,11 +374,12 @@ __global__ __launch_bounds__(NT) void k_stats(const void* __restrict__ logits,
   const uint4* prv4 = reinterpret_cast<const uint4*>(prv);
   const int64_t nC = V / VEC;
   const int tail = static_cast<int>(V - nC * VEC);
+  const int64_t c_lo = nC * s / S, c_hi = nC * (s + 1) / S;  // this split's chunks
+  const int64_t n_c = c_hi - c_lo;
   constexpr int64_t SEG = static_cast<int64_t>(U) * NT;
-  const int64_t n_full = nC / SEG;
+  const int64_t n_full = n_c / SEG;
 
-  CurState c{kLow, kLow * kL2E, 0.f, 0.f, 0.f, -1, VEC};  // h sentinel: integral
-  PrvState p{kLow, kLow * kL2E, 0.f};
+  LaneState c{kLow, kLow * kL2E, 0.f, 0.f, 0.f, 0.f, -1, VEC};  // sentinel h is integral
   bool allv[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) allv[u] = true;
@@ -305,65 +390,64 @@ __global__ __launch_bounds__(NT) void k_stats(const void* __restrict__ logits,
   if (n_full > 0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      qc[u] = cur4[u * NT + tid];
-      if constexpr (PREV) qp[u] = prv4[u * NT + tid];
+      qc[u] = load16(cur4 + c_lo + u * NT + tid);
+      if constexpr (PREV) qp[u] = load16(prv4 + c_lo + u * NT + tid);
     }
   }
   for (int64_t it = 0; it < n_full; ++it) {
-    float x[U][VEC], y[U][VEC];
+    float x[U][VEC];
+    uint4 yq[U];
     int64_t st[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       unpack<BF16>(qc[u], x[u]);
-      if constexpr (PREV) unpack<BF16>(qp[u], y[u]);
-      st[u] = (it * SEG + u * NT + tid) * VEC;
+      if constexpr (PREV) yq[u] = qp[u];
+      st[u] = (c_lo + it * SEG + u * NT + tid) * VEC;
     }
     if (it + 1 < n_full) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t ch = (it + 1) * SEG + u * NT + tid;
-        qc[u] = cur4[ch];
-        if constexpr (PREV) qp[u] = prv4[ch];
+        const int64_t ch = c_lo + (it + 1) * SEG + u * NT + tid;
+        qc[u] = load16(cur4 + ch);
+        if constexpr (PREV) qp[u] = load16(prv4 + ch);
       }
     }
-    fold<U, VEC, PREV>(c, p, x, y, allv, st);
+    fold<U, VEC, BF16, PREV>(c, x, yq, nullptr, allv, st);
   }
-  // last, partial segment
-  if (n_full * SEG < nC) {
-    float x[U][VEC], y[U][VEC];
+  // last, partial segment of this split
+  if (n_full * SEG < n_c) {
+    float x[U][VEC];
+    uint4 yq[U];
     int64_t st[U];
     bool val[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t ch = n_full * SEG + u * NT + tid;
-      val[u] = ch < nC;
+      const int64_t ch = c_lo + n_full * SEG + u * NT + tid;
+      val[u] = ch < c_hi;
       uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
       if (val[u]) {
-        a = cur4[ch];
-        if constexpr (PREV) b = prv4[ch];
+        a = load16(cur4 + ch);
+        if constexpr (PREV) b = load16(prv4 + ch);
       }
       unpack<BF16>(a, x[u]);
-      if constexpr (PREV) unpack<BF16>(b, y[u]);
+      yq[u] = b;
       st[u] = ch * VEC;
     }
-    fold<U, VEC, PREV>(c, p, x, y, val, st);
+    fold<U, VEC, BF16, PREV>(c, x, yq, nullptr, val, st);
   }
-  // scalar tail elements (vocab not a multiple of the chunk width)
-  if (tid < tail) {
+  // scalar tail elements (vocab not a multiple of the chunk width): last split
+  if (s == S - 1 && tid < tail) {
     const int64_t v = nC * VEC + tid;
-    float x[1][1], y[1][1];
+    float x[1][1];
     x[0][0] = load_elem<BF16>(cur, v);
-    y[0][0] = PREV ? load_elem<BF16>(prv, v) : 0.f;
+    const float y = PREV ? load_elem<BF16>(prv, v) : 0.f;
     const bool val[1] = {true};
     const int64_t st[1] = {v};
-    fold<1, 1, PREV>(c, p, x, y, val, st);
-    if (c.best == v) c.bestw = 1;
+    fold<1, 1, BF16, PREV>(c, x, nullptr, &y, val, st);
   }
 
   // ---- combine lanes
   const float M = dlm::block_max<NT>(c.m, sh.f);
-  float M2 = 0.f;
-  if constexpr (PREV) M2 = dlm::block_max<NT>(p.m, sh.f);
   int cand = INT32_MAX;
   if (c.m == M && c.best >= 0) {
     if (c.bestw == 1) {
@@ -378,7 +462,7 @@ __global__ __launch_bounds__(NT) void k_stats(const void* __restrict__ logits,
   }
   const int yhat = dlm::block_min_i<NT>(cand, sh.i);
 
-  // Lane sums relative to the row's integer reference hM = ceil(M*log2e):
+  // Lane sums relative to the workgroup's integer reference hM = ceil(M*log2e):
   // exact power-of-two scaling.  Sentinel lanes (no finite data) scale to 0.
   const float hM = ceilf(M * kL2E);
   const int di = static_cast<int>(fmaxf(c.h - hM, -1100.f));
@@ -386,92 +470,150 @@ __global__ __launch_bounds__(NT) void k_stats(const void* __restrict__ logits,
   double A = ldexp(static_cast<double>(c.A) + static_cast<double>(c.h - hM) *
                                                  static_cast<double>(c.Z), di);
   double B = 0.0, Z2 = 0.0;
-  float hM2 = 0.f;
   if constexpr (PREV) {
     B = ldexp(static_cast<double>(c.B), di);
-    hM2 = ceilf(M2 * kL2E);
-    Z2 = ldexp(static_cast<double>(p.Z), static_cast<int>(fmaxf(p.h - hM2, -1100.f)));
+    Z2 = ldexp(static_cast<double>(c.Z2), di);
   }
-  block_sum4<NT>(Z, A, B, Z2, sh.d);
+  block_sum4_to0<NT>(Z, A, B, Z2, sh.d);
+
+  if (S == 1) {
+    if (tid == 0) sh.flag = finalize<PREV>(p, r, M, hM, yhat, Z, A, B, Z2);
+    __syncthreads();
+    if (!sh.flag)
+      careful_row<NT, BF16, PREV>(cur, prv, V, sh, r, p.conf, p.argmax, p.ent, p.kl, p.lse);
+    return;
+  }
+
+  // ---- publish this split; the last workgroup of the row merges
   if (tid == 0) {
-    bool ok = isfinite(Z) && Z > 0.0 && isfinite(A) && M > kLow && isfinite(M) && yhat >= 0 &&
-              yhat != INT32_MAX;
-    if constexpr (PREV)
-      ok = ok && isfinite(B) && isfinite(Z2) && Z2 > 0.0 && M2 > kLow && isfinite(M2);
-    sh.flag = ok;
-    if (ok) {
-      // Z_true = Z * 2^cM with cM = hM - M*log2e in [0, 1]: conf and lse need
-      // it; entropy does not (it cancels); KL needs cM2 - cM.
-      const double cM = static_cast<double>(hM) - static_cast<double>(M) * kL2Ed;
-      const double lz = log(Z);
-      argmax[r] = yhat;
-      lse[r] = static_cast<float>(static_cast<double>(M) + lz + kLN2 * cM);
-      conf[r] = static_cast<float>(exp2(-cM) / Z);
-      ent[r] = static_cast<float>(lz - kLN2 * (A / Z));
-      if constexpr (PREV) {
-        const double cM2 = static_cast<double>(hM2) - static_cast<double>(M2) * kL2Ed;
-        kl[r] = static_cast<float>(B / Z + (static_cast<double>(M2) - static_cast<double>(M)) +
-                                   log(Z2 / Z) + kLN2 * (cM2 - cM));
-      }
-    }
+    Partial* mine = p.parts + r * S + s;
+    st_agent(&mine->Z, Z);
+    st_agent(&mine->A, A);
+    st_agent(&mine->B, B);
+    st_agent(&mine->Z2, Z2);
+    st_agent(&mine->m, M);
+    st_agent(&mine->h, hM);
+    st_agent(&mine->cand, yhat);
+    __threadfence();  // release the partial before counting in
+    const int arrived = atomicAdd(p.counters + r, 1);
+    sh.flag = arrived == S - 1 ? 1 : 0;
   }
   __syncthreads();
-  if (!sh.flag) careful_row<NT, BF16, PREV>(cur, prv, V, sh, r, conf, argmax, ent, kl, lse);
+  if (!sh.flag) return;  // not the last split of this row (uniform)
+  if (tid == 0) {
+    __threadfence();  // acquire the other splits' partials
+    Partial* row = p.parts + r * S;
+    float Mr = kLow;
+    for (int k = 0; k < S; ++k) Mr = fmaxf(Mr, ld_agent(&row[k].m));
+    const float hR = ceilf(Mr * kL2E);
+    double Zr = 0.0, Ar = 0.0, Br = 0.0, Z2r = 0.0;
+    int yr = INT32_MAX;
+    for (int k = 0; k < S; ++k) {  // split order: deterministic
+      const float mk = ld_agent(&row[k].m);
+      const float hk = ld_agent(&row[k].h);
+      const double zk = ld_agent(&row[k].Z);
+      const double d = static_cast<double>(hk - hR);
+      const int dk = static_cast<int>(fmax(d, -1100.0));
+      Zr += ldexp(zk, dk);
+      Ar += ldexp(ld_agent(&row[k].A) + d * zk, dk);
+      if constexpr (PREV) {
+        Br += ldexp(ld_agent(&row[k].B), dk);
+        Z2r += ldexp(ld_agent(&row[k].Z2), dk);
+      }
+      const int ck = ld_agent(&row[k].cand);
+      if (mk == Mr && ck < yr) yr = ck;
+    }
+    st_agent(p.counters + r, 0);  // ready for the next call
+    sh.flag = finalize<PREV>(p, r, Mr, hR, yr, Zr, Ar, Br, Z2r);
+  }
+  __syncthreads();
+  if (!sh.flag)
+    careful_row<NT, BF16, PREV>(cur, prv, V, sh, r, p.conf, p.argmax, p.ent, p.kl, p.lse);
 }
 
 template <int NT, bool BF16>
-hipError_t launch_nt(const void* logits, const void* prev, int64_t V, int64_t ld,
-                     const int64_t* row_index, int64_t n_rows, float* conf, int32_t* argmax,
-                     float* ent, float* kl, float* lse, int aligned, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(n_rows));
-  if (prev)
-    hipLaunchKernelGGL((k_stats<NT, BF16, true>), grid, dim3(NT), 0, s, logits, prev, V, ld,
-                       row_index, conf, argmax, ent, kl, lse, aligned);
+hipError_t launch_nt(const StatsArgs& a, int64_t n_rows, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(n_rows * a.splits));
+  if (a.prev)
+    hipLaunchKernelGGL((k_stats<NT, BF16, true>), grid, dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL((k_stats<NT, BF16, false>), grid, dim3(NT), 0, s, logits, prev, V, ld,
-                       row_index, conf, argmax, ent, kl, lse, aligned);
+    hipLaunchKernelGGL((k_stats<NT, BF16, false>), grid, dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
 template <bool BF16>
-hipError_t launch_dt(int nt, const void* logits, const void* prev, int64_t V, int64_t ld,
-                     const int64_t* row_index, int64_t n_rows, float* conf, int32_t* argmax,
-                     float* ent, float* kl, float* lse, int aligned, hipStream_t s) {
+hipError_t launch_dt(int nt, const StatsArgs& a, int64_t n_rows, hipStream_t s) {
   switch (nt) {
     case 256:
-      return launch_nt<256, BF16>(logits, prev, V, ld, row_index, n_rows, conf, argmax, ent,
-                                  kl, lse, aligned, s);
-    case 512:
-      return launch_nt<512, BF16>(logits, prev, V, ld, row_index, n_rows, conf, argmax, ent,
-                                  kl, lse, aligned, s);
+      return launch_nt<256, BF16>(a, n_rows, s);
+    case 1024:
+      return launch_nt<1024, BF16>(a, n_rows, s);
     default:
-      return launch_nt<1024, BF16>(logits, prev, V, ld, row_index, n_rows, conf, argmax, ent,
-                                   kl, lse, aligned, s);
+      return launch_nt<512, BF16>(a, n_rows, s);
   }
 }
 
-// Threads per row: enough waves in flight to cover HBM latency.  Few rows
-// (one step of one sequence) get the widest workgroups; many rows get
-// narrower ones so several rows share a CU.
-int threads_per_row(int64_t n_rows) {
-  static int forced = -1;
-  if (forced < 0) {
+constexpr int kMaxSplits = 8;
+constexpr size_t kCounterAlign = 256;
+
+size_t counters_bytes(int64_t n_rows) {
+  const size_t b = static_cast<size_t>(n_rows) * sizeof(int);
+  return (b + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
+}
+size_t bytes_for(int64_t rows) {
+  return counters_bytes(rows) + static_cast<size_t>(rows) * kMaxSplits * sizeof(Partial);
+}
+// Rows a workspace of `bytes` serves.  The layout (counters, then partials)
+// depends on the workspace size only, never on the call's row count, so calls
+// with different row counts can share one zero-filled buffer.
+int64_t workspace_rows(size_t bytes) {
+  int64_t c = static_cast<int64_t>(bytes / (sizeof(int) + kMaxSplits * sizeof(Partial)));
+  while (c > 0 && bytes_for(c) > bytes) --c;
+  return c;
+}
+
+// Threads per row and splits per row.  Many rows: one workgroup per row (256
+// threads from 4096 rows up, else 512).  Very few rows (<= 64) with a
+// workspace: split each row so that the launch has about one workgroup per
+// CU.  Splitting more rows than that costs more than it gains: each split's
+// agent-scope release/acquire writes back / invalidates its XCD's L2 while
+// the other workgroups stream through it.
+void launch_shape(int64_t n_rows, int64_t n_chunks, bool can_split, int* nt, int* splits) {
+  static int forced_nt = -1, forced_s = -1;
+  if (forced_nt < 0) {
     const char* e = getenv("DLM_STATS_THREADS");
     const int v = e ? atoi(e) : 0;
-    forced = (v == 256 || v == 512 || v == 1024) ? v : 0;
+    forced_nt = (v == 256 || v == 512 || v == 1024) ? v : 0;
+    const char* f = getenv("DLM_STATS_SPLITS");
+    const int w = f ? atoi(f) : 0;
+    forced_s = (w >= 1 && w <= kMaxSplits) ? w : 0;
   }
-  if (forced) return forced;
-  if (n_rows >= 4096) return 256;
-  if (n_rows >= 1024) return 512;
-  return 1024;
+  *nt = n_rows >= 4096 ? 256 : 512;
+  int sp = 1;
+  if (can_split && n_rows <= 64) {
+    sp = static_cast<int>((256 + n_rows - 1) / n_rows);
+    if (sp > kMaxSplits) sp = kMaxSplits;
+    // each split should keep every lane busy for at least two segments
+    const int64_t cap = n_chunks / (2 * 2 * 512);
+    if (sp > cap) sp = static_cast<int>(cap < 1 ? 1 : cap);
+  }
+  if (forced_nt) *nt = forced_nt;
+  if (forced_s && can_split) sp = forced_s;
+  *splits = sp;
 }
 
 }  // namespace
 
+extern "C" size_t dlm_step_stats_workspace_bytes(int64_t n_rows) {
+  if (n_rows <= 0 || n_rows > 2147483647LL) return 0;
+  return bytes_for(n_rows);
+}
+
 extern "C" int dlm_step_stats(const void* logits, const void* prev_logits, int dtype,
                               int64_t vocab, int64_t ld, const int64_t* row_index,
                               int64_t n_rows, float* conf, int32_t* argmax, float* entropy,
-                              float* kl, float* lse, void* stream) {
+                              float* kl, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   if (!logits || !row_index || !conf || !argmax || !entropy || !lse) return DLM_ERR_ARG;
   if ((prev_logits == nullptr) != (kl == nullptr)) return DLM_ERR_ARG;
   if (dtype != DLM_BF16 && dtype != DLM_F32) return DLM_ERR_UNSUPPORTED;
@@ -481,15 +623,21 @@ extern "C" int dlm_step_stats(const void* logits, const void* prev_logits, int d
   const uintptr_t a = reinterpret_cast<uintptr_t>(logits);
   const uintptr_t b = reinterpret_cast<uintptr_t>(prev_logits);
   if (a % es || b % es) return DLM_ERR_ARG;
+  if (workspace) {
+    if (reinterpret_cast<uintptr_t>(workspace) % 16) return DLM_ERR_ARG;
+    if (workspace_bytes < dlm_step_stats_workspace_bytes(n_rows)) return DLM_ERR_ARG;
+  }
   const int aligned = (a % 16 == 0) && (b % 16 == 0) && ((ld * es) % 16 == 0);
+  int nt, splits;
+  launch_shape(n_rows, vocab / (16 / es), workspace != nullptr && aligned, &nt, &splits);
+  StatsArgs args{logits, prev_logits, vocab, ld, row_index, conf, entropy, kl, lse, argmax,
+                 aligned, splits, static_cast<int*>(workspace),
+                 workspace ? reinterpret_cast<Partial*>(
+                                 static_cast<char*>(workspace) +
+                                 counters_bytes(workspace_rows(workspace_bytes)))
+                           : nullptr};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int nt = threads_per_row(n_rows);
-  hipError_t err;
-  if (dtype == DLM_BF16)
-    err = launch_dt<true>(nt, logits, prev_logits, vocab, ld, row_index, n_rows, conf, argmax,
-                          entropy, kl, lse, aligned, s);
-  else
-    err = launch_dt<false>(nt, logits, prev_logits, vocab, ld, row_index, n_rows, conf, argmax,
-                           entropy, kl, lse, aligned, s);
+  const hipError_t err = dtype == DLM_BF16 ? launch_dt<true>(nt, args, n_rows, s)
+                                           : launch_dt<false>(nt, args, n_rows, s);
   return err == hipSuccess ? DLM_OK : DLM_ERR_HIP;
 }

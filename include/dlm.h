@@ -107,11 +107,24 @@ extern "C" {
  * vocab: 1 <= vocab < 2^31; ld >= vocab.
  * row_index (device int64 [n_rows]); n_rows >= 1.
  * conf, entropy, kl, lse (device f32 [n_rows]); argmax (device int32 [n_rows]).
+ * workspace (device, optional): NULL, or at least
+ *   dlm_step_stats_workspace_bytes(n_rows) bytes, 16-byte aligned and
+ *   zero-filled before its first use; every call leaves its counters zero
+ *   again.  Its layout depends on workspace_bytes only, so one buffer (always
+ *   passed with the same size) serves calls with any row count it covers.
+ *   With a workspace, launches of few rows split each row over several
+ *   workgroups (the last one merges, always in the same order, so results do
+ *   not depend on which finishes first); without one, one workgroup per row.
+ *   Calls that overlap in time must not share a workspace.
  * Floating point: fp32 element arithmetic with fp64 cross-lane combination.
  */
 int dlm_step_stats(const void* logits, const void* prev_logits, int dtype, int64_t vocab,
                    int64_t ld, const int64_t* row_index, int64_t n_rows, float* conf,
-                   int32_t* argmax, float* entropy, float* kl, float* lse, void* stream);
+                   int32_t* argmax, float* entropy, float* kl, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Workspace bytes dlm_step_stats may use for n_rows rows (0 if n_rows is invalid). */
+size_t dlm_step_stats_workspace_bytes(int64_t n_rows);
 
 /*
  * dlm_fastdllm_select — [FastR, Method]; [FastN, Key ideas, Technical details]:

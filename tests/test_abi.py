@@ -31,7 +31,8 @@ def test_status_strings(L):
 
 def test_step_stats_validation(L):
     f = L.dlm_step_stats
-    args = [FAKE, None, _lib.BF16, 1000, 1000, FAKE, 4, FAKE, FAKE, FAKE, None, FAKE, None]
+    args = [FAKE, None, _lib.BF16, 1000, 1000, FAKE, 4, FAKE, FAKE, FAKE, None, FAKE, None, 0,
+            None]
     bad = list(args)
     bad[0] = None
     assert f(*bad) == _lib.ERR_ARG                      # NULL logits
@@ -54,6 +55,13 @@ def test_step_stats_validation(L):
     bad[3] = 2**31
     bad[4] = 2**31
     assert f(*bad) == _lib.ERR_UNSUPPORTED              # vocab >= 2^31
+    need = L.dlm_step_stats_workspace_bytes(4)
+    assert need > 0 and L.dlm_step_stats_workspace_bytes(0) == 0
+    bad = list(args)
+    bad[12], bad[13] = FAKE, need - 1
+    assert f(*bad) == _lib.ERR_ARG                      # workspace too small
+    bad[12], bad[13] = FAKE + 8, need
+    assert f(*bad) == _lib.ERR_ARG                      # workspace misaligned
 
 
 def test_rule_validation(L):
@@ -83,7 +91,9 @@ def test_rule_validation(L):
 
 
 def test_dapd_validation(L):
-    assert L.dlm_dapd_workspace_bytes(8, 256) == 2 * 8 * 256 * 256 * 4
+    # a and its transpose (fp32) plus the adjacency bitsets, keys and edge flags
+    assert L.dlm_dapd_workspace_bytes(8, 256) >= 2 * 8 * 256 * 256 * 4 + 8 * 256 * (32 + 8 + 1)
+    assert L.dlm_dapd_workspace_bytes(8, 256) % 256 == 0
     assert L.dlm_dapd_workspace_bytes(1, 1025) == 0
     assert L.dlm_dapd_workspace_bytes(0, 10) == 0
     f = L.dlm_dapd_select

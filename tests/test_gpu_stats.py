@@ -120,3 +120,42 @@ def test_full_size_sampled(name, sample):
     assert bool(torch.all(H >= -1e-5)) and bool(torch.all(H <= np.log(V) + 1e-5))
     if prev is not None:
         assert bool(torch.all(out["kl"] >= -1e-5))
+
+
+@pytest.mark.parametrize("rows,vocab", [(1, 126464), (3, 126467), (37, 100003), (256, 126464)])
+def test_split_rows_match_oracle_and_repeat(rows, vocab):
+    # few rows over a wide vocabulary: each row is split over several
+    # workgroups and merged by the last one to arrive
+    spec = synth.Spec("split", 12, 1, rows, vocab, torch.bfloat16, 2.0, 0.6, 12.0, 0.5)
+    cur, prev, so, ri = synth.logits(spec, DEV)
+    out, ref = _compare(cur, prev, tag=f"split {rows}x{vocab} ")
+    single = api.step_stats(cur, prev, split=False)
+    for k in ("conf", "entropy", "kl", "lse"):
+        assert_close(single[k], ref[k], f"single-workgroup {k}")
+    assert torch.equal(single["argmax"], out["argmax"])
+    for _ in range(3):                                    # arrival order must not matter
+        again = api.step_stats(cur, prev)
+        for k in ("conf", "entropy", "kl", "lse", "argmax"):
+            assert torch.equal(out[k], again[k]), f"split {k} not bitwise reproducible"
+
+
+def test_split_rows_non_finite():
+    spec = synth.Spec("splitnf", 13, 1, 6, 126464, torch.float32, 2.0, 0.6, 12.0, 0.5)
+    cur, prev, so, ri = synth.logits(spec, DEV)
+    cur[0, 100000] = float("nan")                       # in a late split
+    cur[1, 5:] = float("-inf")                          # -inf across every split
+    prev[2, 120000] = float("-inf")                     # KL = +inf
+    cur[3, 126463] = cur[3].max() + 2.0                 # max in the last element
+    cur[4, 0] = cur[4].max() + 2.0                      # max in the first element
+    _compare(cur.to(torch.bfloat16), prev.to(torch.bfloat16), tag="split non-finite bf16 ")
+    _compare(cur, prev, tag="split non-finite f32 ")
+
+
+def test_one_workspace_serves_any_row_count():
+    # a 37-row call leaves its partials where a 256-row layout would put
+    # counters if the layout depended on the row count; it must not
+    outs = []
+    for rows in (37, 256, 3, 256, 37):
+        spec = synth.Spec("mix", 14 + rows, 1, rows, 126464, torch.bfloat16, 2.0, 0.6, 12.0, 0.5)
+        cur, prev, so, ri = synth.logits(spec, DEV)
+        outs.append(_compare(cur, prev, tag=f"shared workspace {rows} rows "))
