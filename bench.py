@@ -230,6 +230,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-iters", type=int, default=200)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 10 plain device-to-device copies of MIB MiB (the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
                     help="graph: the step is captured once per input replica and replayed")
     args = ap.parse_args()
@@ -245,6 +248,15 @@ def main() -> int:
         return 2
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.randint(0, 255, (n,), device=dev, dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n, "copies": 10}), flush=True)
+        return 0
     step = LladaStep(args.replicas, dev)
     R = args.replicas
     sm = step.torch_stream
