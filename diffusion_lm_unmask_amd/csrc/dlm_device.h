@@ -39,6 +39,57 @@ __device__ __forceinline__ int wave_max_i(int v) {
   return v;
 }
 
+// Wave reductions on the DPP crossbar (no LDS traffic).  Inside each row of
+// 16 lanes, four steps pair every lane with one lane of the other half of its
+// current group: quad swaps (xor 1, xor 2), then the half-row mirror (i with
+// 7-i) and the row mirror (i with 15-i).  Each lane then holds its row's
+// total, bitwise equal across the row because + , max and min are
+// commutative.  The four row totals (lanes 0, 16, 32, 48) are combined in a
+// fixed order and returned to every lane.  Call with all 64 lanes active.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(dpp<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = dpp<CTRL>(static_cast<int>(b));
+  const int hi = dpp<CTRL>(static_cast<int>(b >> 32));
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+__device__ __forceinline__ int rdlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float rdlane(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double rdlane(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), l);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), l);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = op(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp<0x141>(v));  // row_half_mirror
+  v = op(v, dpp<0x140>(v));  // row_mirror
+  return op(op(rdlane(v, 0), rdlane(v, 16)), op(rdlane(v, 32), rdlane(v, 48)));
+}
+struct OpAdd {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a + b; }
+};
+struct OpMaxF {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpMinI {
+  __device__ int operator()(int a, int b) const { return min(a, b); }
+};
+
 // Workgroup reductions. `sh` must hold NT/64 elements; every thread gets the
 // result.  Each call ends with a barrier-protected read, so `sh` may be
 // reused by the next call after it returns (the leading barrier covers it).

@@ -19,9 +19,12 @@
 //    (ldexp) in fp64 relative to the row's integer reference, and the
 //    fractional offset between that reference and the row max is applied
 //    once, in fp64, when the statistics are formed;
-//  * the argmax costs one compare per chunk in the hot loop: a lane records
-//    the first chunk where its running max strictly grew; only lanes whose
-//    max equals the row max re-read that one chunk to find the element;
+//  * the argmax costs one compare and a register copy per chunk in the hot
+//    loop: a lane keeps the raw bits of the first chunk where its running max
+//    strictly grew, and finds the element in it after the stream, without a
+//    second memory access;
+//  * lanes are merged per wave on the DPP crossbar, waves through one LDS
+//    record each and a single barrier;
 //  * any non-finite total (NaN/inf entries, -inf logits, empty rows) sends
 //    the row to an element-wise path that applies the definitions'
 //    conventions exactly (0 log 0 = 0, q = 0 with p > 0 gives KL = +inf).
@@ -100,17 +103,19 @@ struct LaneState {
   float m, h;       // running max of the current row, integer reference
   float Z, A, B;    // sum e, sum e*t (log2 units), sum e*(x - y)
   float Z2;         // sum 2^(y*log2e - h)
-  int64_t best;     // first element index of the chunk holding the lane max
+  int best;         // first element index of the chunk holding the lane max
   int bestw;        // width of that chunk (VEC, or 1 for a tail element)
+  uint4 bq;         // raw bits of that chunk (VEC > 1)
 };
 
 // Fold NSUB sub-blocks of W values into the lane state.  qc/qp hold the raw
-// chunks (W values each); x is the unpacked current row; `valid` masks whole
-// sub-blocks; start[u] is the element index of sub-block u (argmax record).
+// chunks (W values each; qc is unused for W == 1); x is the unpacked current
+// row; `valid` masks whole sub-blocks; start[u] is the element index of
+// sub-block u (argmax record).
 template <int NSUB, int W, bool BF16, bool PREV>
-__device__ __forceinline__ void fold(LaneState& c, const float (*x)[W], const uint4* qp,
-                                     const float* ys, const bool* valid,
-                                     const int64_t* start) {
+__device__ __forceinline__ void fold(LaneState& c, const float (*x)[W], const uint4* qc,
+                                     const uint4* qp, const float* ys, const bool* valid,
+                                     const int* start) {
   // segment maxima and the first-strict-increase chunk record
   float mr = c.m;
 #pragma unroll
@@ -122,6 +127,7 @@ __device__ __forceinline__ void fold(LaneState& c, const float (*x)[W], const ui
       if (cm > mr) {
         c.best = start[u];
         c.bestw = W;
+        if constexpr (W > 1) c.bq = qc[u];
       }
       mr = fmaxf(mr, cm);
     }
@@ -200,11 +206,21 @@ __device__ __forceinline__ void block_sum4_to0(double& a, double& b, double& c, 
   }
 }
 
+// Partial statistics of one wave, workgroup or split of a row: its max m,
+// the lowest index holding m, and sums relative to its integer reference
+// h = ceil(m * log2 e).
+struct Partial {
+  double Z, A, B, Z2;
+  float m, h;
+  int cand, pad;
+};
+
 template <int NT>
 struct Shared {
   float f[NT / DLM_WAVE];
   int i[NT / DLM_WAVE];
   double d[4][NT / DLM_WAVE];
+  Partial rec[NT / DLM_WAVE];
   int flag;
 };
 
@@ -291,14 +307,6 @@ __device__ void careful_row(const char* cur, const char* prv, int64_t V, Shared<
   }
 }
 
-// Partial statistics of one split of a row: sums relative to the split's
-// integer reference h = ceil(m * log2 e), its max m and lowest argmax index.
-struct Partial {
-  double Z, A, B, Z2;
-  float m, h;
-  int cand, pad;
-};
-
 struct StatsArgs {
   const void* logits;
   const void* prev;
@@ -311,27 +319,75 @@ struct StatsArgs {
   Partial* parts;    // [rows][splits]
 };
 
-// Turn row totals (relative to the integer reference hM) into the outputs.
+// Sums taken relative to the integer reference h, moved to the reference
+// hn >= h: an exact power-of-two scaling (terms that fall below the double
+// range, such as those of lanes that saw no finite data, become zero).
+__device__ __forceinline__ void rebase(double& Z, double& A, double& B, double& Z2, float h,
+                                       float hn) {
+  const double d = static_cast<double>(h) - static_cast<double>(hn);  // integer <= 0
+  const int di = static_cast<int>(fmax(d, -1100.0));
+  A = ldexp(fma(d, Z, A), di);
+  Z = ldexp(Z, di);
+  B = ldexp(B, di);
+  Z2 = ldexp(Z2, di);
+}
+
+// Merge n partial records (got in index order 0..n-1, a fixed order) into
+// one: the max, the lowest index among records holding it, and the sums
+// relative to the max's integer reference.
+template <bool PREV, typename Get>
+__device__ __forceinline__ Partial merge(int n, Get get) {
+  Partial t;
+  t.m = kLow;
+  for (int k = 0; k < n; ++k) t.m = fmaxf(t.m, get(k).m);
+  t.h = ceilf(t.m * kL2E);
+  t.cand = INT32_MAX;
+  t.Z = t.A = t.B = t.Z2 = 0.0;
+  for (int k = 0; k < n; ++k) {
+    const Partial q = get(k);
+    double Z = q.Z, A = q.A, B = q.B, Z2 = q.Z2;
+    rebase(Z, A, B, Z2, q.h, t.h);
+    t.Z += Z;
+    t.A += A;
+    if constexpr (PREV) {
+      t.B += B;
+      t.Z2 += Z2;
+    }
+    if (q.m == t.m && q.cand < t.cand) t.cand = q.cand;
+  }
+  return t;
+}
+
+// log2 of a positive finite double: exact exponent plus an fp32 log2 of the
+// mantissa in [0.5, 1) (absolute error about 1e-7).
+__device__ __forceinline__ double log2_split(double v) {
+  int e;
+  const double f = frexp(v, &e);
+  return static_cast<double>(e) + static_cast<double>(log2f(static_cast<float>(f)));
+}
+
+// Turn row totals (relative to the integer reference t.h) into the outputs.
 // Returns false when a total is not finite (or the previous row's mass is out
 // of the reference's range): the caller then runs the element-wise path.
 template <bool PREV>
-__device__ __forceinline__ bool finalize(const StatsArgs& p, int64_t r, float M, float hM,
-                                         int yhat, double Z, double A, double B, double Z2) {
-  bool ok = isfinite(Z) && Z > 0.0 && isfinite(A) && M > kLow && isfinite(M) && yhat >= 0 &&
-            yhat != INT32_MAX;
+__device__ __forceinline__ bool finalize(const StatsArgs& p, int64_t r, const Partial& t) {
+  const float M = t.m;
+  bool ok = isfinite(t.Z) && t.Z > 0.0 && isfinite(t.A) && M > kLow && isfinite(M) &&
+            t.cand >= 0 && t.cand != INT32_MAX;
   // Z2 below 2^-60 would mean the previous row's mass sits far below the
   // current row's reference, where fp32 terms lose precision: exact path.
-  if constexpr (PREV) ok = ok && isfinite(B) && isfinite(Z2) && Z2 >= 0x1p-60;
+  if constexpr (PREV) ok = ok && isfinite(t.B) && isfinite(t.Z2) && t.Z2 >= 0x1p-60;
   if (!ok) return false;
-  // Z_true = Z * 2^cM with cM = hM - M*log2e in [0, 1]: conf and lse need it;
+  // Z_true = Z * 2^cM with cM = h - M*log2e in [0, 1]: conf and lse need it;
   // entropy does not (it cancels) and KL uses a common reference.
-  const double cM = static_cast<double>(hM) - static_cast<double>(M) * kL2Ed;
-  const double lz = log(Z);
-  p.argmax[r] = yhat;
-  p.lse[r] = static_cast<float>(static_cast<double>(M) + lz + kLN2 * cM);
-  p.conf[r] = static_cast<float>(exp2(-cM) / Z);
-  p.ent[r] = static_cast<float>(lz - kLN2 * (A / Z));
-  if constexpr (PREV) p.kl[r] = static_cast<float>(B / Z + log(Z2 / Z));
+  const double cM = static_cast<double>(t.h) - static_cast<double>(M) * kL2Ed;
+  const double iz = 1.0 / t.Z;
+  const double l2z = log2_split(t.Z);
+  p.argmax[r] = t.cand;
+  p.lse[r] = static_cast<float>(static_cast<double>(M) + kLN2 * (l2z + cM));
+  p.conf[r] = static_cast<float>(static_cast<double>(exp2f(static_cast<float>(-cM))) * iz);
+  p.ent[r] = static_cast<float>(kLN2 * (l2z - t.A * iz));
+  if constexpr (PREV) p.kl[r] = static_cast<float>(t.B * iz + kLN2 * log2_split(t.Z2 * iz));
   return true;
 }
 
@@ -379,12 +435,13 @@ __global__ __launch_bounds__(NT) void k_stats(const StatsArgs p) {
   constexpr int64_t SEG = static_cast<int64_t>(U) * NT;
   const int64_t n_full = n_c / SEG;
 
-  LaneState c{kLow, kLow * kL2E, 0.f, 0.f, 0.f, 0.f, -1, VEC};  // sentinel h is integral
+  LaneState c{kLow, kLow * kL2E, 0.f, 0.f, 0.f, 0.f, -1, VEC, make_uint4(0u, 0u, 0u, 0u)};
+  // (the sentinel's h is integral)
   bool allv[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) allv[u] = true;
 
-  // software-pipelined full segments: loads of segment it+1 are issued
+  // software-pipelined full segments: the loads of segment it+1 are issued
   // before segment it is folded
   uint4 qc[U], qp[U];
   if (n_full > 0) {
@@ -396,13 +453,14 @@ __global__ __launch_bounds__(NT) void k_stats(const StatsArgs p) {
   }
   for (int64_t it = 0; it < n_full; ++it) {
     float x[U][VEC];
-    uint4 yq[U];
-    int64_t st[U];
+    uint4 xq[U], yq[U];
+    int st[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       unpack<BF16>(qc[u], x[u]);
+      xq[u] = qc[u];
       if constexpr (PREV) yq[u] = qp[u];
-      st[u] = (c_lo + it * SEG + u * NT + tid) * VEC;
+      st[u] = static_cast<int>((c_lo + it * SEG + u * NT + tid) * VEC);
     }
     if (it + 1 < n_full) {
 #pragma unroll
@@ -412,13 +470,13 @@ __global__ __launch_bounds__(NT) void k_stats(const StatsArgs p) {
         if constexpr (PREV) qp[u] = load16(prv4 + ch);
       }
     }
-    fold<U, VEC, BF16, PREV>(c, x, yq, nullptr, allv, st);
+    fold<U, VEC, BF16, PREV>(c, x, xq, yq, nullptr, allv, st);
   }
   // last, partial segment of this split
   if (n_full * SEG < n_c) {
     float x[U][VEC];
-    uint4 yq[U];
-    int64_t st[U];
+    uint4 xq[U], yq[U];
+    int st[U];
     bool val[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -430,10 +488,11 @@ __global__ __launch_bounds__(NT) void k_stats(const StatsArgs p) {
         if constexpr (PREV) b = load16(prv4 + ch);
       }
       unpack<BF16>(a, x[u]);
+      xq[u] = a;
       yq[u] = b;
-      st[u] = ch * VEC;
+      st[u] = static_cast<int>(ch * VEC);
     }
-    fold<U, VEC, BF16, PREV>(c, x, yq, nullptr, val, st);
+    fold<U, VEC, BF16, PREV>(c, x, xq, yq, nullptr, val, st);
   }
   // scalar tail elements (vocab not a multiple of the chunk width): last split
   if (s == S - 1 && tid < tail) {
@@ -442,42 +501,49 @@ __global__ __launch_bounds__(NT) void k_stats(const StatsArgs p) {
     x[0][0] = load_elem<BF16>(cur, v);
     const float y = PREV ? load_elem<BF16>(prv, v) : 0.f;
     const bool val[1] = {true};
-    const int64_t st[1] = {v};
-    fold<1, 1, BF16, PREV>(c, x, nullptr, &y, val, st);
+    const int st[1] = {static_cast<int>(v)};
+    fold<1, 1, BF16, PREV>(c, x, nullptr, nullptr, &y, val, st);
   }
 
-  // ---- combine lanes
-  const float M = dlm::block_max<NT>(c.m, sh.f);
+  // ---- this lane's argmax candidate, from the chunk kept in registers
   int cand = INT32_MAX;
-  if (c.m == M && c.best >= 0) {
+  if (c.best >= 0) {
     if (c.bestw == 1) {
-      cand = static_cast<int>(c.best);
+      cand = c.best;
     } else {
-      float x[VEC];
-      unpack<BF16>(cur4[c.best / VEC], x);
 #pragma unroll
       for (int k = VEC - 1; k >= 0; --k)
-        if (x[k] == M) cand = static_cast<int>(c.best + k);
+        if (elem_of<BF16>(c.bq, k) == c.m) cand = c.best + k;
     }
   }
-  const int yhat = dlm::block_min_i<NT>(cand, sh.i);
 
-  // Lane sums relative to the workgroup's integer reference hM = ceil(M*log2e):
-  // exact power-of-two scaling.  Sentinel lanes (no finite data) scale to 0.
-  const float hM = ceilf(M * kL2E);
-  const int di = static_cast<int>(fmaxf(c.h - hM, -1100.f));
-  double Z = ldexp(static_cast<double>(c.Z), di);
-  double A = ldexp(static_cast<double>(c.A) + static_cast<double>(c.h - hM) *
-                                                 static_cast<double>(c.Z), di);
-  double B = 0.0, Z2 = 0.0;
-  if constexpr (PREV) {
-    B = ldexp(static_cast<double>(c.B), di);
-    Z2 = ldexp(static_cast<double>(c.Z2), di);
+  // ---- wave merge (DPP): max, lowest index holding it, and the sums moved
+  // to the wave's integer reference hw = ceil(Mw*log2e)
+  Partial w;
+  w.m = dlm::wave_reduce(c.m, dlm::OpMaxF{});
+  w.cand = dlm::wave_reduce(c.m == w.m ? cand : INT32_MAX, dlm::OpMinI{});
+  w.h = ceilf(w.m * kL2E);
+  {
+    double Z = c.Z, A = c.A, B = c.B, Z2 = c.Z2;
+    rebase(Z, A, B, Z2, c.h, w.h);
+    w.Z = dlm::wave_reduce(Z, dlm::OpAdd{});
+    w.A = dlm::wave_reduce(A, dlm::OpAdd{});
+    if constexpr (PREV) {
+      w.B = dlm::wave_reduce(B, dlm::OpAdd{});
+      w.Z2 = dlm::wave_reduce(Z2, dlm::OpAdd{});
+    } else {
+      w.B = w.Z2 = 0.0;
+    }
   }
-  block_sum4_to0<NT>(Z, A, B, Z2, sh.d);
+  // ---- workgroup merge: one record per wave, one barrier, thread 0 merges
+  if (tid % DLM_WAVE == 0) sh.rec[tid / DLM_WAVE] = w;
+  __syncthreads();
 
   if (S == 1) {
-    if (tid == 0) sh.flag = finalize<PREV>(p, r, M, hM, yhat, Z, A, B, Z2);
+    if (tid == 0) {
+      const Partial t = merge<PREV>(NT / DLM_WAVE, [&](int k) { return sh.rec[k]; });
+      sh.flag = finalize<PREV>(p, r, t);
+    }
     __syncthreads();
     if (!sh.flag)
       careful_row<NT, BF16, PREV>(cur, prv, V, sh, r, p.conf, p.argmax, p.ent, p.kl, p.lse);
@@ -486,14 +552,15 @@ __global__ __launch_bounds__(NT) void k_stats(const StatsArgs p) {
 
   // ---- publish this split; the last workgroup of the row merges
   if (tid == 0) {
+    const Partial t = merge<PREV>(NT / DLM_WAVE, [&](int k) { return sh.rec[k]; });
     Partial* mine = p.parts + r * S + s;
-    st_agent(&mine->Z, Z);
-    st_agent(&mine->A, A);
-    st_agent(&mine->B, B);
-    st_agent(&mine->Z2, Z2);
-    st_agent(&mine->m, M);
-    st_agent(&mine->h, hM);
-    st_agent(&mine->cand, yhat);
+    st_agent(&mine->Z, t.Z);
+    st_agent(&mine->A, t.A);
+    st_agent(&mine->B, t.B);
+    st_agent(&mine->Z2, t.Z2);
+    st_agent(&mine->m, t.m);
+    st_agent(&mine->h, t.h);
+    st_agent(&mine->cand, t.cand);
     __threadfence();  // release the partial before counting in
     const int arrived = atomicAdd(p.counters + r, 1);
     sh.flag = arrived == S - 1 ? 1 : 0;
@@ -503,28 +570,19 @@ __global__ __launch_bounds__(NT) void k_stats(const StatsArgs p) {
   if (tid == 0) {
     __threadfence();  // acquire the other splits' partials
     Partial* row = p.parts + r * S;
-    float Mr = kLow;
-    for (int k = 0; k < S; ++k) Mr = fmaxf(Mr, ld_agent(&row[k].m));
-    const float hR = ceilf(Mr * kL2E);
-    double Zr = 0.0, Ar = 0.0, Br = 0.0, Z2r = 0.0;
-    int yr = INT32_MAX;
-    for (int k = 0; k < S; ++k) {  // split order: deterministic
-      const float mk = ld_agent(&row[k].m);
-      const float hk = ld_agent(&row[k].h);
-      const double zk = ld_agent(&row[k].Z);
-      const double d = static_cast<double>(hk - hR);
-      const int dk = static_cast<int>(fmax(d, -1100.0));
-      Zr += ldexp(zk, dk);
-      Ar += ldexp(ld_agent(&row[k].A) + d * zk, dk);
-      if constexpr (PREV) {
-        Br += ldexp(ld_agent(&row[k].B), dk);
-        Z2r += ldexp(ld_agent(&row[k].Z2), dk);
-      }
-      const int ck = ld_agent(&row[k].cand);
-      if (mk == Mr && ck < yr) yr = ck;
-    }
+    const Partial t = merge<PREV>(S, [&](int k) {  // split order: deterministic
+      Partial q;
+      q.Z = ld_agent(&row[k].Z);
+      q.A = ld_agent(&row[k].A);
+      q.B = ld_agent(&row[k].B);
+      q.Z2 = ld_agent(&row[k].Z2);
+      q.m = ld_agent(&row[k].m);
+      q.h = ld_agent(&row[k].h);
+      q.cand = ld_agent(&row[k].cand);
+      return q;
+    });
     st_agent(p.counters + r, 0);  // ready for the next call
-    sh.flag = finalize<PREV>(p, r, Mr, hR, yr, Zr, Ar, Br, Z2r);
+    sh.flag = finalize<PREV>(p, r, t);
   }
   __syncthreads();
   if (!sh.flag)
@@ -546,8 +604,6 @@ hipError_t launch_dt(int nt, const StatsArgs& a, int64_t n_rows, hipStream_t s) 
   switch (nt) {
     case 256:
       return launch_nt<256, BF16>(a, n_rows, s);
-    case 1024:
-      return launch_nt<1024, BF16>(a, n_rows, s);
     default:
       return launch_nt<512, BF16>(a, n_rows, s);
   }
@@ -583,7 +639,7 @@ void launch_shape(int64_t n_rows, int64_t n_chunks, bool can_split, int* nt, int
   if (forced_nt < 0) {
     const char* e = getenv("DLM_STATS_THREADS");
     const int v = e ? atoi(e) : 0;
-    forced_nt = (v == 256 || v == 512 || v == 1024) ? v : 0;
+    forced_nt = (v == 256 || v == 512) ? v : 0;
     const char* f = getenv("DLM_STATS_SPLITS");
     const int w = f ? atoi(f) : 0;
     forced_s = (w >= 1 && w <= kMaxSplits) ? w : 0;
