@@ -6,15 +6,18 @@
 // Three kernels:
 //  k_dapd_avg    grid-wide, HBM-bound.  Streams only the masked x masked
 //                sub-blocks of the n_lh attention maps (fp32 accumulation) and
-//                writes a and its transpose to the workspace.  A workgroup owns
-//                32 (row, 8-column chunk) items = one row x 256 columns, so each
-//                wave reads whole 512-byte row segments of two maps; its 1024
-//                lanes are 32 map groups x 32 items, so a single sequence already
-//                fills every CU.  Map groups are summed in LDS in a fixed order.
+//                writes a to the workspace.  A workgroup owns 32 (row, 8-column
+//                chunk) items = one row x 256 columns, so each wave reads whole
+//                512-byte row segments of two maps; its 1024 lanes are 32 map
+//                groups x 32 items, so a single sequence already fills every CU.
+//                A lane keeps 4 maps in flight (more only queues up behind the
+//                memory system).  Map groups are summed in LDS in a fixed order.
 //  k_dapd_sym    grid-wide: s = (a + aT)/2 for 16 rows per workgroup, one
-//                16-lane team per row with float4 loads; each lane turns its 16
-//                columns into a 16-bit slice of the row's adjacency bitset;
-//                fp64 proxy degree and the ordering key.
+//                16-lane team per row, lane l taking columns l, l+16, ...; the
+//                transposed half a[j][i] is read from a itself (the four teams
+//                of a wave share its cache lines), so no transposed copy is
+//                written; each step's 16 edge bits are one ballot slice; fp64
+//                proxy degree and the ordering key.
 //  k_dapd_select one workgroup (1024 threads) per sequence:
 //                1. the adjacency bitset and keys into LDS;
 //                2. rank sort of the 64-bit keys (key desc, position asc);
@@ -28,7 +31,13 @@
 
 namespace {
 
-constexpr int kGroups = 32;          // map groups per workgroup
+#ifndef DLM_DAPD_GROUPS
+#define DLM_DAPD_GROUPS 32
+#endif
+#ifndef DLM_DAPD_UNR_BF16
+#define DLM_DAPD_UNR_BF16 4
+#endif
+constexpr int kGroups = DLM_DAPD_GROUPS;  // map groups per workgroup
 constexpr int kItems = 32;           // (row, chunk) items per workgroup
 constexpr int kAvgNT = kGroups * kItems;
 constexpr int kTileRows = 1;
@@ -52,8 +61,7 @@ __global__ __launch_bounds__(kAvgNT) void k_dapd_avg(const void* __restrict__ at
                                                      const int32_t* __restrict__ masked_pos,
                                                      const int32_t* __restrict__ seq_offsets,
                                                      int m_max, int n_tc, int vec_ok,
-                                                     float* __restrict__ ws_a,
-                                                     float* __restrict__ ws_at) {
+                                                     float* __restrict__ ws_a) {
   __shared__ float red[kGroups][kItems][9];
   const int b = blockIdx.y;
   const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
@@ -85,9 +93,8 @@ __global__ __launch_bounds__(kAvgNT) void k_dapd_avg(const void* __restrict__ at
                        static_cast<int64_t>(b) * batch_stride * (BF16 ? 2 : 4);
     const int64_t map_stride = S * S;
     if (contig) {
-      // every map this lane owns is loaded before any is summed (one round
-      // trip for up to UNR * kGroups maps)
-      constexpr int UNR = BF16 ? 12 : 6;
+      // UNR maps per lane in flight, then summed in map order
+      constexpr int UNR = BF16 ? DLM_DAPD_UNR_BF16 : 2;
       for (int lh0 = g; lh0 < n_lh; lh0 += kGroups * UNR) {
         uint4 q[UNR][BF16 ? 1 : 2];
 #pragma unroll
@@ -151,7 +158,6 @@ __global__ __launch_bounds__(kAvgNT) void k_dapd_avg(const void* __restrict__ at
       const float a = s / static_cast<float>(n_lh);
       const int ld = ws_ld(m_max);
       ws_a[(static_cast<int64_t>(b) * m_max + ri) * ld + rj] = a;
-      ws_at[(static_cast<int64_t>(b) * m_max + rj) * ld + ri] = a;
     }
   }
 }
@@ -163,12 +169,12 @@ __device__ __forceinline__ uint32_t desc_bits(float f) {
 }
 
 // Workspace layout (every region 256-byte aligned), for n_seq x m_max:
-//   a, aT      f32 [n_seq][m_max][ws_ld]     averaged maps and transpose
+//   a          f32 [n_seq][m_max][ws_ld]     averaged maps
 //   adj        u64 [n_seq][m_max][words]     adjacency bitsets, words = ceil(m_max/64)
 //   keys       u64 [n_seq][m_max]            (order key, position)
 //   has_edge   u8  [n_seq][m_max]
 struct Layout {
-  size_t a, at, adj, keys, has_edge, total;
+  size_t a, adj, keys, has_edge, total;
   int ld, words;
 };
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -178,19 +184,21 @@ __host__ __device__ inline Layout layout(int n_seq, int m_max) {
   L.words = (m_max + 63) / 64;
   const size_t nm = static_cast<size_t>(n_seq) * m_max;
   L.a = 0;
-  L.at = align256(nm * L.ld * sizeof(float));
-  L.adj = L.at + align256(nm * L.ld * sizeof(float));
+  L.adj = align256(nm * L.ld * sizeof(float));
   L.keys = L.adj + align256(nm * L.words * sizeof(uint64_t));
   L.has_edge = L.keys + align256(nm * sizeof(uint64_t));
   L.total = L.has_edge + align256(nm);
   return L;
 }
 
-constexpr int kSymRows = 16;           // rows per k_dapd_sym workgroup (16 lanes each)
+#ifndef DLM_DAPD_SYM_ROWS
+#define DLM_DAPD_SYM_ROWS 4
+#endif
+constexpr int kSymRows = DLM_DAPD_SYM_ROWS;  // rows per k_dapd_sym workgroup (16 lanes each)
 constexpr int kSymNT = kSymRows * 16;
 
-// s = (a + aT)/2 for 16 rows per workgroup: adjacency bits (16-bit slices
-// per lane), fp64 proxy degree (fixed-pattern 16-lane reduction), ordering key.
+// s = (a + aT)/2 for 16 rows per workgroup: adjacency bits (ballot slices),
+// fp64 proxy degree (fixed-pattern 16-lane reduction), ordering key.
 __global__ __launch_bounds__(kSymNT) void k_dapd_sym(
     const int32_t* __restrict__ seq_offsets, int m_max, const float* __restrict__ conf,
     float tau, const char* __restrict__ ws, Layout L, float* __restrict__ degree,
@@ -206,52 +214,49 @@ __global__ __launch_bounds__(kSymNT) void k_dapd_sym(
       for (int j = tl; j < m_max; j += 16) sym[sbase + static_cast<int64_t>(i) * m_max + j] = NAN;
     return;
   }
-  const float* ar = reinterpret_cast<const float*>(ws + L.a) +
-                    (static_cast<int64_t>(b) * m_max + i) * L.ld;
-  const float* tr = reinterpret_cast<const float*>(ws + L.at) +
-                    (static_cast<int64_t>(b) * m_max + i) * L.ld;
+  const float* A = reinterpret_cast<const float*>(ws + L.a) + static_cast<int64_t>(b) * m_max * L.ld;
+  const float* ar = A + static_cast<int64_t>(i) * L.ld;
   uint16_t* adj16 = reinterpret_cast<uint16_t*>(
       const_cast<char*>(ws) + L.adj + (static_cast<int64_t>(b) * m_max + i) * L.words * 8);
   const int nw = (M + 63) / 64;
   float* so = sym ? sym + sbase + static_cast<int64_t>(i) * m_max : nullptr;
+  const int shift = 16 * (team % (DLM_WAVE / 16));  // this team's lanes in a ballot
   double dsum = 0.0;
   bool any = false;
   for (int c0 = 0; c0 < 64 * nw; c0 += 256) {
-    const int j0 = c0 + tl * 16;
+    // step e covers columns c0 + 16e .. c0 + 16e + 15, column c0 + 16e + tl
+    // on this lane; lane e keeps step e's 16 edge bits.  a[j][i] (the
+    // transposed half) is read straight from a: the four teams of a wave read
+    // neighbouring columns of the same rows, so a wave load touches 16 lines.
     float va[16], vt[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float4 xa = make_float4(0.f, 0.f, 0.f, 0.f), xt = xa;
-      if (j0 + 4 * q < M) {  // stays inside the 16-float padded row
-        xa = reinterpret_cast<const float4*>(ar + j0)[q];
-        xt = reinterpret_cast<const float4*>(tr + j0)[q];
+    for (int e = 0; e < 16; ++e) {
+      const int j = c0 + 16 * e + tl;
+      va[e] = vt[e] = 0.f;
+      if (j < M) {
+        va[e] = ar[j];
+        vt[e] = A[static_cast<int64_t>(j) * L.ld + i];
       }
-      va[4 * q + 0] = xa.x;
-      va[4 * q + 1] = xa.y;
-      va[4 * q + 2] = xa.z;
-      va[4 * q + 3] = xa.w;
-      vt[4 * q + 0] = xt.x;
-      vt[4 * q + 1] = xt.y;
-      vt[4 * q + 2] = xt.z;
-      vt[4 * q + 3] = xt.w;
     }
-    if (j0 >= 64 * nw) continue;
-    uint32_t bits = 0u;
+    uint32_t mine = 0u;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int j = j0 + e;
+      const int j = c0 + 16 * e + tl;
       float sv = NAN;
+      bool edge = false;
       if (j < M) {
         sv = 0.5f * (va[e] + vt[e]);
         if (j != i) {
           dsum += static_cast<double>(sv);
-          bits |= static_cast<uint32_t>(sv > tau) << e;
+          edge = sv > tau;
         }
       }
       if (so && j < m_max) so[j] = sv;
+      const uint32_t slice = static_cast<uint32_t>(__ballot(edge) >> shift) & 0xffffu;
+      if (e == tl) mine = slice;
     }
-    adj16[j0 / 16] = static_cast<uint16_t>(bits);  // zero past M, up to the last word
-    any = any || bits != 0u;
+    if (c0 + 16 * tl < 64 * nw) adj16[c0 / 16 + tl] = static_cast<uint16_t>(mine);  // zero past M
+    any = any || mine != 0u;
   }
   if (so)
     for (int j = 64 * nw + tl; j < m_max; j += 16) so[j] = NAN;
@@ -419,17 +424,16 @@ extern "C" int dlm_dapd_select(const void* attn, int dtype, int32_t n_lh, int64_
   const Layout L = layout(n_seq, m_max);
   char* ws = static_cast<char*>(workspace);
   float* ws_a = reinterpret_cast<float*>(ws + L.a);
-  float* ws_at = reinterpret_cast<float*>(ws + L.at);
   const int n_ti = (m_max + kTileRows - 1) / kTileRows;
   const int n_tc = (m_max + 8 * kTileChunks - 1) / (8 * kTileChunks);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(n_ti * n_tc, n_seq);
   if (dtype == DLM_BF16)
     hipLaunchKernelGGL(k_dapd_avg<true>, grid, dim3(kAvgNT), 0, s, attn, n_lh, S, batch_stride,
-                       masked_pos, seq_offsets, m_max, n_tc, vec_ok, ws_a, ws_at);
+                       masked_pos, seq_offsets, m_max, n_tc, vec_ok, ws_a);
   else
     hipLaunchKernelGGL(k_dapd_avg<false>, grid, dim3(kAvgNT), 0, s, attn, n_lh, S, batch_stride,
-                       masked_pos, seq_offsets, m_max, n_tc, vec_ok, ws_a, ws_at);
+                       masked_pos, seq_offsets, m_max, n_tc, vec_ok, ws_a);
   DLM_CHECK_LAUNCH();
   hipLaunchKernelGGL(k_dapd_sym, dim3((m_max + kSymRows - 1) / kSymRows, n_seq), dim3(kSymNT), 0,
                      s, seq_offsets, m_max, conf, tau, ws, L, degree, sym, key);

@@ -190,8 +190,9 @@ int dlm_cap_select(const void* logits, int dtype, int64_t vocab, int64_t ld,
 
 /*
  * dlm_dapd_workspace_bytes — device workspace that dlm_dapd_select needs for
- * n_seq sequences of at most m_max masked positions (two fp32 m_max x m_max
- * matrices per sequence).  Returns 0 for invalid sizes.
+ * n_seq sequences of at most m_max masked positions (per sequence: the fp32
+ * m_max x m_max attention average, the adjacency bitsets and the ordering
+ * keys).  Returns 0 for invalid sizes.
  */
 size_t dlm_dapd_workspace_bytes(int32_t n_seq, int32_t m_max);
 
