@@ -73,10 +73,16 @@ def _declare(L):
     L.dlmo_dapd_greedy.argtypes = [_P, _I32, _I64, _D, _P, _P]
     L.dlmo_dapd_select.argtypes = [_P, _INT, _I32, _I64, _I64, _P, _P, _I32, _P, _D, _P, _P, _P,
                                    _P, _I32, _P, _INT]
+    L.dlmo_topk_select.argtypes = [_P, _P, _P, _I32, _I32, _P, _P]
+    L.dlmo_factor_select.argtypes = [_P, _P, _P, _I32, _D, _P, _P, _P]
+    L.dlmo_fixed_block_eligible.argtypes = [_P, _P, _I32, _P, _I32, _P]
+    L.dlmo_dapd_step.argtypes = [_P, _INT, _I32, _I64, _I64, _P, _P, _I32, _P, _D, _P, _D, _D,
+                                 _INT, _P, _P, _P, _INT]
     for name in ("dlmo_step_stats", "dlmo_fastdllm_select", "dlmo_depcap_scores",
                  "dlmo_depcap_decide", "dlmo_cap_pool", "dlmo_cap_dmatrix", "dlmo_cap_greedy",
                  "dlmo_cap_select", "dlmo_dapd_average", "dlmo_dapd_graph", "dlmo_dapd_greedy",
-                 "dlmo_dapd_select"):
+                 "dlmo_dapd_select", "dlmo_topk_select", "dlmo_factor_select",
+                 "dlmo_fixed_block_eligible", "dlmo_dapd_step"):
         getattr(L, name).restype = _INT
 
 
@@ -346,3 +352,61 @@ def dapd_select(attn: torch.Tensor, masked_pos, seq_offsets, conf, tau, m_max=No
     _check(rc, "dapd_select")
     return {"commit": commit, "n_commit": n_commit, "degree": degree, "key": key,
             "sym": sym.reshape(max(n_seq, 0), m_max, m_max)}
+
+
+def topk_select(conf, seq_offsets, k, eligible=None):
+    """dlmo_topk_select: the k most confident eligible rows per sequence."""
+    c, so, el = _f64(conf), _i32(seq_offsets), _u8(eligible)
+    n_seq = so.shape[0] - 1
+    commit = np.zeros(c.shape[0], np.uint8)
+    n_commit = np.zeros(max(n_seq, 0), np.int32)
+    rc = lib().dlmo_topk_select(_ptr(c), _ptr(el), _ptr(so), n_seq, int(k), _ptr(commit),
+                                _ptr(n_commit))
+    _check(rc, "topk_select")
+    return commit, n_commit
+
+
+def factor_select(conf, seq_offsets, f=1.0, eligible=None):
+    """dlmo_factor_select: returns commit, n_commit and the Theorem-1 certificate."""
+    c, so, el = _f64(conf), _i32(seq_offsets), _u8(eligible)
+    n_seq = so.shape[0] - 1
+    commit = np.zeros(c.shape[0], np.uint8)
+    n_commit = np.zeros(max(n_seq, 0), np.int32)
+    cert = np.zeros(max(n_seq, 0), np.uint8)
+    rc = lib().dlmo_factor_select(_ptr(c), _ptr(el), _ptr(so), n_seq, float(f), _ptr(commit),
+                                  _ptr(n_commit), _ptr(cert))
+    _check(rc, "factor_select")
+    return commit, n_commit, cert
+
+
+def fixed_block_eligible(masked_pos, seq_offsets, block_len, gen_start=None):
+    """dlmo_fixed_block_eligible: masked rows of each sequence's active fixed block."""
+    mp, so = _i32(masked_pos), _i32(seq_offsets)
+    gs = None if gen_start is None else _i32(gen_start)
+    n_seq = so.shape[0] - 1
+    el = np.zeros(mp.shape[0], np.uint8)
+    rc = lib().dlmo_fixed_block_eligible(_ptr(mp), _ptr(so), n_seq, _ptr(gs), int(block_len),
+                                         _ptr(el))
+    _check(rc, "fixed_block_eligible")
+    return el
+
+
+def dapd_step(attn: torch.Tensor, masked_pos, seq_offsets, conf, tau, gen_len=None,
+              late_frac=0.5, late_tau=0.9, pre_unmask=True, n_threads=None):
+    """dlmo_dapd_step: returns commit, n_commit and the per-sequence stage (1 = late)."""
+    B, n_lh, S, S2 = attn.shape
+    at, ap = _host(attn)
+    mp, so, c = _i32(masked_pos), _i32(seq_offsets), _f64(conf)
+    gl = None if gen_len is None else _i32(gen_len)
+    n_seq = so.shape[0] - 1
+    if n_seq > B:
+        raise ValueError("more sequences than attention batches")
+    commit = np.zeros(c.shape[0], np.uint8)
+    n_commit = np.zeros(max(n_seq, 0), np.int32)
+    stage = np.zeros(max(n_seq, 0), np.uint8)
+    rc = lib().dlmo_dapd_step(ap, _dtype_code(attn), n_lh, S, n_lh * S * S, _ptr(mp), _ptr(so),
+                              n_seq, _ptr(c), float(tau), _ptr(gl), float(late_frac),
+                              float(late_tau), int(bool(pre_unmask)), _ptr(commit),
+                              _ptr(n_commit), _ptr(stage), n_threads or default_threads())
+    _check(rc, "dapd_step")
+    return {"commit": commit, "n_commit": n_commit, "stage": stage}

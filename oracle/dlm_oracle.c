@@ -644,3 +644,163 @@ int dlmo_dapd_select(const void* attn, int dtype, int32_t n_lh, int64_t S, int64
   parallel_for(n_seq, n_threads, dapd_range, &c);
   return 0;
 }
+
+/* ------------------------------------------------------ schedules (NEXT) */
+
+/* A sequence's eligible rows with a non-NaN confidence, ordered by
+ * (confidence desc, row asc); plain insertion sort.  Returns the count. */
+static int32_t conf_order(const double* conf, const uint8_t* eligible, int32_t lo, int32_t hi,
+                          int32_t* ord) {
+  int32_t n = 0;
+  for (int32_t r = lo; r < hi; ++r)
+    if ((eligible ? eligible[r] != 0 : 1) && !isnan(conf[r])) ord[n++] = r;
+  for (int32_t a = 1; a < n; ++a) {
+    int32_t x = ord[a], p = a - 1;
+    while (p >= 0 && conf[ord[p]] < conf[x]) {
+      ord[p + 1] = ord[p];
+      --p;
+    }
+    ord[p + 1] = x;
+  }
+  return n;
+}
+
+/*
+ * [Fast-dLLM review, Prior limitations; Comparison]: LLaDA's default
+ * schedule commits a fixed number K of tokens per step, the K most confident,
+ * whatever their confidence.
+ * Readings: ties go to the lower row; rows with NaN confidence are never
+ * committed; with fewer than K eligible rows, all of them are committed.
+ */
+int dlmo_topk_select(const double* conf, const uint8_t* eligible, const int32_t* seq_offsets,
+                     int32_t n_seq, int32_t k, uint8_t* commit, int32_t* n_commit) {
+  if (!conf || !seq_offsets || !commit || !n_commit || n_seq < 0 || k < 1) return 1;
+  for (int32_t b = 0; b < n_seq; ++b) {
+    int32_t lo = seq_offsets[b], hi = seq_offsets[b + 1];
+    int32_t* ord = (int32_t*)malloc(sizeof(int32_t) * (size_t)(hi > lo ? hi - lo : 1));
+    int32_t n = conf_order(conf, eligible, lo, hi, ord);
+    for (int32_t r = lo; r < hi; ++r) commit[r] = 0;
+    int32_t take = n < k ? n : k;
+    for (int32_t t = 0; t < take; ++t) commit[ord[t]] = 1;
+    n_commit[b] = take;
+    free(ord);
+  }
+  return 0;
+}
+
+/*
+ * [Fast-dLLM review, Method (factor decoding); Key idea (Theorem 1)]: with
+ * c(1) >= c(2) >= ... the eligible confidences in descending order, commit
+ * the n most confident rows for the largest n with (n+1)(1 - c(n)) < f.
+ * Readings:
+ *   - the left side never decreases with n, so the admissible n form a
+ *     prefix 1..n*; the test is evaluated in double precision on the given
+ *     confidences (exact for fp32 inputs: 1 - c and the product by an integer
+ *     below 2^29 are representable);
+ *   - at least one row is committed when any is eligible (the progress
+ *     guarantee of the threshold rule, [Fast-dLLM review, Method]);
+ *   - ties go to the lower row; NaN confidences are never committed.
+ * certificate[b] (optional) = 1 iff n >= 1 and (n+1)(1 - min committed c) <= 1,
+ * Theorem 1's sufficient condition (its "(n+1) eps <= 1" form) for the
+ * parallel commit to coincide with greedy one-at-a-time decoding.
+ */
+int dlmo_factor_select(const double* conf, const uint8_t* eligible, const int32_t* seq_offsets,
+                       int32_t n_seq, double f, uint8_t* commit, int32_t* n_commit,
+                       uint8_t* certificate) {
+  if (!conf || !seq_offsets || !commit || !n_commit || n_seq < 0 || isnan(f)) return 1;
+  for (int32_t b = 0; b < n_seq; ++b) {
+    int32_t lo = seq_offsets[b], hi = seq_offsets[b + 1];
+    int32_t* ord = (int32_t*)malloc(sizeof(int32_t) * (size_t)(hi > lo ? hi - lo : 1));
+    int32_t n = conf_order(conf, eligible, lo, hi, ord);
+    int32_t best = 0;
+    for (int32_t m = 1; m <= n; ++m)
+      if ((double)(m + 1) * (1.0 - conf[ord[m - 1]]) < f) best = m;
+    if (best == 0 && n > 0) best = 1;
+    for (int32_t r = lo; r < hi; ++r) commit[r] = 0;
+    for (int32_t t = 0; t < best; ++t) commit[ord[t]] = 1;
+    n_commit[b] = best;
+    if (certificate)
+      certificate[b] =
+          (uint8_t)(best >= 1 && (double)(best + 1) * (1.0 - conf[ord[best - 1]]) <= 1.0);
+    free(ord);
+  }
+  return 0;
+}
+
+/*
+ * [DepCap summary, Experiments]: confidence decoding with fixed 16/32/64-token
+ * blocks, as a baseline schedule.
+ * Readings: blocks tile the generation in lengths of block_len from its first
+ * position gen_start[b] (NULL: 0); the active block is the earliest block that
+ * still holds a masked position; the eligible rows are the masked rows inside
+ * it (the threshold rule then runs on them).  A masked position before
+ * gen_start belongs to no block and is never eligible.
+ */
+int dlmo_fixed_block_eligible(const int32_t* masked_pos, const int32_t* seq_offsets,
+                              int32_t n_seq, const int32_t* gen_start, int32_t block_len,
+                              uint8_t* eligible) {
+  if (!masked_pos || !seq_offsets || !eligible || n_seq < 0 || block_len < 1) return 1;
+  for (int32_t b = 0; b < n_seq; ++b) {
+    int32_t lo = seq_offsets[b], hi = seq_offsets[b + 1];
+    int64_t g0 = gen_start ? gen_start[b] : 0, first = -1;
+    for (int32_t r = lo; r < hi; ++r) {
+      int64_t rel = (int64_t)masked_pos[r] - g0;
+      if (rel < 0) continue;
+      int64_t blk = rel / block_len;
+      if (first < 0 || blk < first) first = blk;
+    }
+    for (int32_t r = lo; r < hi; ++r) {
+      int64_t rel = (int64_t)masked_pos[r] - g0;
+      eligible[r] = (uint8_t)(rel >= 0 && first >= 0 && rel / block_len == first);
+    }
+  }
+  return 0;
+}
+
+/*
+ * [DAPD note, overall framework; key design 3 (late-stage confidence
+ * sparsification)]: the full DAPD step.  For sequence b with M_b masked rows
+ * out of a generation of gen_len[b] tokens:
+ *   - late stage iff M_b < late_frac * gen_len[b] (the remaining masks fell
+ *     below 50%): no graph, commit every row with conf > late_tau (0.9);
+ *   - otherwise the dependency-graph independent set (dlmo_dapd_select);
+ *   - with pre_unmask, every row whose confidence is exactly 1.0 is also
+ *     committed, in either stage (such a position takes the same token under
+ *     every compatible joint distribution).
+ * Readings: strict < for the switch and strict > for the threshold; a late
+ * stage that commits nothing commits the most confident row (the threshold
+ * rule's progress guarantee; the page gives none); pre-unmasked rows are added
+ * to the set the stage chose, the graph being built over all masked rows as in
+ * the plain step.  gen_len == NULL disables the late stage.  stage[b]
+ * (optional) = 1 for a late-stage sequence.
+ */
+int dlmo_dapd_step(const void* attn, int dtype, int32_t n_lh, int64_t S, int64_t batch_stride,
+                   const int32_t* masked_pos, const int32_t* seq_offsets, int32_t n_seq,
+                   const double* conf, double tau, const int32_t* gen_len, double late_frac,
+                   double late_tau, int pre_unmask, uint8_t* commit, int32_t* n_commit,
+                   uint8_t* stage, int n_threads) {
+  if (!attn || !masked_pos || !seq_offsets || !conf || !commit || !n_commit || n_seq < 0 ||
+      isnan(tau) || isnan(late_frac) || isnan(late_tau))
+    return 1;
+  int rc = dlmo_dapd_select(attn, dtype, n_lh, S, batch_stride, masked_pos, seq_offsets, n_seq,
+                            conf, tau, commit, n_commit, NULL, NULL, 0, NULL, n_threads);
+  if (rc) return rc;
+  for (int32_t b = 0; b < n_seq; ++b) {
+    int32_t lo = seq_offsets[b], hi = seq_offsets[b + 1];
+    int late = gen_len && (double)(hi - lo) < late_frac * (double)gen_len[b];
+    if (stage) stage[b] = (uint8_t)late;
+    if (late) {
+      int32_t sub[2] = {0, hi - lo};
+      dlmo_fastdllm_select(conf + lo, NULL, sub, 1, late_tau, commit + lo, n_commit + b);
+    }
+    if (pre_unmask) {
+      int32_t cnt = 0;
+      for (int32_t r = lo; r < hi; ++r) {
+        if (conf[r] == 1.0) commit[r] = 1;
+        cnt += commit[r];
+      }
+      n_commit[b] = cnt;
+    }
+  }
+  return 0;
+}

@@ -93,7 +93,26 @@ int dlmo_dapd_select(const void* attn, int dtype, int32_t n_lh, int64_t S, int64
                      const double* conf, double tau, uint8_t* commit, int32_t* n_commit,
                      double* degree, double* sym, int32_t m_max, double* key, int n_threads);
 
+/* Fixed top-K per step (LLaDA's default schedule). */
+int dlmo_topk_select(const double* conf, const uint8_t* eligible, const int32_t* seq_offsets,
+                     int32_t n_seq, int32_t k, uint8_t* commit, int32_t* n_commit);
+/* Factor decoding: largest n with (n+1)(1 - c(n)) < f; certificate optional. */
+int dlmo_factor_select(const double* conf, const uint8_t* eligible, const int32_t* seq_offsets,
+                       int32_t n_seq, double f, uint8_t* commit, int32_t* n_commit,
+                       uint8_t* certificate);
+/* Eligible rows of fixed-length block decoding: the earliest block with a mask. */
+int dlmo_fixed_block_eligible(const int32_t* masked_pos, const int32_t* seq_offsets,
+                              int32_t n_seq, const int32_t* gen_start, int32_t block_len,
+                              uint8_t* eligible);
+/* Full DAPD step: late-stage threshold switch and conf == 1 pre-unmask. */
+int dlmo_dapd_step(const void* attn, int dtype, int32_t n_lh, int64_t S, int64_t batch_stride,
+                   const int32_t* masked_pos, const int32_t* seq_offsets, int32_t n_seq,
+                   const double* conf, double tau, const int32_t* gen_len, double late_frac,
+                   double late_tau, int pre_unmask, uint8_t* commit, int32_t* n_commit,
+                   uint8_t* stage, int n_threads);
+
 #ifdef __cplusplus
 }
 #endif
 #endif
+
