@@ -16,7 +16,7 @@ DEFAULTS = dict(
     fastdllm_tau=0.9, fastdllm_block=32,
     depcap_lambda=1.2, depcap_l_min=8, depcap_l_max=128, depcap_radius=1, depcap_eps=1e-12,
     cap_tau_low=0.8, cap_tau_high=0.95, cap_gamma=-16.0,
-    dapd_layer_frac=0.3, dapd_late_frac=0.5, dapd_late_tau=0.9,
+    dapd_layer_frac=0.3, dapd_late_frac=0.5, dapd_late_tau=0.9, factor_f=1.0,
 )
 
 
@@ -220,3 +220,97 @@ def dapd_select(attn, masked_pos, seq_offsets, conf, tau, m_max=None, workspace=
                                     workspace.data_ptr(), workspace.numel(), _stream(attn))
     _lib.check(st, "dlm_dapd_select")
     return {"commit": commit, "n_commit": n_commit, "degree": degree, "key": key, "sym": sym}
+
+
+def dapd_step(attn, masked_pos, seq_offsets, conf, tau, gen_len=None,
+              late_frac=DEFAULTS["dapd_late_frac"], late_tau=DEFAULTS["dapd_late_tau"],
+              pre_unmask=True, m_max=None, workspace=None, want_degree=False, want_key=False,
+              want_sym=False):
+    """dlm_dapd_step: dlm_dapd_select plus the late-stage switch (gen_len int32
+    per sequence, or None) and the conf = 1 pre-unmask.  Returns dict(commit,
+    n_commit, stage, degree, key, sym)."""
+    _dev(attn, "attn")
+    if attn.dim() != 4 or not attn.is_contiguous() or attn.shape[2] != attn.shape[3]:
+        raise DLMError("attn must be a contiguous [B, n_lh, S, S] tensor")
+    dev = attn.device
+    B, n_lh, S, _ = attn.shape
+    _vec(masked_pos, "masked_pos", torch.int32, dev)
+    _vec(seq_offsets, "seq_offsets", torch.int32, dev)
+    _vec(conf, "conf", torch.float32, dev)
+    _opt(gen_len, "gen_len", torch.int32, dev)
+    n_seq = seq_offsets.numel() - 1
+    if n_seq > B:
+        raise DLMError("more sequences than attention batches")
+    if m_max is None:
+        raise DLMError("m_max (an upper bound on masked positions per sequence) is required")
+    need = dapd_workspace_bytes(n_seq, m_max)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    _vec(workspace, "workspace", torch.uint8, dev)
+    n = conf.numel()
+    f = dict(device=dev, dtype=torch.float32)
+    commit = torch.empty(n, device=dev, dtype=torch.uint8)
+    n_commit = torch.empty(max(n_seq, 0), device=dev, dtype=torch.int32)
+    stage = torch.empty(max(n_seq, 0), device=dev, dtype=torch.uint8)
+    degree = torch.empty(n, **f) if want_degree else None
+    key = torch.empty(n, **f) if want_key else None
+    sym = torch.empty(max(n_seq, 0), m_max, m_max, **f) if want_sym else None
+    st = _lib.lib().dlm_dapd_step(attn.data_ptr(), _dtype_code(attn), n_lh, S, n_lh * S * S,
+                                  masked_pos.data_ptr(), seq_offsets.data_ptr(), n_seq,
+                                  int(m_max), conf.data_ptr(), float(tau), _ptr(gen_len),
+                                  float(late_frac), float(late_tau), int(bool(pre_unmask)),
+                                  commit.data_ptr(), n_commit.data_ptr(), stage.data_ptr(),
+                                  _ptr(degree), _ptr(sym), _ptr(key), workspace.data_ptr(),
+                                  workspace.numel(), _stream(attn))
+    _lib.check(st, "dlm_dapd_step")
+    return {"commit": commit, "n_commit": n_commit, "stage": stage, "degree": degree,
+            "key": key, "sym": sym}
+
+
+def _select_common(conf, seq_offsets, eligible):
+    _dev(conf, "conf", torch.float32)
+    dev = conf.device
+    _vec(conf, "conf", torch.float32, dev)
+    _vec(seq_offsets, "seq_offsets", torch.int32, dev)
+    _opt(eligible, "eligible", torch.uint8, dev)
+    n_seq = seq_offsets.numel() - 1
+    commit = torch.empty(conf.numel(), device=dev, dtype=torch.uint8)
+    n_commit = torch.empty(max(n_seq, 0), device=dev, dtype=torch.int32)
+    return dev, n_seq, commit, n_commit
+
+
+def factor_select(conf, seq_offsets, f=DEFAULTS["factor_f"], eligible=None):
+    """dlm_factor_select: returns commit, n_commit and the Theorem-1 certificate."""
+    dev, n_seq, commit, n_commit = _select_common(conf, seq_offsets, eligible)
+    cert = torch.empty(max(n_seq, 0), device=dev, dtype=torch.uint8)
+    st = _lib.lib().dlm_factor_select(conf.data_ptr(), _ptr(eligible), seq_offsets.data_ptr(),
+                                      n_seq, float(f), commit.data_ptr(), n_commit.data_ptr(),
+                                      cert.data_ptr(), _stream(conf))
+    _lib.check(st, "dlm_factor_select")
+    return commit, n_commit, cert
+
+
+def topk_select(conf, seq_offsets, k, eligible=None):
+    """dlm_topk_select: the k most confident eligible rows per sequence."""
+    dev, n_seq, commit, n_commit = _select_common(conf, seq_offsets, eligible)
+    st = _lib.lib().dlm_topk_select(conf.data_ptr(), _ptr(eligible), seq_offsets.data_ptr(),
+                                    n_seq, int(k), commit.data_ptr(), n_commit.data_ptr(),
+                                    _stream(conf))
+    _lib.check(st, "dlm_topk_select")
+    return commit, n_commit
+
+
+def fixed_block_eligible(masked_pos, seq_offsets, block_len, gen_start=None):
+    """dlm_fixed_block_eligible: masked rows of each sequence's active fixed block."""
+    _dev(masked_pos, "masked_pos", torch.int32)
+    dev = masked_pos.device
+    _vec(masked_pos, "masked_pos", torch.int32, dev)
+    _vec(seq_offsets, "seq_offsets", torch.int32, dev)
+    _opt(gen_start, "gen_start", torch.int32, dev)
+    n_seq = seq_offsets.numel() - 1
+    el = torch.empty(masked_pos.numel(), device=dev, dtype=torch.uint8)
+    st = _lib.lib().dlm_fixed_block_eligible(masked_pos.data_ptr(), seq_offsets.data_ptr(), n_seq,
+                                             _ptr(gen_start), int(block_len), el.data_ptr(),
+                                             _stream(masked_pos))
+    _lib.check(st, "dlm_fixed_block_eligible")
+    return el

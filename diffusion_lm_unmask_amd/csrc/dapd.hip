@@ -25,6 +25,13 @@
 //                   blocked by an earlier block's chosen node (bitset AND) or by
 //                   an earlier node of its own block (ballots), which gives the
 //                   same set as the one-node-at-a-time scan.
+//
+// dlm_dapd_step adds the full step policy (DAPD note, key design 3): a
+// sequence whose masked rows fell below late_frac of its generation length
+// skips the graph (no attention read, no adjacency) and commits conf >
+// late_tau with a top-1 fallback; rows with conf exactly 1.0 may be
+// committed in either stage (pre-unmask).  Every kernel evaluates the same
+// stage test, in fp64: M < late_frac * gen_len.
 #include <math.h>
 
 #include "dlm_device.h"
@@ -49,6 +56,19 @@ constexpr int kWords = kMaxM / 64;
 // Row stride (floats) of the workspace matrices: 16-float aligned rows.
 __host__ __device__ inline int ws_ld(int m_max) { return (m_max + 15) & ~15; }
 
+// The full-step policy; gen_len == nullptr and pre_unmask == 0 give the plain
+// DAPD selection.
+struct Policy {
+  const int32_t* gen_len;  // [n_seq] generation length per sequence, or null
+  float late_frac, late_tau;
+  int pre_unmask;
+  uint8_t* stage;          // [n_seq] 1 = late stage, or null
+};
+__device__ __forceinline__ bool late_stage(const Policy& P, int b, int M) {
+  return P.gen_len != nullptr &&
+         static_cast<double>(M) < static_cast<double>(P.late_frac) * static_cast<double>(P.gen_len[b]);
+}
+
 template <bool BF16>
 __device__ __forceinline__ float ld1(const void* base, int64_t idx) {
   if constexpr (BF16) return dlm::bf16_at(static_cast<const uint16_t*>(base), idx);
@@ -61,11 +81,11 @@ __global__ __launch_bounds__(kAvgNT) void k_dapd_avg(const void* __restrict__ at
                                                      const int32_t* __restrict__ masked_pos,
                                                      const int32_t* __restrict__ seq_offsets,
                                                      int m_max, int n_tc, int vec_ok,
-                                                     float* __restrict__ ws_a) {
+                                                     float* __restrict__ ws_a, Policy P) {
   __shared__ float red[kGroups][kItems][9];
   const int b = blockIdx.y;
   const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
-  if (M > m_max || M <= 0) return;
+  if (M > m_max || M <= 0 || late_stage(P, b, M)) return;  // late stage: no graph
   const int ti = blockIdx.x / n_tc, tc = blockIdx.x % n_tc;
   const int i0 = ti * kTileRows, c0 = tc * kTileChunks;
   if (i0 >= M || c0 * 8 >= M) return;  // whole workgroup idle (uniform)
@@ -202,14 +222,18 @@ constexpr int kSymNT = kSymRows * 16;
 __global__ __launch_bounds__(kSymNT) void k_dapd_sym(
     const int32_t* __restrict__ seq_offsets, int m_max, const float* __restrict__ conf,
     float tau, const char* __restrict__ ws, Layout L, float* __restrict__ degree,
-    float* __restrict__ sym, float* __restrict__ key_out) {
+    float* __restrict__ sym, float* __restrict__ key_out, Policy P) {
   const int b = blockIdx.y;
   const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
   const int team = threadIdx.x / 16, tl = threadIdx.x % 16;
   const int i = blockIdx.x * kSymRows + team;
   const int64_t sbase = static_cast<int64_t>(b) * m_max * m_max;
   if (M > m_max || M < 0 || i >= m_max) return;  // over-long sequences: k_dapd_select reports
-  if (i >= M) {  // pad rows of the optional sym output
+  if (i >= M || late_stage(P, b, M)) {  // pad rows, or no graph: NaN in the optional outputs
+    if (i < M && tl == 0) {
+      if (degree) degree[lo + i] = NAN;
+      if (key_out) key_out[lo + i] = NAN;
+    }
     if (sym)
       for (int j = tl; j < m_max; j += 16) sym[sbase + static_cast<int64_t>(i) * m_max + j] = NAN;
     return;
@@ -282,14 +306,15 @@ __global__ __launch_bounds__(kSymNT) void k_dapd_sym(
 // Per sequence: load the graph into LDS, order the nodes, run the greedy.
 __global__ __launch_bounds__(kSelNT) void k_dapd_select(
     const int32_t* __restrict__ seq_offsets, int m_max, const char* __restrict__ ws, Layout L,
-    uint8_t* __restrict__ commit, int32_t* __restrict__ n_commit, float* __restrict__ degree,
-    float* __restrict__ sym, float* __restrict__ key_out) {
+    const float* __restrict__ conf, uint8_t* __restrict__ commit, int32_t* __restrict__ n_commit,
+    float* __restrict__ degree, float* __restrict__ sym, float* __restrict__ key_out, Policy P) {
   __shared__ uint64_t adj[kMaxM][kWords];  // 128 KiB; row i = neighbours of node i
   __shared__ uint64_t keys[kMaxM];
   __shared__ int16_t order[kMaxM];
   __shared__ uint64_t chosen[kWords];
   __shared__ uint8_t has_edge[kMaxM];
   __shared__ int shi[kSelNT / DLM_WAVE];
+  __shared__ float shf[kSelNT / DLM_WAVE];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int wv = tid / DLM_WAVE, ln = tid % DLM_WAVE;
   const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
@@ -304,7 +329,36 @@ __global__ __launch_bounds__(kSelNT) void k_dapd_select(
     if (sym)
       for (int64_t e = tid; e < static_cast<int64_t>(m_max) * m_max; e += kSelNT)
         sym[sbase + e] = NAN;
-    if (tid == 0) n_commit[b] = -1;
+    if (tid == 0) {
+      n_commit[b] = -1;
+      if (P.stage) P.stage[b] = 0;
+    }
+    return;
+  }
+  const bool late = late_stage(P, b, M);  // uniform over the workgroup
+  if (tid == 0 && P.stage) P.stage[b] = static_cast<uint8_t>(late);
+  if (late) {  // no graph: conf > late_tau, else the most confident row
+    int above = 0, bi = INT32_MAX;
+    float bv = -INFINITY;
+    for (int r = tid; r < M; r += kSelNT) {
+      const float cf = conf[lo + r];
+      above += cf > P.late_tau;
+      if (cf == cf && (bi == INT32_MAX || cf > bv)) {
+        bv = cf;
+        bi = r;
+      }
+    }
+    above = dlm::block_sum<kSelNT>(above, shi);
+    const int fb = above == 0 ? dlm::block_argmax<kSelNT>(bv, bi, shf, shi) : INT32_MAX;
+    int cnt = 0;
+    for (int r = tid; r < M; r += kSelNT) {
+      const float cf = conf[lo + r];
+      const int c = (cf > P.late_tau) || r == fb || (P.pre_unmask && cf == 1.0f);
+      commit[lo + r] = static_cast<uint8_t>(c);
+      cnt += c;
+    }
+    cnt = dlm::block_sum<kSelNT>(cnt, shi);
+    if (tid == 0) n_commit[b] = cnt;
     return;
   }
   const int nw = (M + 63) / 64;  // adjacency words in use
@@ -387,7 +441,8 @@ __global__ __launch_bounds__(kSelNT) void k_dapd_select(
   __syncthreads();
   int cnt = 0;
   for (int r = tid; r < M; r += kSelNT) {
-    const int c = static_cast<int>((chosen[r >> 6] >> (r & 63)) & 1ull);
+    const int c = static_cast<int>((chosen[r >> 6] >> (r & 63)) & 1ull) |
+                  (P.pre_unmask && conf[lo + r] == 1.0f);  // pre-unmask
     commit[lo + r] = static_cast<uint8_t>(c);
     cnt += c;
   }
@@ -402,15 +457,17 @@ extern "C" size_t dlm_dapd_workspace_bytes(int32_t n_seq, int32_t m_max) {
   return layout(n_seq, m_max).total;
 }
 
-extern "C" int dlm_dapd_select(const void* attn, int dtype, int32_t n_lh, int64_t S,
-                               int64_t batch_stride, const int32_t* masked_pos,
-                               const int32_t* seq_offsets, int32_t n_seq, int32_t m_max,
-                               const float* conf, float tau, uint8_t* commit,
-                               int32_t* n_commit, float* degree, float* sym, float* key,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+int dapd_run(const void* attn, int dtype, int32_t n_lh, int64_t S, int64_t batch_stride,
+             const int32_t* masked_pos, const int32_t* seq_offsets, int32_t n_seq, int32_t m_max,
+             const float* conf, float tau, const Policy& P, uint8_t* commit, int32_t* n_commit,
+             float* degree, float* sym, float* key, void* workspace, size_t workspace_bytes,
+             void* stream) {
   if (!attn || !masked_pos || !seq_offsets || !conf || !commit || !n_commit || !workspace)
     return DLM_ERR_ARG;
   if (n_lh <= 0 || S <= 0 || n_seq <= 0 || m_max <= 0 || tau != tau) return DLM_ERR_ARG;
+  if (P.late_frac != P.late_frac || P.late_tau != P.late_tau) return DLM_ERR_ARG;
   if (dtype != DLM_BF16 && dtype != DLM_F32) return DLM_ERR_UNSUPPORTED;
   if (m_max > DLM_MAX_SEQ_ROWS || S > 2147483647LL) return DLM_ERR_UNSUPPORTED;
   const int64_t maps = static_cast<int64_t>(n_lh) * S * S;
@@ -430,16 +487,41 @@ extern "C" int dlm_dapd_select(const void* attn, int dtype, int32_t n_lh, int64_
   const dim3 grid(n_ti * n_tc, n_seq);
   if (dtype == DLM_BF16)
     hipLaunchKernelGGL(k_dapd_avg<true>, grid, dim3(kAvgNT), 0, s, attn, n_lh, S, batch_stride,
-                       masked_pos, seq_offsets, m_max, n_tc, vec_ok, ws_a);
+                       masked_pos, seq_offsets, m_max, n_tc, vec_ok, ws_a, P);
   else
     hipLaunchKernelGGL(k_dapd_avg<false>, grid, dim3(kAvgNT), 0, s, attn, n_lh, S, batch_stride,
-                       masked_pos, seq_offsets, m_max, n_tc, vec_ok, ws_a);
+                       masked_pos, seq_offsets, m_max, n_tc, vec_ok, ws_a, P);
   DLM_CHECK_LAUNCH();
   hipLaunchKernelGGL(k_dapd_sym, dim3((m_max + kSymRows - 1) / kSymRows, n_seq), dim3(kSymNT), 0,
-                     s, seq_offsets, m_max, conf, tau, ws, L, degree, sym, key);
+                     s, seq_offsets, m_max, conf, tau, ws, L, degree, sym, key, P);
   DLM_CHECK_LAUNCH();
   hipLaunchKernelGGL(k_dapd_select, dim3(n_seq), dim3(kSelNT), 0, s, seq_offsets, m_max, ws, L,
-                     commit, n_commit, degree, sym, key);
+                     conf, commit, n_commit, degree, sym, key, P);
   DLM_CHECK_LAUNCH();
   return DLM_OK;
+}
+
+}  // namespace
+
+extern "C" int dlm_dapd_select(const void* attn, int dtype, int32_t n_lh, int64_t S,
+                               int64_t batch_stride, const int32_t* masked_pos,
+                               const int32_t* seq_offsets, int32_t n_seq, int32_t m_max,
+                               const float* conf, float tau, uint8_t* commit,
+                               int32_t* n_commit, float* degree, float* sym, float* key,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  const Policy P{nullptr, 0.f, 0.f, 0, nullptr};
+  return dapd_run(attn, dtype, n_lh, S, batch_stride, masked_pos, seq_offsets, n_seq, m_max, conf,
+                  tau, P, commit, n_commit, degree, sym, key, workspace, workspace_bytes, stream);
+}
+
+extern "C" int dlm_dapd_step(const void* attn, int dtype, int32_t n_lh, int64_t S,
+                             int64_t batch_stride, const int32_t* masked_pos,
+                             const int32_t* seq_offsets, int32_t n_seq, int32_t m_max,
+                             const float* conf, float tau, const int32_t* gen_len, float late_frac,
+                             float late_tau, int32_t pre_unmask, uint8_t* commit,
+                             int32_t* n_commit, uint8_t* stage, float* degree, float* sym,
+                             float* key, void* workspace, size_t workspace_bytes, void* stream) {
+  const Policy P{gen_len, late_frac, late_tau, pre_unmask != 0 ? 1 : 0, stage};
+  return dapd_run(attn, dtype, n_lh, S, batch_stride, masked_pos, seq_offsets, n_seq, m_max, conf,
+                  tau, P, commit, n_commit, degree, sym, key, workspace, workspace_bytes, stream);
 }

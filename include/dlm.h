@@ -11,6 +11,12 @@
  *   3. dlm_depcap_boundary — DepCap DepGA-Block boundary scan;
  *   4. dlm_cap_select      — DepCap CAP-Decoding conflict-aware pick;
  *   5. dlm_dapd_select     — DAPD attention graph + Welsh-Powell independent set.
+ * and the schedules around them:
+ *   6. dlm_dapd_step       — DAPD's full step: late-stage threshold switch and
+ *                            pre-unmask of certain rows;
+ *   7. dlm_factor_select   — Fast-dLLM factor decoding (+ Theorem-1 certificate);
+ *   8. dlm_topk_select     — LLaDA's fixed top-K per step;
+ *   9. dlm_fixed_block_eligible — active block of fixed-length block decoding.
  *
  * Conventions for every entry point
  *   - Pointers marked (device) are device pointers owned by the caller; the
@@ -63,7 +69,7 @@ extern "C" {
 /* limits */
 #define DLM_MAX_VOCAB 2147483647LL /* vocab < 2^31                                       */
 #define DLM_MAX_WINDOW 1024        /* DepCap l_max                                        */
-#define DLM_MAX_SEQ_ROWS 1024      /* CAP rows per sequence, DAPD masked positions (m_max)*/
+#define DLM_MAX_SEQ_ROWS 1024      /* CAP, top-K and factor rows per sequence; DAPD m_max */
 #define DLM_MAX_KMAX 128           /* CAP candidate cap                                   */
 
 /* default parameters quoted by the pages */
@@ -80,6 +86,8 @@ extern "C" {
 #define DLM_DAPD_LAYER_FRAC 0.3    /* [DAPD, overall framework]: last ~30% of layers       */
 #define DLM_DAPD_LATE_FRAC 0.5     /* [DAPD, key design 3]: late-stage switch point       */
 #define DLM_DAPD_LATE_TAU 0.9f     /* [DAPD, key design 3]: late-stage threshold          */
+#define DLM_FACTOR_F 1.0f          /* [FastR, Method; Key idea]: f = Theorem 1's bound (a
+                                      reading: the pages give no value)                    */
 
 /*
  * dlm_step_stats — [DepCap, Methodology] H_k = H(p_curr^k) and
@@ -221,6 +229,75 @@ int dlm_dapd_select(const void* attn, int dtype, int32_t n_lh, int64_t S, int64_
                     int32_t m_max, const float* conf, float tau, uint8_t* commit,
                     int32_t* n_commit, float* degree, float* sym, float* key, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * dlm_dapd_step — [DAPD, overall framework; key design 3]: dlm_dapd_select
+ * with the full step policy.  For sequence b with M_b masked rows:
+ *   - late stage iff gen_len != NULL and M_b < late_frac * gen_len[b]
+ *     (evaluated in double; DLM_DAPD_LATE_FRAC = 0.5, "below 50%"): the graph
+ *     is skipped (no attention read) and the rows with conf > late_tau
+ *     (DLM_DAPD_LATE_TAU) are committed, or the most confident row (lowest
+ *     row on ties, NaN never) when none is (a reading: the page gives no
+ *     fallback);
+ *   - otherwise the graph stage of dlm_dapd_select;
+ *   - with pre_unmask != 0, every row whose conf is exactly 1.0f is also
+ *     committed in either stage (the graph is still built over all rows).
+ * gen_len (device int32 [n_seq]) or NULL (never late).  stage (device u8
+ * [n_seq] or NULL): 1 for a late-stage sequence.  degree and key are NaN for
+ * late-stage rows and sym is NaN for late-stage sequences.  Every other
+ * argument, and the errors, are those of dlm_dapd_select; late_frac or
+ * late_tau NaN gives DLM_ERR_ARG.
+ */
+int dlm_dapd_step(const void* attn, int dtype, int32_t n_lh, int64_t S, int64_t batch_stride,
+                  const int32_t* masked_pos, const int32_t* seq_offsets, int32_t n_seq,
+                  int32_t m_max, const float* conf, float tau, const int32_t* gen_len,
+                  float late_frac, float late_tau, int32_t pre_unmask, uint8_t* commit,
+                  int32_t* n_commit, uint8_t* stage, float* degree, float* sym, float* key,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dlm_factor_select — [FastR, Method] factor decoding; [FastR, Key idea]
+ * Theorem 1.  Per sequence, with c(1) >= c(2) >= ... the confidences of the
+ * eligible rows (NaN excluded; ties by lower row), commit the n most
+ * confident rows for the largest n with (n+1)(1 - c(n)) < f, evaluated in
+ * double on the fp32 values (exact).  At least one row is committed when any
+ * is eligible (a reading).  DLM_FACTOR_F = 1 is the theorem's bound.
+ * conf (device f32 [rows]); eligible (device u8 [rows] or NULL = all);
+ * commit (device u8 [rows]); n_commit (device int32 [n_seq]); certificate
+ * (device u8 [n_seq] or NULL): 1 iff n >= 1 and (n+1)(1 - c(n)) <= 1, the
+ * theorem's sufficient condition for the parallel commit to equal greedy
+ * one-token decoding.  A sequence with more than DLM_MAX_SEQ_ROWS rows gets
+ * n_commit = -1 and nothing committed.  f NaN, n_seq <= 0 or a NULL
+ * required pointer: DLM_ERR_ARG.
+ */
+int dlm_factor_select(const float* conf, const uint8_t* eligible, const int32_t* seq_offsets,
+                      int32_t n_seq, float f, uint8_t* commit, int32_t* n_commit,
+                      uint8_t* certificate, void* stream);
+
+/*
+ * dlm_topk_select — [FastR, Prior limitations; Comparison]: LLaDA's default
+ * schedule, the k most confident eligible rows of each sequence whatever
+ * their confidence (ties by lower row; NaN never; all of them when fewer
+ * than k are eligible).  Arguments, limits and errors as dlm_factor_select,
+ * with k >= 1 (else DLM_ERR_ARG).
+ */
+int dlm_topk_select(const float* conf, const uint8_t* eligible, const int32_t* seq_offsets,
+                    int32_t n_seq, int32_t k, uint8_t* commit, int32_t* n_commit, void* stream);
+
+/*
+ * dlm_fixed_block_eligible — [DepCap, Experiments]: confidence decoding with
+ * fixed 16/32/64-token blocks.  Blocks of block_len tile the generation from
+ * its first position gen_start[b] (device int32 [n_seq], values >= 0, or NULL
+ * = 0); eligible[r] = 1 iff masked_pos[r] lies in the earliest block that
+ * still holds a masked position of the sequence (a position before gen_start
+ * is never eligible).  Pass the result to dlm_fastdllm_select as `eligible`.
+ * masked_pos (device int32 [rows], CSR by seq_offsets); eligible (device u8
+ * [rows]).  block_len < 1, n_seq <= 0 or a NULL required pointer:
+ * DLM_ERR_ARG.
+ */
+int dlm_fixed_block_eligible(const int32_t* masked_pos, const int32_t* seq_offsets,
+                             int32_t n_seq, const int32_t* gen_start, int32_t block_len,
+                             uint8_t* eligible, void* stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* dlm_status_string(int status);

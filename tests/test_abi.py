@@ -109,6 +109,26 @@ def test_dapd_validation(L):
         assert f(*bad) == code, (i, v)
 
 
+def test_schedule_validation(L):
+    assert L.dlm_topk_select(FAKE, None, FAKE, 1, 0, FAKE, FAKE, None) == _lib.ERR_ARG      # k < 1
+    assert L.dlm_topk_select(None, None, FAKE, 1, 2, FAKE, FAKE, None) == _lib.ERR_ARG
+    assert L.dlm_topk_select(FAKE, None, FAKE, 0, 2, FAKE, FAKE, None) == _lib.ERR_ARG      # n_seq
+    assert L.dlm_factor_select(FAKE, None, FAKE, 1, math.nan, FAKE, FAKE, None, None) == _lib.ERR_ARG
+    assert L.dlm_factor_select(FAKE, None, FAKE, 1, 1.0, None, FAKE, None, None) == _lib.ERR_ARG
+    assert L.dlm_fixed_block_eligible(FAKE, FAKE, 1, None, 0, FAKE, None) == _lib.ERR_ARG  # len 0
+    assert L.dlm_fixed_block_eligible(FAKE, FAKE, 1, None, 32, None, None) == _lib.ERR_ARG
+    need = L.dlm_dapd_workspace_bytes(2, 64)
+    ok = [FAKE, _lib.BF16, 4, 96, 4 * 96 * 96, FAKE, FAKE, 2, 64, FAKE, 0.01, None, 0.5, 0.9, 1,
+          FAKE, FAKE, None, None, None, None, FAKE, need, None]
+    f = L.dlm_dapd_step
+    for i, v, code in ((12, math.nan, _lib.ERR_ARG), (13, math.nan, _lib.ERR_ARG),
+                       (22, need - 1, _lib.ERR_ARG), (8, 1025, _lib.ERR_UNSUPPORTED),
+                       (15, None, _lib.ERR_ARG)):
+        bad = list(ok)
+        bad[i] = v
+        assert f(*bad) == code, (i, v)
+
+
 def test_binding_fails_loudly_without_device_tensors():
     torch = pytest.importorskip("torch")
     import diffusion_lm_unmask_amd as d
