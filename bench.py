@@ -221,6 +221,144 @@ def cpu_baseline(step: LladaStep, seconds: float):
                       f"in {el:.1f} s on {threads} threads; host CPU: {model}"}
 
 
+def per_call(dev: str, iters: int) -> dict:
+    """Time every entry point on the workloads it is defined on (the five
+    workload shapes of the decision step).  Each measurement captures `iters`
+    calls (rotating input replicas where the inputs would fit in the 256 MB
+    Infinity Cache) in a HIP graph and times replays with HIP events, so small
+    kernels are timed on the GPU rather than through host launch latency.
+    HBM-bound calls also report GB/s against the 8 TB/s peak."""
+    import torch
+    from diffusion_lm_unmask_amd import api, synth
+
+    res = {}
+    stream = torch.cuda.Stream(device=dev)
+
+    def timed(name, fn, n_rep=1, nbytes=None, note=None):
+        # every input was produced on `stream` (see below); wait for it all
+        # before the first use, and keep every launch on that one stream
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for i in range(2):
+                fn(i % n_rep)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(iters):
+                fn(i % n_rep)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        with torch.cuda.stream(stream):
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / (reps * iters)
+        entry = {"us": round(us, 2)}
+        if nbytes:
+            entry["GB/s"] = round(nbytes / us / 1e3, 1)
+            entry["frac_of_peak"] = round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)
+        if note:
+            entry["workload"] = note
+        res[name] = entry
+        print(f"[calls] {name}: {entry}", file=sys.stderr, flush=True)
+        del g
+
+    def stats_of(name, replicas):
+        spec = synth.SPECS[name]
+        cur, prev, so, ri = synth.logits(name, dev)
+        curs = [cur] + [cur.clone() for _ in range(replicas - 1)]
+        prevs = None if prev is None else [prev] + [prev.clone() for _ in range(replicas - 1)]
+        nb = cur.numel() * cur.element_size() * (1 if prev is None else 2)
+        timed(f"step_stats/{name}",
+              lambda r: api.step_stats(curs[r], None if prevs is None else prevs[r]),
+              replicas, nb, f"{cur.shape[0]} rows x V={spec.vocab} "
+                            f"{'cur+prev' if prev is not None else 'cur'} {cur.dtype}")
+        st = api.step_stats(cur, prev)
+        return spec, cur, prev, so, ri, st, curs
+
+    def schedules(tag, st, so, el, pos, offs):
+        conf = st["conf"]
+        gs = pos[offs[:-1].long()].contiguous()  # each sequence's first masked position
+        timed(f"fastdllm_select/{tag}", lambda r: api.fastdllm_select(conf, so, 0.9, eligible=el))
+        timed(f"topk_select/{tag}", lambda r: api.topk_select(conf, so, 2, eligible=el))
+        timed(f"factor_select/{tag}", lambda r: api.factor_select(conf, so, 1.0, eligible=el))
+        timed(f"fixed_block_eligible/{tag}",
+              lambda r: api.fixed_block_eligible(pos, offs, 32, gen_start=gs))
+
+    with torch.cuda.stream(stream):
+        return _per_call_body(dev, timed, stats_of, schedules, res)
+
+
+def _per_call_body(dev, timed, stats_of, schedules, res):
+    """The workloads of per_call, run with its stream current: the inputs,
+    the reference statistics the rules consume and every timed call are
+    ordered on one stream."""
+    import torch
+    from diffusion_lm_unmask_amd import api, synth
+
+    # tiny
+    spec, cur, prev, so, ri, st, _ = stats_of("tiny", 4)
+    del cur, prev, st
+    # llada-shaped step inputs
+    spec, cur, prev, so, ri, st, curs = stats_of("llada", 4)
+    R = synth.RULES["llada"]
+    block = torch.zeros(cur.shape[0], device=dev, dtype=torch.uint8)
+    block[R["fast_block"][0]:R["fast_block"][1]] = 1
+    pos, offs = synth.gen_positions("llada", dev)
+    schedules("llada", st, so, block, pos, offs)
+    timed("depcap_boundary/llada", lambda r: api.depcap_boundary(st["kl"], st["entropy"], so))
+    timed("cap_select/llada", lambda r: api.cap_select(
+        curs[r], ri, so, st["conf"], st["argmax"], st["lse"], eligible=block, k_max=R["k_max"]), 4)
+    attn = [synth.attention("llada", dev, batch=1) for _ in range(4)]
+    ws = torch.empty(api.dapd_workspace_bytes(1, 256), device=dev, dtype=torch.uint8)
+    nb = 320 * 256 * 256 * 2 + 256 * 256 * 4
+    timed("dapd_select/llada", lambda r: api.dapd_select(attn[r], pos, offs, st["conf"], 0.01,
+                                                         m_max=256, workspace=ws), 4, nb,
+          "1 x [320, 768, 768] bf16 maps, 256 masked")
+    del cur, prev, curs, attn, st
+    torch.cuda.empty_cache()
+    # dream: CAP with K_max 64 over every row
+    spec, cur, prev, so, ri, st, _ = stats_of("dream", 1)
+    Rd = synth.RULES["dream"]
+    timed("cap_select/dream", lambda r: api.cap_select(
+        cur, ri, so, st["conf"], st["argmax"], st["lse"], tau_low=Rd["tau_low"],
+        k_max=Rd["k_max"]))
+    del cur, st
+    torch.cuda.empty_cache()
+    # dapd: 8 sequences, plain selection and the full step (half of them late)
+    spec, cur, prev, so, ri, st, _ = stats_of("dapd", 2)
+    pos, offs = synth.gen_positions("dapd", dev)
+    attn = [synth.attention("dapd", dev, variant="cov", masked_pos=pos[:spec.rows])]
+    ws = torch.empty(api.dapd_workspace_bytes(spec.batch, 256), device=dev, dtype=torch.uint8)
+    nb = spec.batch * (320 * 256 * 256 * 2 + 256 * 256 * 4)
+    timed("dapd_select/dapd", lambda r: api.dapd_select(attn[0], pos, offs, st["conf"], 0.01,
+                                                        m_max=256, workspace=ws), 1, nb,
+          "8 x [320, 768, 768] bf16 maps, 256 masked each, partner-covariance variant")
+    gen_len = torch.tensor([256, 384, 512, 600, 256, 700, 1000, 400], device=dev,
+                           dtype=torch.int32)
+    timed("dapd_step/dapd", lambda r: api.dapd_step(attn[0], pos, offs, st["conf"], 0.01,
+                                                    gen_len=gen_len, m_max=256, workspace=ws),
+          1, None, "same, 3 of 8 sequences in the late stage")
+    del cur, attn, st
+    torch.cuda.empty_cache()
+    # stress: 64 x 1024 rows with prev (33 GB)
+    spec, cur, prev, so, ri, st, _ = stats_of("stress", 1)
+    pos = (torch.arange(1024, device=dev, dtype=torch.int32) + 512).repeat(spec.batch)
+    schedules("stress", st, so, None, pos, so)
+    timed("depcap_boundary/stress", lambda r: api.depcap_boundary(st["kl"], st["entropy"], so))
+    timed("cap_select/stress", lambda r: api.cap_select(cur, ri, so, st["conf"], st["argmax"],
+                                                        st["lse"], k_max=128))
+    del cur, prev, st
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,6 +373,9 @@ def main() -> int:
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
                     help="graph: the step is captured once per input replica and replayed")
+    ap.add_argument("--calls", action="store_true",
+                    help="only time every entry point on its workloads and print one JSON line")
+    ap.add_argument("--call-iters", type=int, default=20)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -256,6 +397,10 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": n, "copies": 10}), flush=True)
+        return 0
+    if args.calls:
+        print(json.dumps({"calls": per_call(dev, args.call_iters), "n_gpus": 1,
+                          "data": "synthetic"}), flush=True)
         return 0
     step = LladaStep(args.replicas, dev)
     R = args.replicas

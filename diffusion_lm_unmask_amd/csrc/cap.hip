@@ -55,7 +55,8 @@ __device__ __forceinline__ float gather(const void* logits, int64_t idx) {
 
 template <bool BF16>
 __global__ __launch_bounds__(kNT) void k_cap(
-    const void* __restrict__ logits, int64_t ld, const int64_t* __restrict__ row_index,
+    const void* __restrict__ logits, int64_t ld, int64_t vocab,
+    const int64_t* __restrict__ row_index,
     const int32_t* __restrict__ seq_offsets, const float* __restrict__ conf,
     const int32_t* __restrict__ argmax, const float* __restrict__ lse,
     const uint8_t* __restrict__ eligible, float tau_low, float tau_high, float gamma, int k_max,
@@ -70,22 +71,29 @@ __global__ __launch_bounds__(kNT) void k_cap(
   __shared__ uint32_t sel[kMaxRows / 32];
   __shared__ float shf[kNT / DLM_WAVE];
   __shared__ int shi[kNT / DLM_WAVE];
-  __shared__ int npool;
+  __shared__ int npool, bad;
 
   const int b = blockIdx.x, tid = threadIdx.x;
   const int lo = seq_offsets[b], n = seq_offsets[b + 1] - lo;
   const int64_t dbase = static_cast<int64_t>(b) * k_max * k_max;
 
-  if (n > kMaxRows || n < 0) {  // device-side limit: report, commit nothing
+  // a violated device-side precondition: commit nothing, report -1
+  auto report = [&]() {
     for (int r = tid; r < n; r += kNT) commit[lo + r] = 0;
     if (cand_out)
       for (int a = tid; a < k_max; a += kNT) cand_out[b * k_max + a] = -1;
     if (dmat_out)
       for (int e = tid; e < k_max * k_max; e += kNT) dmat_out[dbase + e] = NAN;
     if (tid == 0) n_commit[b] = -1;
+  };
+  if (n > kMaxRows || n < 0) {  // device-side limit
+    report();
     return;
   }
-  if (tid == 0) npool = 0;
+  if (tid == 0) {
+    npool = 0;
+    bad = 0;
+  }
   for (int w = tid; w < kMaxRows / 32; w += kNT) sel[w] = 0u;
   __syncthreads();
 
@@ -132,8 +140,14 @@ __global__ __launch_bounds__(kNT) void k_cap(
     cy[a] = argmax[r];
     clse[a] = lse[r];
     coff[a] = row_index[r] * ld;
+    // every gather below is at coff[.] + cy[.]: check the indices first
+    if (cy[a] < 0 || cy[a] >= vocab || row_index[r] < 0) bad = 1;
   }
   __syncthreads();
+  if (bad) {  // an argmax outside [0, vocab) or a negative row index
+    report();
+    return;
+  }
 
   // 3. gathers G[a][b] = log p_a(yhat_b), eight in flight per lane
   const int KK = K * K;
@@ -222,11 +236,11 @@ extern "C" int dlm_cap_select(const void* logits, int dtype, int64_t vocab, int6
   if (reinterpret_cast<uintptr_t>(logits) % es) return DLM_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == DLM_BF16)
-    hipLaunchKernelGGL(k_cap<true>, dim3(n_seq), dim3(kNT), 0, s, logits, ld, row_index,
+    hipLaunchKernelGGL(k_cap<true>, dim3(n_seq), dim3(kNT), 0, s, logits, ld, vocab, row_index,
                        seq_offsets, conf, argmax, lse, eligible, tau_low, tau_high, gamma,
                        k_max, commit, n_commit, cand, dmat);
   else
-    hipLaunchKernelGGL(k_cap<false>, dim3(n_seq), dim3(kNT), 0, s, logits, ld, row_index,
+    hipLaunchKernelGGL(k_cap<false>, dim3(n_seq), dim3(kNT), 0, s, logits, ld, vocab, row_index,
                        seq_offsets, conf, argmax, lse, eligible, tau_low, tau_high, gamma,
                        k_max, commit, n_commit, cand, dmat);
   DLM_CHECK_LAUNCH();

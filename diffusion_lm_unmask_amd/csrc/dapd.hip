@@ -92,8 +92,10 @@ __global__ __launch_bounds__(kAvgNT) void k_dapd_avg(const void* __restrict__ at
   const int g = threadIdx.x / kItems, it = threadIdx.x % kItems;
   const int i = i0 + it / kTileChunks, c = c0 + it % kTileChunks;
   const int j0 = c * 8;
-  const bool item_ok = i < M && j0 < M;
   const int* pos = masked_pos + lo;
+  // positions outside [0, S) are never dereferenced (k_dapd_select reports
+  // the sequence)
+  const bool item_ok = i < M && j0 < M && pos[i] >= 0 && pos[i] < S;
 
   float acc[8];
 #pragma unroll
@@ -106,7 +108,8 @@ __global__ __launch_bounds__(kAvgNT) void k_dapd_avg(const void* __restrict__ at
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       pj[k] = (j0 + k < M) ? pos[j0 + k] : -1;
-      contig = contig && (pj[k] == pj[0] + k);
+      if (pj[k] >= S) pj[k] = -1;
+      contig = contig && (pj[k] >= 0) && (pj[k] == pj[0] + k);
     }
     contig = contig && (pj[0] % (BF16 ? 8 : 4) == 0);
     const char* base = static_cast<const char*>(attn) +
@@ -305,6 +308,7 @@ __global__ __launch_bounds__(kSymNT) void k_dapd_sym(
 
 // Per sequence: load the graph into LDS, order the nodes, run the greedy.
 __global__ __launch_bounds__(kSelNT) void k_dapd_select(
+    const int32_t* __restrict__ masked_pos, int64_t S,
     const int32_t* __restrict__ seq_offsets, int m_max, const char* __restrict__ ws, Layout L,
     const float* __restrict__ conf, uint8_t* __restrict__ commit, int32_t* __restrict__ n_commit,
     float* __restrict__ degree, float* __restrict__ sym, float* __restrict__ key_out, Policy P) {
@@ -320,7 +324,13 @@ __global__ __launch_bounds__(kSelNT) void k_dapd_select(
   const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
   const int64_t sbase = static_cast<int64_t>(b) * m_max * m_max;
 
-  if (M > m_max || M < 0) {
+  int bad_pos = 0;  // a masked position outside [0, S): the sequence is reported
+  for (int r = tid; r < M && M <= m_max; r += kSelNT) {
+    const int p = masked_pos[lo + r];
+    bad_pos |= p < 0 || p >= S;
+  }
+  bad_pos = dlm::block_max_i<kSelNT>(bad_pos, shi);
+  if (M > m_max || M < 0 || bad_pos) {
     for (int r = tid; r < M; r += kSelNT) {
       commit[lo + r] = 0;
       if (degree) degree[lo + r] = NAN;
@@ -495,8 +505,8 @@ int dapd_run(const void* attn, int dtype, int32_t n_lh, int64_t S, int64_t batch
   hipLaunchKernelGGL(k_dapd_sym, dim3((m_max + kSymRows - 1) / kSymRows, n_seq), dim3(kSymNT), 0,
                      s, seq_offsets, m_max, conf, tau, ws, L, degree, sym, key, P);
   DLM_CHECK_LAUNCH();
-  hipLaunchKernelGGL(k_dapd_select, dim3(n_seq), dim3(kSelNT), 0, s, seq_offsets, m_max, ws, L,
-                     conf, commit, n_commit, degree, sym, key, P);
+  hipLaunchKernelGGL(k_dapd_select, dim3(n_seq), dim3(kSelNT), 0, s, masked_pos, S, seq_offsets,
+                     m_max, ws, L, conf, commit, n_commit, degree, sym, key, P);
   DLM_CHECK_LAUNCH();
   return DLM_OK;
 }

@@ -183,7 +183,10 @@ int dlm_depcap_boundary(const float* kl, const float* entropy, const int32_t* se
  * gathered at (candidate row, candidate argmax).  conf, argmax, lse: the
  * outputs of dlm_step_stats for the same rows.
  * Limits: rows per sequence <= 1024 (else n_commit[b] = -1 and no commit);
- * 1 <= k_max <= 128.
+ * 1 <= k_max <= 128.  Before any gather, every candidate's argmax is checked
+ * to lie in [0, vocab) and its row_index to be >= 0; a sequence failing the
+ * check gets n_commit[b] = -1 and no commit (row_index values past the end
+ * of the logits cannot be checked: the caller keeps them in range).
  * commit (device u8 [rows]); n_commit (device int32 [n_seq]);
  * cand (device int32 [n_seq*k_max] or NULL): candidate rows in priority
  * order, -1 pad; dmat (device f32 [n_seq*k_max*k_max] or NULL): D in
@@ -215,9 +218,11 @@ size_t dlm_dapd_workspace_bytes(int32_t n_seq, int32_t m_max);
  *   into the chosen set (Welsh-Powell order); NaN keys are never chosen.
  * attn (device, dtype): sequence b's maps start at attn + b*batch_stride
  * elements; map lh is the S x S row-major matrix at offset lh*S*S.
- * masked_pos (device int32 [rows], CSR by seq_offsets): positions in [0, S).
- * conf (device f32 [rows]) in the same row order.  1 <= m_max <= 1024 bounds
- * the masked positions per sequence (a longer sequence gets n_commit = -1).
+ * masked_pos (device int32 [rows], CSR by seq_offsets): positions in [0, S);
+ * a sequence holding a position outside it is never read and gets
+ * n_commit = -1.  conf (device f32 [rows]) in the same row order.
+ * 1 <= m_max <= 1024 bounds the masked positions per sequence (a longer
+ * sequence gets n_commit = -1).
  * workspace (device, >= dlm_dapd_workspace_bytes(n_seq, m_max) bytes, 256-byte
  * aligned): scratch, overwritten.
  * commit (device u8 [rows]); n_commit (device int32 [n_seq]); degree, key

@@ -326,3 +326,49 @@ def test_dapd_scattered_positions_and_edges():
     # a sequence longer than m_max is reported
     out = api.dapd_select(attn, pos, so, g["conf"], 0.01, m_max=30)
     assert host(out["n_commit"]).tolist() == [-1, -1, -1]
+
+
+def test_cap_reports_out_of_range_argmax():
+    # the kernel checks each candidate's argmax before gathering: a sequence
+    # whose candidates carry an index outside [0, vocab) is reported, the
+    # others are decided as usual
+    cur, prev, so, ri = synth.logits("tiny", DEV)
+    g = api.step_stats(cur)
+    so3 = torch.tensor([0, 12, 24, 32], device=DEV, dtype=torch.int32)
+    # tau_low 0 and k_max 16 make every row of a 12-row sequence a candidate
+    ref = api.cap_select(cur, ri, so3, g["conf"], g["argmax"], g["lse"], tau_low=0.0, k_max=16)
+    for bad in (cur.shape[1], -1):
+        am = g["argmax"].clone()
+        am[13] = bad                                  # a candidate of sequence 1
+        out = api.cap_select(cur, ri, so3, g["conf"], am, g["lse"], tau_low=0.0, k_max=16,
+                             want_cand=True)
+        torch.cuda.synchronize()
+        assert host(out["n_commit"]).tolist()[1] == -1
+        assert int(host(out["commit"])[12:24].sum()) == 0
+        assert bool(torch.all(out["cand"][1] == -1))
+        for lo, hi, b in ((0, 12, 0), (24, 32, 2)):
+            assert torch.equal(out["commit"][lo:hi], ref["commit"][lo:hi])
+            assert int(host(out["n_commit"])[b]) == int(host(ref["n_commit"])[b])
+
+
+def test_dapd_reports_out_of_range_position():
+    # a masked position outside [0, S) is never dereferenced; its sequence is
+    # reported and the other sequences keep their selection
+    spec = synth.SPECS["tiny"]
+    cur, prev, so, ri = synth.logits("tiny", DEV)
+    g = api.step_stats(cur)
+    attn = torch.cat([synth.attention("tiny", DEV)] * 3)
+    pos = torch.cat([torch.arange(32, device=DEV, dtype=torch.int32)[:10]] * 3).contiguous()
+    so3 = torch.tensor([0, 10, 20, 30], device=DEV, dtype=torch.int32)
+    conf = g["conf"][:30].contiguous()
+    ref = api.dapd_select(attn, pos, so3, conf, 0.01, m_max=16)
+    for bad in (spec.seq_len, -3):
+        p2 = pos.clone()
+        p2[14] = bad                                  # sequence 1
+        out = api.dapd_select(attn, p2, so3, conf, 0.01, m_max=16, want_sym=True)
+        torch.cuda.synchronize()
+        assert host(out["n_commit"]).tolist()[1] == -1
+        assert int(host(out["commit"])[10:20].sum()) == 0
+        assert bool(torch.all(torch.isnan(out["sym"][1])))
+        for lo, hi, b in ((0, 10, 0), (20, 30, 2)):
+            assert torch.equal(out["commit"][lo:hi], ref["commit"][lo:hi])
