@@ -20,33 +20,6 @@ constexpr int kNT = 256;
 constexpr int kMaxRows = DLM_MAX_SEQ_ROWS;
 constexpr int kKM = DLM_MAX_KMAX;
 
-// 32-bit key whose unsigned ascending order is the float's descending order.
-__device__ __forceinline__ uint32_t desc_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ~asc;
-}
-
-// Bitonic sort of n (power of two, <= kMaxRows) 64-bit keys in LDS, ascending.
-template <int NT>
-__device__ void bitonic_sort(uint64_t* keys, int n) {
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int t = threadIdx.x; t < n / 2; t += NT) {
-        const int i = 2 * j * (t / j) + (t % j);
-        const int p = i + j;
-        const bool up = (i & k) == 0;
-        const uint64_t a = keys[i], b = keys[p];
-        if ((a > b) == up) {
-          keys[i] = b;
-          keys[p] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
 template <bool BF16>
 __device__ __forceinline__ float gather(const void* logits, int64_t idx) {
   if constexpr (BF16) return dlm::bf16_at(static_cast<const uint16_t*>(logits), idx);
@@ -110,7 +83,7 @@ __global__ __launch_bounds__(kNT) void k_cap(
     }
     if (c >= tau_low) {
       const int slot = atomicAdd(&npool, 1);
-      keys[slot] = (static_cast<uint64_t>(desc_bits(c)) << 32) | static_cast<uint32_t>(r);
+      keys[slot] = (static_cast<uint64_t>(dlm::desc_bits(c)) << 32) | static_cast<uint32_t>(r);
     }
   }
   __syncthreads();
@@ -119,7 +92,7 @@ __global__ __launch_bounds__(kNT) void k_cap(
   while (n2 < P) n2 <<= 1;
   for (int i = P + tid; i < n2; i += kNT) keys[i] = ~0ull;
   __syncthreads();
-  if (P > 1) bitonic_sort<kNT>(keys, n2);
+  if (P > 1) dlm::bitonic_sort<kNT>(keys, n2);
   const int K = min(P, k_max);
 
   if (K == 0) {  // 2. no candidate: top-1 eligible row

@@ -185,12 +185,6 @@ __global__ __launch_bounds__(kAvgNT) void k_dapd_avg(const void* __restrict__ at
   }
 }
 
-__device__ __forceinline__ uint32_t desc_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ~asc;
-}
-
 // Workspace layout (every region 256-byte aligned), for n_seq x m_max:
 //   a          f32 [n_seq][m_max][ws_ld]     averaged maps
 //   adj        u64 [n_seq][m_max][words]     adjacency bitsets, words = ceil(m_max/64)
@@ -297,7 +291,7 @@ __global__ __launch_bounds__(kSymNT) void k_dapd_sym(
     const float kk = df * conf[lo + i];
     if (degree) degree[lo + i] = df;
     if (key_out) key_out[lo + i] = kk;
-    const uint64_t hi = (kk != kk) ? 0xffffffffull : static_cast<uint64_t>(desc_bits(kk));
+    const uint64_t hi = (kk != kk) ? 0xffffffffull : static_cast<uint64_t>(dlm::desc_bits(kk));
     // NaN keys sort last; every other key maps below 0xffffffff
     reinterpret_cast<uint64_t*>(const_cast<char*>(ws) + L.keys)[static_cast<int64_t>(b) * m_max + i] =
         (hi << 32) | static_cast<uint32_t>(i);

@@ -1,5 +1,6 @@
 // dlm_device.h — small device helpers shared by the library's kernels:
-// bf16 unpacking, 64-wide wavefront reductions and workgroup reductions.
+// bf16 unpacking, 64-wide wavefront reductions (shuffle and DPP), sort keys,
+// an LDS bitonic sort and workgroup reductions.
 // gfx950 only (wave64).
 #pragma once
 #include <hip/hip_runtime.h>
@@ -89,6 +90,36 @@ struct OpMaxF {
 struct OpMinI {
   __device__ int operator()(int a, int b) const { return min(a, b); }
 };
+
+// Order-preserving key of a float for a descending sort: a larger value gives
+// a smaller key (NaN is the caller's to exclude); -0 and +0 share a key, so
+// equal values tie and a secondary key (a row in the low bits) decides.
+__device__ __forceinline__ uint32_t desc_bits(float f) {
+  const uint32_t u = f == 0.f ? 0u : __float_as_uint(f);
+  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ~asc;
+}
+
+// Bitonic sort of n (a power of two) 64-bit keys in LDS, ascending; every
+// thread of the NT-thread workgroup must call it.
+template <int NT>
+__device__ void bitonic_sort(uint64_t* keys, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int t = threadIdx.x; t < n / 2; t += NT) {
+        const int i = 2 * j * (t / j) + (t % j);
+        const int p = i + j;
+        const bool up = (i & k) == 0;
+        const uint64_t a = keys[i], b = keys[p];
+        if ((a > b) == up) {
+          keys[i] = b;
+          keys[p] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
 
 // Workgroup reductions. `sh` must hold NT/64 elements; every thread gets the
 // result.  Each call ends with a barrier-protected read, so `sh` may be

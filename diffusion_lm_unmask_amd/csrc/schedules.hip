@@ -11,83 +11,115 @@
 //    blocks (DepCap summary, Experiments): the masked rows of the earliest
 //    block that still holds a mask.
 //
-// k_rank_select: one workgroup (1024 threads) per sequence, one row per
-// thread.  A row's rank in (conf desc, row asc) order among the eligible
-// non-NaN rows is counted against the sequence's confidences held in LDS
-// (broadcast reads, four per ds_read_b128).  Both rules then follow from the
-// ranks; factor decoding takes the largest admissible rank (a max
-// reduction), so it equals "the largest n" for any input, monotone or not.
-// The factor test runs in fp64 on the fp32 confidences, where it is exact.
+// k_rank_select: one workgroup (256 threads) per sequence.  The eligible
+// non-NaN rows are keyed (confidence descending, row ascending), gathered
+// into LDS (slot order is irrelevant: the sort decides) and sorted: up to 64
+// keys by one wave in registers (shuffle bitonic network, no barriers), more
+// with the LDS bitonic sort.  Position t of the sorted keys is the row of rank
+// t.  Top-K takes positions < K; factor decoding tests (t+2)(1 - c) < f at
+// every position and takes the largest admissible one (a max reduction, so
+// it equals "the largest n" for any input, monotone or not).  The test runs
+// in fp64 on the fp32 confidences, where it is exact.
 #include <math.h>
 
 #include "dlm_device.h"
 
 namespace {
 
-constexpr int kRankNT = DLM_MAX_SEQ_ROWS;  // one thread per row
+constexpr int kRankNT = 256;
+constexpr int kRankMax = DLM_MAX_SEQ_ROWS;  // rows per sequence
 constexpr int kBlockNT = 256;
 
 enum Mode { kTopK = 0, kFactor = 1 };
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, DLM_WAVE);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, DLM_WAVE);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
 
 template <int MODE>
 __global__ __launch_bounds__(kRankNT) void k_rank_select(
     const float* __restrict__ conf, const uint8_t* __restrict__ eligible,
     const int32_t* __restrict__ seq_offsets, int k, float f, uint8_t* __restrict__ commit,
     int32_t* __restrict__ n_commit, uint8_t* __restrict__ certificate) {
-  __shared__ __align__(16) float cs[kRankNT];  // confidence, NaN when not a candidate
+  __shared__ uint64_t keys[kRankMax];  // candidates' (desc conf, row), then ~0 padding
+  __shared__ float cs[kRankMax];       // confidence by row
+  __shared__ uint8_t take[kRankMax];   // selected, by row
   __shared__ int shi[kRankNT / DLM_WAVE];
-  const int b = blockIdx.x, i = threadIdx.x;
+  __shared__ int cnt;
+  const int b = blockIdx.x, tid = threadIdx.x;
   const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
-  if (M > kRankNT || M < 0) {  // over-long sequence: nothing committed, reported as -1
-    for (int r = i; r < M; r += kRankNT) commit[lo + r] = 0;
-    if (i == 0) {
+  if (M > kRankMax || M < 0) {  // over-long sequence: nothing committed, reported as -1
+    for (int r = tid; r < M; r += kRankNT) commit[lo + r] = 0;
+    if (tid == 0) {
       n_commit[b] = -1;
       if (MODE == kFactor && certificate) certificate[b] = 0;
     }
     return;
   }
-  float c = NAN;
-  if (i < M && (!eligible || eligible[lo + i])) c = conf[lo + i];
-  const bool ok = c == c;
-  cs[i] = c;  // rows >= M hold NaN
+  if (tid == 0) cnt = 0;
   __syncthreads();
-
-  // rank = candidates before this row: higher confidence, or equal and lower row
-  int rank = 0;
-  if (ok) {
-    const float4* c4 = reinterpret_cast<const float4*>(cs);
-    const int n4 = (M + 3) / 4;
-    for (int q = 0; q < n4; ++q) {
-      const float4 v = c4[q];
-      const int j = 4 * q;
-      rank += (v.x > c) | ((v.x == c) & (j + 0 < i));
-      rank += (v.y > c) | ((v.y == c) & (j + 1 < i));
-      rank += (v.z > c) | ((v.z == c) & (j + 2 < i));
-      rank += (v.w > c) | ((v.w == c) & (j + 3 < i));
+  for (int r = tid; r < M; r += kRankNT) {
+    float c = NAN;
+    if (!eligible || eligible[lo + r]) c = conf[lo + r];
+    cs[r] = c;
+    take[r] = 0;
+    if (c == c) {
+      const int slot = atomicAdd(&cnt, 1);
+      keys[slot] = (static_cast<uint64_t>(dlm::desc_bits(c)) << 32) | static_cast<uint32_t>(r);
     }
   }
-  const int n_ok = dlm::block_sum<kRankNT>(ok ? 1 : 0, shi);
+  __syncthreads();
+  const int n_ok = cnt;
+  int n2 = 1;
+  while (n2 < n_ok) n2 <<= 1;
+  for (int s = n_ok + tid; s < n2; s += kRankNT) keys[s] = ~0ull;
+  __syncthreads();
+  if (n2 <= DLM_WAVE) {
+    if (tid < DLM_WAVE) {  // one wave, in registers: lane l holds key l
+      uint64_t v = tid < n2 ? keys[tid] : ~0ull;
+      for (int kk = 2; kk <= n2; kk <<= 1) {
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+          const uint64_t o = shfl_xor64(v, j);
+          // the lower lane of a pair keeps the min in an ascending run
+          const bool keep_min = ((tid & j) == 0) == ((tid & kk) == 0);
+          v = keep_min ? (v < o ? v : o) : (v < o ? o : v);
+        }
+      }
+      if (tid < n2) keys[tid] = v;
+    }
+    __syncthreads();
+  } else {
+    dlm::bitonic_sort<kRankNT>(keys, n2);
+  }
   int n;
   if constexpr (MODE == kTopK) {
     n = min(k, n_ok);
   } else {
-    const bool adm =
-        ok && static_cast<double>(rank + 2) * (1.0 - static_cast<double>(c)) <
-                  static_cast<double>(f);
-    n = dlm::block_max_i<kRankNT>(adm ? rank + 1 : 0, shi);
+    int adm = 0;  // largest admissible position + 1 among this thread's positions
+    for (int t = tid; t < n_ok; t += kRankNT) {
+      const float ct = cs[keys[t] & 0xffffffffu];
+      if (static_cast<double>(t + 2) * (1.0 - static_cast<double>(ct)) < static_cast<double>(f))
+        adm = t + 1;
+    }
+    n = dlm::block_max_i<kRankNT>(adm, shi);
     if (n == 0 && n_ok > 0) n = 1;  // progress: the most confident row
     if (certificate) {
       if (n == 0) {
-        if (i == 0) certificate[b] = 0;
-      } else if (ok && rank == n - 1) {
+        if (tid == 0) certificate[b] = 0;
+      } else if ((n - 1) % kRankNT == tid) {
+        const float ct = cs[keys[n - 1] & 0xffffffffu];
         certificate[b] = static_cast<uint8_t>(static_cast<double>(n + 1) *
-                                                  (1.0 - static_cast<double>(c)) <=
+                                                  (1.0 - static_cast<double>(ct)) <=
                                               1.0);
       }
     }
   }
-  if (i < M) commit[lo + i] = static_cast<uint8_t>(ok && rank < n);
-  if (i == 0) n_commit[b] = n;
+  for (int t = tid; t < n; t += kRankNT) take[keys[t] & 0xffffffffu] = 1;
+  __syncthreads();
+  for (int r = tid; r < M; r += kRankNT) commit[lo + r] = take[r];
+  if (tid == 0) n_commit[b] = n;
 }
 
 __global__ __launch_bounds__(kBlockNT) void k_fixed_block(const int32_t* __restrict__ masked_pos,
