@@ -40,8 +40,27 @@ SIGNATURES = {
     "dlm_factor_select": (_INT, [_P, _P, _P, _I32, _F, _P, _P, _P, _P]),
     "dlm_topk_select": (_INT, [_P, _P, _P, _I32, _I32, _P, _P, _P]),
     "dlm_fixed_block_eligible": (_INT, [_P, _P, _I32, _P, _I32, _P, _P]),
+    "dlm_decide_step": (_INT, [_P, _P]),
     "dlm_status_string": (ctypes.c_char_p, [_INT]),
 }
+
+
+class StepDesc(ctypes.Structure):
+    """ctypes mirror of `dlm_step_desc` (include/dlm.h), field for field."""
+    _fields_ = [
+        ("logits", _P), ("prev_logits", _P), ("dtype", _I32), ("vocab", _I64), ("ld", _I64),
+        ("row_index", _P), ("n_rows", _I64), ("conf", _P), ("argmax", _P), ("entropy", _P),
+        ("kl", _P), ("lse", _P), ("seq_offsets", _P), ("n_seq", _I32),
+        ("fast_eligible", _P), ("fast_tau", _F), ("fast_commit", _P), ("fast_n_commit", _P),
+        ("depcap_has_prev", _P), ("depcap_lambda", _D), ("depcap_l_min", _I32),
+        ("depcap_l_max", _I32), ("depcap_radius", _I32), ("depcap_eps", _D),
+        ("depcap_block_len", _P), ("depcap_score", _P),
+        ("cap_eligible", _P), ("cap_tau_low", _F), ("cap_tau_high", _F), ("cap_gamma", _F),
+        ("cap_k_max", _I32), ("cap_commit", _P), ("cap_n_commit", _P),
+        ("attn", _P), ("attn_dtype", _I32), ("n_lh", _I32), ("S", _I64), ("batch_stride", _I64),
+        ("masked_pos", _P), ("m_max", _I32), ("dapd_tau", _F), ("dapd_commit", _P),
+        ("dapd_n_commit", _P), ("dapd_workspace", _P), ("dapd_workspace_bytes", _SZ),
+    ]
 
 
 class DLMError(RuntimeError):

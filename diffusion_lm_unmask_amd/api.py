@@ -7,6 +7,8 @@ only: every step of the computation runs in the library's kernels.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -314,3 +316,98 @@ def fixed_block_eligible(masked_pos, seq_offsets, block_len, gen_start=None):
                                              _stream(masked_pos))
     _lib.check(st, "dlm_fixed_block_eligible")
     return el
+
+
+def decide_step(logits, prev=None, seq_offsets=None, row_index=None, vocab=None, fast=None,
+                depcap=None, cap=None, dapd=None):
+    """dlm_decide_step: statistics plus the enabled rules in three launches.
+
+    Each rule part is None (off) or a dict of its parameters, named as in the
+    individual wrappers:
+      fast   = dict(eligible=None, tau=0.9)
+      depcap = dict(has_prev=None, lam=1.2, l_min=8, l_max=128, radius=1, eps=1e-12)
+      cap    = dict(eligible=None, tau_low=0.8, tau_high=0.95, gamma=-16.0, k_max=64)
+      dapd   = dict(attn=..., masked_pos=..., m_max=..., tau=0.01, workspace=None)
+    Returns a dict with the statistics (conf, argmax, entropy, kl, lse) and, per
+    enabled part, its outputs (fast / depcap / cap / dapd)."""
+    ld = _rows2d(logits, "logits")
+    dev = logits.device
+    vocab = logits.shape[1] if vocab is None else int(vocab)
+    if prev is not None:
+        _rows2d(prev, "prev")
+        if prev.dtype != logits.dtype or prev.stride(0) != ld or prev.shape != logits.shape:
+            raise DLMError("prev must match logits in dtype, shape and strides")
+    if row_index is None:
+        row_index = torch.arange(logits.shape[0], device=dev, dtype=torch.int64)
+    _vec(row_index, "row_index", torch.int64, dev)
+    if seq_offsets is None:
+        seq_offsets = torch.tensor([0, row_index.numel()], device=dev, dtype=torch.int32)
+    _vec(seq_offsets, "seq_offsets", torch.int32, dev)
+    n = row_index.numel()
+    n_seq = seq_offsets.numel() - 1
+    f = dict(device=dev, dtype=torch.float32)
+    i32 = dict(device=dev, dtype=torch.int32)
+    u8 = dict(device=dev, dtype=torch.uint8)
+    out = {"conf": torch.empty(n, **f), "argmax": torch.empty(n, **i32),
+           "entropy": torch.empty(n, **f), "lse": torch.empty(n, **f),
+           "kl": torch.empty(n, **f) if prev is not None else None}
+    d = _lib.StepDesc()
+    d.logits, d.prev_logits = logits.data_ptr(), _ptr(prev)
+    d.dtype, d.vocab, d.ld = _dtype_code(logits), vocab, ld
+    d.row_index, d.n_rows = row_index.data_ptr(), n
+    d.conf, d.argmax = out["conf"].data_ptr(), out["argmax"].data_ptr()
+    d.entropy, d.kl, d.lse = out["entropy"].data_ptr(), _ptr(out["kl"]), out["lse"].data_ptr()
+    d.seq_offsets, d.n_seq = seq_offsets.data_ptr(), n_seq
+    keep = [row_index, seq_offsets]
+    if fast is not None:
+        el = _opt(fast.get("eligible"), "eligible", torch.uint8, dev)
+        out["fast"] = (torch.empty(n, **u8), torch.empty(max(n_seq, 0), **i32))
+        d.fast_eligible, d.fast_tau = _ptr(el), float(fast.get("tau", DEFAULTS["fastdllm_tau"]))
+        d.fast_commit, d.fast_n_commit = out["fast"][0].data_ptr(), out["fast"][1].data_ptr()
+        keep.append(el)
+    if depcap is not None:
+        hp = _opt(depcap.get("has_prev"), "has_prev", torch.uint8, dev)
+        out["depcap"] = (torch.empty(max(n_seq, 0), **i32), torch.empty(n, **f))
+        d.depcap_has_prev = _ptr(hp)
+        d.depcap_lambda = float(depcap.get("lam", DEFAULTS["depcap_lambda"]))
+        d.depcap_l_min = int(depcap.get("l_min", DEFAULTS["depcap_l_min"]))
+        d.depcap_l_max = int(depcap.get("l_max", DEFAULTS["depcap_l_max"]))
+        d.depcap_radius = int(depcap.get("radius", DEFAULTS["depcap_radius"]))
+        d.depcap_eps = float(depcap.get("eps", DEFAULTS["depcap_eps"]))
+        d.depcap_block_len, d.depcap_score = (out["depcap"][0].data_ptr(),
+                                              out["depcap"][1].data_ptr())
+        keep.append(hp)
+    if cap is not None:
+        el = _opt(cap.get("eligible"), "eligible", torch.uint8, dev)
+        out["cap"] = (torch.empty(n, **u8), torch.empty(max(n_seq, 0), **i32))
+        d.cap_eligible = _ptr(el)
+        d.cap_tau_low = float(cap.get("tau_low", DEFAULTS["cap_tau_low"]))
+        d.cap_tau_high = float(cap.get("tau_high", DEFAULTS["cap_tau_high"]))
+        d.cap_gamma = float(cap.get("gamma", DEFAULTS["cap_gamma"]))
+        d.cap_k_max = int(cap.get("k_max", 64))
+        d.cap_commit, d.cap_n_commit = out["cap"][0].data_ptr(), out["cap"][1].data_ptr()
+        keep.append(el)
+    if dapd is not None:
+        attn = dapd["attn"]
+        _dev(attn, "attn")
+        if attn.dim() != 4 or not attn.is_contiguous() or attn.shape[2] != attn.shape[3]:
+            raise DLMError("attn must be a contiguous [B, n_lh, S, S] tensor")
+        if n_seq > attn.shape[0]:
+            raise DLMError("more sequences than attention batches")
+        pos = _vec(dapd["masked_pos"], "masked_pos", torch.int32, dev)
+        m_max = int(dapd["m_max"])
+        ws = dapd.get("workspace")
+        if ws is None:
+            ws = torch.empty(max(dapd_workspace_bytes(n_seq, m_max), 1), **u8)
+        _vec(ws, "workspace", torch.uint8, dev)
+        B, n_lh, S, _ = attn.shape
+        out["dapd"] = (torch.empty(n, **u8), torch.empty(max(n_seq, 0), **i32))
+        d.attn, d.attn_dtype, d.n_lh, d.S = attn.data_ptr(), _dtype_code(attn), n_lh, S
+        d.batch_stride, d.masked_pos, d.m_max = n_lh * S * S, pos.data_ptr(), m_max
+        d.dapd_tau = float(dapd.get("tau", 0.01))
+        d.dapd_commit, d.dapd_n_commit = out["dapd"][0].data_ptr(), out["dapd"][1].data_ptr()
+        d.dapd_workspace, d.dapd_workspace_bytes = ws.data_ptr(), ws.numel()
+        keep += [attn, pos, ws]
+    st = _lib.lib().dlm_decide_step(ctypes.byref(d), _stream(logits))
+    _lib.check(st, "dlm_decide_step")
+    return out

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "libdlm.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["stats.hip", "rules.hip", "cap.hip", "dapd.hip", "schedules.hip"]
+SOURCES = ["stats.hip", "rules.hip", "cap.hip", "dapd.hip", "schedules.hip", "fused.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1,457 +1,35 @@
-// dapd.hip — dlm_dapd_select: DAPD dependency graph and Welsh-Powell-ordered
-// independent set (DAPD paper note: overall framework; key design 1
-// (s_ij = (a_ij + a_ji)/2, edge iff s_ij > tau); key design 2 (proxy degree,
-// order by degree x confidence, maximal independent set)).
-//
-// Three kernels:
-//  k_dapd_avg    grid-wide, HBM-bound.  Streams only the masked x masked
-//                sub-blocks of the n_lh attention maps (fp32 accumulation) and
-//                writes a to the workspace.  A workgroup owns 32 (row, 8-column
-//                chunk) items = one row x 256 columns, so each wave reads whole
-//                512-byte row segments of two maps; its 1024 lanes are 32 map
-//                groups x 32 items, so a single sequence already fills every CU.
-//                A lane keeps 4 maps in flight (more only queues up behind the
-//                memory system).  Map groups are summed in LDS in a fixed order.
-//  k_dapd_sym    grid-wide: s = (a + aT)/2 for 16 rows per workgroup, one
-//                16-lane team per row, lane l taking columns l, l+16, ...; the
-//                transposed half a[j][i] is read from a itself (the four teams
-//                of a wave share its cache lines), so no transposed copy is
-//                written; each step's 16 edge bits are one ballot slice; fp64
-//                proxy degree and the ordering key.
-//  k_dapd_select one workgroup (1024 threads) per sequence:
-//                1. the adjacency bitset and keys into LDS;
-//                2. rank sort of the 64-bit keys (key desc, position asc);
-//                3. greedy over blocks of 64 nodes in that order: a node is
-//                   blocked by an earlier block's chosen node (bitset AND) or by
-//                   an earlier node of its own block (ballots), which gives the
-//                   same set as the one-node-at-a-time scan.
-//
-// dlm_dapd_step adds the full step policy (DAPD note, key design 3): a
-// sequence whose masked rows fell below late_frac of its generation length
-// skips the graph (no attention read, no adjacency) and commits conf >
-// late_tau with a top-1 fallback; rows with conf exactly 1.0 may be
-// committed in either stage (pre-unmask).  Every kernel evaluates the same
-// stage test, in fp64: M < late_frac * gen_len.
-#include <math.h>
-
-#include "dlm_device.h"
+// dapd.hip — dlm_dapd_select and dlm_dapd_step: the three kernels (device
+// code and design notes in dapd_impl.h), the workspace size and the host
+// entry points.
+#include "checks.h"
+#include "dapd_impl.h"
 
 namespace {
 
-#ifndef DLM_DAPD_GROUPS
-#define DLM_DAPD_GROUPS 32
-#endif
-#ifndef DLM_DAPD_UNR_BF16
-#define DLM_DAPD_UNR_BF16 4
-#endif
-constexpr int kGroups = DLM_DAPD_GROUPS;  // map groups per workgroup
-constexpr int kItems = 32;           // (row, chunk) items per workgroup
-constexpr int kAvgNT = kGroups * kItems;
-constexpr int kTileRows = 1;
-constexpr int kTileChunks = kItems / kTileRows;  // 32 chunks of 8 columns = 256 columns
-constexpr int kSelNT = 1024;
-constexpr int kMaxM = DLM_MAX_SEQ_ROWS;
-constexpr int kWords = kMaxM / 64;
-
-// Row stride (floats) of the workspace matrices: 16-float aligned rows.
-__host__ __device__ inline int ws_ld(int m_max) { return (m_max + 15) & ~15; }
-
-// The full-step policy; gen_len == nullptr and pre_unmask == 0 give the plain
-// DAPD selection.
-struct Policy {
-  const int32_t* gen_len;  // [n_seq] generation length per sequence, or null
-  float late_frac, late_tau;
-  int pre_unmask;
-  uint8_t* stage;          // [n_seq] 1 = late stage, or null
-};
-__device__ __forceinline__ bool late_stage(const Policy& P, int b, int M) {
-  return P.gen_len != nullptr &&
-         static_cast<double>(M) < static_cast<double>(P.late_frac) * static_cast<double>(P.gen_len[b]);
-}
-
 template <bool BF16>
-__device__ __forceinline__ float ld1(const void* base, int64_t idx) {
-  if constexpr (BF16) return dlm::bf16_at(static_cast<const uint16_t*>(base), idx);
-  return static_cast<const float*>(base)[idx];
+__global__ __launch_bounds__(kAvgNT) void k_dapd_avg(
+    const void* __restrict__ attn, int n_lh, int64_t S, int64_t batch_stride,
+    const int32_t* __restrict__ masked_pos, const int32_t* __restrict__ seq_offsets, int m_max,
+    int n_tc, int vec_ok, float* __restrict__ ws_a, Policy P) {
+  dapd_avg_tile<BF16>(blockIdx.y, blockIdx.x, attn, n_lh, S, batch_stride, masked_pos,
+                      seq_offsets, m_max, n_tc, vec_ok, ws_a, P);
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kAvgNT) void k_dapd_avg(const void* __restrict__ attn, int n_lh,
-                                                     int64_t S, int64_t batch_stride,
-                                                     const int32_t* __restrict__ masked_pos,
-                                                     const int32_t* __restrict__ seq_offsets,
-                                                     int m_max, int n_tc, int vec_ok,
-                                                     float* __restrict__ ws_a, Policy P) {
-  __shared__ float red[kGroups][kItems][9];
-  const int b = blockIdx.y;
-  const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
-  if (M > m_max || M <= 0 || late_stage(P, b, M)) return;  // late stage: no graph
-  const int ti = blockIdx.x / n_tc, tc = blockIdx.x % n_tc;
-  const int i0 = ti * kTileRows, c0 = tc * kTileChunks;
-  if (i0 >= M || c0 * 8 >= M) return;  // whole workgroup idle (uniform)
-  const int g = threadIdx.x / kItems, it = threadIdx.x % kItems;
-  const int i = i0 + it / kTileChunks, c = c0 + it % kTileChunks;
-  const int j0 = c * 8;
-  const int* pos = masked_pos + lo;
-  // positions outside [0, S) are never dereferenced (k_dapd_select reports
-  // the sequence)
-  const bool item_ok = i < M && j0 < M && pos[i] >= 0 && pos[i] < S;
-
-  float acc[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-
-  if (item_ok) {
-    const int64_t prow = static_cast<int64_t>(pos[i]) * S;
-    int pj[8];
-    bool contig = vec_ok && (j0 + 8 <= M);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      pj[k] = (j0 + k < M) ? pos[j0 + k] : -1;
-      if (pj[k] >= S) pj[k] = -1;
-      contig = contig && (pj[k] >= 0) && (pj[k] == pj[0] + k);
-    }
-    contig = contig && (pj[0] % (BF16 ? 8 : 4) == 0);
-    const char* base = static_cast<const char*>(attn) +
-                       static_cast<int64_t>(b) * batch_stride * (BF16 ? 2 : 4);
-    const int64_t map_stride = S * S;
-    if (contig) {
-      // UNR maps per lane in flight, then summed in map order
-      constexpr int UNR = BF16 ? DLM_DAPD_UNR_BF16 : 2;
-      for (int lh0 = g; lh0 < n_lh; lh0 += kGroups * UNR) {
-        uint4 q[UNR][BF16 ? 1 : 2];
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-          const int lh = lh0 + kGroups * u;
-          const int64_t e = static_cast<int64_t>(lh) * map_stride + prow + pj[0];
-          if constexpr (BF16) {
-            q[u][0] = lh < n_lh ? *reinterpret_cast<const uint4*>(base + e * 2)
-                                : make_uint4(0u, 0u, 0u, 0u);
-          } else {
-            q[u][0] = lh < n_lh ? *reinterpret_cast<const uint4*>(base + e * 4)
-                                : make_uint4(0u, 0u, 0u, 0u);
-            q[u][1] = lh < n_lh ? *reinterpret_cast<const uint4*>(base + e * 4 + 16)
-                                : make_uint4(0u, 0u, 0u, 0u);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-          if (lh0 + kGroups * u >= n_lh) break;
-          if constexpr (BF16) {
-            acc[0] += dlm::bf16_lo(q[u][0].x);
-            acc[1] += dlm::bf16_hi(q[u][0].x);
-            acc[2] += dlm::bf16_lo(q[u][0].y);
-            acc[3] += dlm::bf16_hi(q[u][0].y);
-            acc[4] += dlm::bf16_lo(q[u][0].z);
-            acc[5] += dlm::bf16_hi(q[u][0].z);
-            acc[6] += dlm::bf16_lo(q[u][0].w);
-            acc[7] += dlm::bf16_hi(q[u][0].w);
-          } else {
-            acc[0] += __uint_as_float(q[u][0].x);
-            acc[1] += __uint_as_float(q[u][0].y);
-            acc[2] += __uint_as_float(q[u][0].z);
-            acc[3] += __uint_as_float(q[u][0].w);
-            acc[4] += __uint_as_float(q[u][1].x);
-            acc[5] += __uint_as_float(q[u][1].y);
-            acc[6] += __uint_as_float(q[u][1].z);
-            acc[7] += __uint_as_float(q[u][1].w);
-          }
-        }
-      }
-    } else {
-      for (int lh = g; lh < n_lh; lh += kGroups) {
-        const int64_t e = static_cast<int64_t>(lh) * map_stride + prow;
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (pj[k] >= 0) acc[k] += ld1<BF16>(base, e + pj[k]);
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) red[g][it][k] = acc[k];
-  __syncthreads();
-  // 32 items x 8 columns = 256 outputs; thread t < 256 finishes one
-  if (threadIdx.x < kItems * 8) {
-    const int oi = threadIdx.x / 8, k = threadIdx.x % 8;
-    const int ri = i0 + oi / kTileChunks, rj = (c0 + oi % kTileChunks) * 8 + k;
-    if (ri < M && rj < M) {
-      float s = red[0][oi][k];
-#pragma unroll
-      for (int q = 1; q < kGroups; ++q) s += red[q][oi][k];  // fixed order
-      const float a = s / static_cast<float>(n_lh);
-      const int ld = ws_ld(m_max);
-      ws_a[(static_cast<int64_t>(b) * m_max + ri) * ld + rj] = a;
-    }
-  }
-}
-
-// Workspace layout (every region 256-byte aligned), for n_seq x m_max:
-//   a          f32 [n_seq][m_max][ws_ld]     averaged maps
-//   adj        u64 [n_seq][m_max][words]     adjacency bitsets, words = ceil(m_max/64)
-//   keys       u64 [n_seq][m_max]            (order key, position)
-//   has_edge   u8  [n_seq][m_max]
-struct Layout {
-  size_t a, adj, keys, has_edge, total;
-  int ld, words;
-};
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-__host__ __device__ inline Layout layout(int n_seq, int m_max) {
-  Layout L;
-  L.ld = ws_ld(m_max);
-  L.words = (m_max + 63) / 64;
-  const size_t nm = static_cast<size_t>(n_seq) * m_max;
-  L.a = 0;
-  L.adj = align256(nm * L.ld * sizeof(float));
-  L.keys = L.adj + align256(nm * L.words * sizeof(uint64_t));
-  L.has_edge = L.keys + align256(nm * sizeof(uint64_t));
-  L.total = L.has_edge + align256(nm);
-  return L;
-}
-
-#ifndef DLM_DAPD_SYM_ROWS
-#define DLM_DAPD_SYM_ROWS 4
-#endif
-constexpr int kSymRows = DLM_DAPD_SYM_ROWS;  // rows per k_dapd_sym workgroup (16 lanes each)
-constexpr int kSymNT = kSymRows * 16;
-
-// s = (a + aT)/2 for 16 rows per workgroup: adjacency bits (ballot slices),
-// fp64 proxy degree (fixed-pattern 16-lane reduction), ordering key.
 __global__ __launch_bounds__(kSymNT) void k_dapd_sym(
     const int32_t* __restrict__ seq_offsets, int m_max, const float* __restrict__ conf,
     float tau, const char* __restrict__ ws, Layout L, float* __restrict__ degree,
     float* __restrict__ sym, float* __restrict__ key_out, Policy P) {
-  const int b = blockIdx.y;
-  const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
-  const int team = threadIdx.x / 16, tl = threadIdx.x % 16;
-  const int i = blockIdx.x * kSymRows + team;
-  const int64_t sbase = static_cast<int64_t>(b) * m_max * m_max;
-  if (M > m_max || M < 0 || i >= m_max) return;  // over-long sequences: k_dapd_select reports
-  if (i >= M || late_stage(P, b, M)) {  // pad rows, or no graph: NaN in the optional outputs
-    if (i < M && tl == 0) {
-      if (degree) degree[lo + i] = NAN;
-      if (key_out) key_out[lo + i] = NAN;
-    }
-    if (sym)
-      for (int j = tl; j < m_max; j += 16) sym[sbase + static_cast<int64_t>(i) * m_max + j] = NAN;
-    return;
-  }
-  const float* A = reinterpret_cast<const float*>(ws + L.a) + static_cast<int64_t>(b) * m_max * L.ld;
-  const float* ar = A + static_cast<int64_t>(i) * L.ld;
-  uint16_t* adj16 = reinterpret_cast<uint16_t*>(
-      const_cast<char*>(ws) + L.adj + (static_cast<int64_t>(b) * m_max + i) * L.words * 8);
-  const int nw = (M + 63) / 64;
-  float* so = sym ? sym + sbase + static_cast<int64_t>(i) * m_max : nullptr;
-  const int shift = 16 * (team % (DLM_WAVE / 16));  // this team's lanes in a ballot
-  double dsum = 0.0;
-  bool any = false;
-  for (int c0 = 0; c0 < 64 * nw; c0 += 256) {
-    // step e covers columns c0 + 16e .. c0 + 16e + 15, column c0 + 16e + tl
-    // on this lane; lane e keeps step e's 16 edge bits.  a[j][i] (the
-    // transposed half) is read straight from a: the four teams of a wave read
-    // neighbouring columns of the same rows, so a wave load touches 16 lines.
-    float va[16], vt[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = c0 + 16 * e + tl;
-      va[e] = vt[e] = 0.f;
-      if (j < M) {
-        va[e] = ar[j];
-        vt[e] = A[static_cast<int64_t>(j) * L.ld + i];
-      }
-    }
-    uint32_t mine = 0u;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = c0 + 16 * e + tl;
-      float sv = NAN;
-      bool edge = false;
-      if (j < M) {
-        sv = 0.5f * (va[e] + vt[e]);
-        if (j != i) {
-          dsum += static_cast<double>(sv);
-          edge = sv > tau;
-        }
-      }
-      if (so && j < m_max) so[j] = sv;
-      const uint32_t slice = static_cast<uint32_t>(__ballot(edge) >> shift) & 0xffffu;
-      if (e == tl) mine = slice;
-    }
-    if (c0 + 16 * tl < 64 * nw) adj16[c0 / 16 + tl] = static_cast<uint16_t>(mine);  // zero past M
-    any = any || mine != 0u;
-  }
-  if (so)
-    for (int j = 64 * nw + tl; j < m_max; j += 16) so[j] = NAN;
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) dsum += __shfl_xor(dsum, o, 16);  // fixed pattern
-  uint32_t anyb = any ? 1u : 0u;
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) anyb |= __shfl_xor(anyb, o, 16);
-  if (tl == 0) {
-    const float df = static_cast<float>(dsum);
-    const float kk = df * conf[lo + i];
-    if (degree) degree[lo + i] = df;
-    if (key_out) key_out[lo + i] = kk;
-    const uint64_t hi = (kk != kk) ? 0xffffffffull : static_cast<uint64_t>(dlm::desc_bits(kk));
-    // NaN keys sort last; every other key maps below 0xffffffff
-    reinterpret_cast<uint64_t*>(const_cast<char*>(ws) + L.keys)[static_cast<int64_t>(b) * m_max + i] =
-        (hi << 32) | static_cast<uint32_t>(i);
-    reinterpret_cast<uint8_t*>(const_cast<char*>(ws) + L.has_edge)[static_cast<int64_t>(b) * m_max + i] =
-        static_cast<uint8_t>(anyb);
-  }
+  dapd_sym_rows(blockIdx.y, blockIdx.x, seq_offsets, m_max, conf, tau, ws, L, degree, sym,
+                key_out, P);
 }
 
-// Per sequence: load the graph into LDS, order the nodes, run the greedy.
 __global__ __launch_bounds__(kSelNT) void k_dapd_select(
-    const int32_t* __restrict__ masked_pos, int64_t S,
-    const int32_t* __restrict__ seq_offsets, int m_max, const char* __restrict__ ws, Layout L,
-    const float* __restrict__ conf, uint8_t* __restrict__ commit, int32_t* __restrict__ n_commit,
-    float* __restrict__ degree, float* __restrict__ sym, float* __restrict__ key_out, Policy P) {
-  __shared__ uint64_t adj[kMaxM][kWords];  // 128 KiB; row i = neighbours of node i
-  __shared__ uint64_t keys[kMaxM];
-  __shared__ int16_t order[kMaxM];
-  __shared__ uint64_t chosen[kWords];
-  __shared__ uint8_t has_edge[kMaxM];
-  __shared__ int shi[kSelNT / DLM_WAVE];
-  __shared__ float shf[kSelNT / DLM_WAVE];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int wv = tid / DLM_WAVE, ln = tid % DLM_WAVE;
-  const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
-  const int64_t sbase = static_cast<int64_t>(b) * m_max * m_max;
-
-  int bad_pos = 0;  // a masked position outside [0, S): the sequence is reported
-  for (int r = tid; r < M && M <= m_max; r += kSelNT) {
-    const int p = masked_pos[lo + r];
-    bad_pos |= p < 0 || p >= S;
-  }
-  bad_pos = dlm::block_max_i<kSelNT>(bad_pos, shi);
-  if (M > m_max || M < 0 || bad_pos) {
-    for (int r = tid; r < M; r += kSelNT) {
-      commit[lo + r] = 0;
-      if (degree) degree[lo + r] = NAN;
-      if (key_out) key_out[lo + r] = NAN;
-    }
-    if (sym)
-      for (int64_t e = tid; e < static_cast<int64_t>(m_max) * m_max; e += kSelNT)
-        sym[sbase + e] = NAN;
-    if (tid == 0) {
-      n_commit[b] = -1;
-      if (P.stage) P.stage[b] = 0;
-    }
-    return;
-  }
-  const bool late = late_stage(P, b, M);  // uniform over the workgroup
-  if (tid == 0 && P.stage) P.stage[b] = static_cast<uint8_t>(late);
-  if (late) {  // no graph: conf > late_tau, else the most confident row
-    int above = 0, bi = INT32_MAX;
-    float bv = -INFINITY;
-    for (int r = tid; r < M; r += kSelNT) {
-      const float cf = conf[lo + r];
-      above += cf > P.late_tau;
-      if (cf == cf && (bi == INT32_MAX || cf > bv)) {
-        bv = cf;
-        bi = r;
-      }
-    }
-    above = dlm::block_sum<kSelNT>(above, shi);
-    const int fb = above == 0 ? dlm::block_argmax<kSelNT>(bv, bi, shf, shi) : INT32_MAX;
-    int cnt = 0;
-    for (int r = tid; r < M; r += kSelNT) {
-      const float cf = conf[lo + r];
-      const int c = (cf > P.late_tau) || r == fb || (P.pre_unmask && cf == 1.0f);
-      commit[lo + r] = static_cast<uint8_t>(c);
-      cnt += c;
-    }
-    cnt = dlm::block_sum<kSelNT>(cnt, shi);
-    if (tid == 0) n_commit[b] = cnt;
-    return;
-  }
-  const int nw = (M + 63) / 64;  // adjacency words in use
-  const uint64_t* gadj = reinterpret_cast<const uint64_t*>(ws + L.adj) +
-                         static_cast<int64_t>(b) * m_max * L.words;
-  for (int e = tid; e < M * nw; e += kSelNT) {
-    const int i = e / nw, w = e - i * nw;
-    adj[i][w] = gadj[static_cast<int64_t>(i) * L.words + w];
-  }
-  const uint64_t* gkeys = reinterpret_cast<const uint64_t*>(ws + L.keys) +
-                          static_cast<int64_t>(b) * m_max;
-  const uint8_t* gedge = reinterpret_cast<const uint8_t*>(ws + L.has_edge) +
-                         static_cast<int64_t>(b) * m_max;
-  for (int e = tid; e < M; e += kSelNT) {
-    keys[e] = gkeys[e];
-    has_edge[e] = gedge[e];
-  }
-  if (tid < kWords) chosen[tid] = 0ull;
-  __syncthreads();
-
-  // ---- rank sort, 4 threads per key (keys are unique: they carry the position)
-  for (int i0 = 0; i0 < M; i0 += kSelNT / 4) {
-    const int i = i0 + tid / 4, part = tid % 4;
-    int rank = 0;
-    if (i < M) {
-      const uint64_t k = keys[i];
-      const int j0 = part * ((M + 3) / 4), j1 = min(M, j0 + (M + 3) / 4);
-#pragma unroll 8
-      for (int j = j0; j < j1; ++j) rank += keys[j] < k;
-    }
-    rank += __shfl_xor(rank, 1, 4);
-    rank += __shfl_xor(rank, 2, 4);
-    if (i < M && part == 0) order[rank] = static_cast<int16_t>(i);
-  }
-  __syncthreads();
-
-  // ---- greedy on wave 0, 64 nodes of the order at a time
-  if (wv == 0) {
-    for (int base = 0; base < M; base += 64) {
-      const int t = base + ln;
-      int v = -1;
-      if (t < M) {
-        const int cand = order[t];
-        if ((keys[cand] >> 32) != 0xffffffffull) v = cand;  // NaN keys never chosen
-      }
-      uint64_t sel;
-      if (__ballot(v >= 0 && has_edge[v]) == 0ull) {
-        sel = __ballot(v >= 0);  // no node of this block has an edge: all chosen
-      } else {
-        // blocked by a node chosen in an earlier block
-        bool blocked = false;
-        if (v >= 0)
-          for (int w = 0; w < nw; ++w) blocked |= (adj[v][w] & chosen[w]) != 0ull;
-        // conflicts with earlier nodes of this block: bit q set when node q < ln
-        // is adjacent (reads unrolled so that they are in flight together)
-        uint64_t local = 0ull;
-#pragma unroll 16
-        for (int q = 0; q < 64; ++q) {
-          const int vq = __builtin_amdgcn_readlane(v, q);
-          const uint64_t word = (v >= 0 && vq >= 0) ? adj[v][vq >> 6] : 0ull;
-          if (q < ln && vq >= 0) local |= ((word >> (vq & 63)) & 1ull) << q;
-        }
-        uint64_t cand = __ballot(v >= 0 && !blocked);
-        if (__ballot(local != 0ull) == 0ull) {
-          sel = cand;  // no conflicts inside the block
-        } else {
-          sel = 0ull;
-          while (cand) {
-            const int p = __builtin_ctzll(cand);
-            sel |= 1ull << p;
-            cand &= ~(1ull << p);
-            cand &= ~__ballot(((local >> p) & 1ull) != 0ull);  // later nodes adjacent to p
-          }
-        }
-      }
-      if ((sel >> ln) & 1ull)
-        atomicOr(reinterpret_cast<unsigned long long*>(&chosen[v >> 6]), 1ull << (v & 63));
-    }
-  }
-  __syncthreads();
-  int cnt = 0;
-  for (int r = tid; r < M; r += kSelNT) {
-    const int c = static_cast<int>((chosen[r >> 6] >> (r & 63)) & 1ull) |
-                  (P.pre_unmask && conf[lo + r] == 1.0f);  // pre-unmask
-    commit[lo + r] = static_cast<uint8_t>(c);
-    cnt += c;
-  }
-  cnt = dlm::block_sum<kSelNT>(cnt, shi);
-  if (tid == 0) n_commit[b] = cnt;
+    const int32_t* __restrict__ masked_pos, int64_t S, const int32_t* __restrict__ seq_offsets,
+    int m_max, const char* __restrict__ ws, Layout L, const float* __restrict__ conf,
+    uint8_t* __restrict__ commit, int32_t* __restrict__ n_commit, float* __restrict__ degree,
+    float* __restrict__ sym, float* __restrict__ key_out, Policy P) {
+  dapd_select_seq(blockIdx.x, masked_pos, S, seq_offsets, m_max, ws, L, conf, commit, n_commit,
+                  degree, sym, key_out, P);
 }
 
 }  // namespace
@@ -468,19 +46,11 @@ int dapd_run(const void* attn, int dtype, int32_t n_lh, int64_t S, int64_t batch
              const float* conf, float tau, const Policy& P, uint8_t* commit, int32_t* n_commit,
              float* degree, float* sym, float* key, void* workspace, size_t workspace_bytes,
              void* stream) {
-  if (!attn || !masked_pos || !seq_offsets || !conf || !commit || !n_commit || !workspace)
-    return DLM_ERR_ARG;
-  if (n_lh <= 0 || S <= 0 || n_seq <= 0 || m_max <= 0 || tau != tau) return DLM_ERR_ARG;
-  if (P.late_frac != P.late_frac || P.late_tau != P.late_tau) return DLM_ERR_ARG;
-  if (dtype != DLM_BF16 && dtype != DLM_F32) return DLM_ERR_UNSUPPORTED;
-  if (m_max > DLM_MAX_SEQ_ROWS || S > 2147483647LL) return DLM_ERR_UNSUPPORTED;
-  const int64_t maps = static_cast<int64_t>(n_lh) * S * S;
-  if (n_seq > 1 && batch_stride < maps) return DLM_ERR_ARG;
-  const int es = dtype == DLM_BF16 ? 2 : 4;
+  const int rc = dlmh::check_dapd(attn, dtype, n_lh, S, batch_stride, masked_pos, seq_offsets, n_seq,
+                                  m_max, conf, tau, P.late_frac, P.late_tau, commit, n_commit,
+                                  workspace, workspace_bytes);
+  if (rc != DLM_OK) return rc;
   const uintptr_t ab = reinterpret_cast<uintptr_t>(attn);
-  if (ab % es) return DLM_ERR_ARG;
-  if (reinterpret_cast<uintptr_t>(workspace) % 16) return DLM_ERR_ARG;
-  if (workspace_bytes < dlm_dapd_workspace_bytes(n_seq, m_max)) return DLM_ERR_ARG;
   const int vec_ok = (ab % 16 == 0) && (S % 8 == 0) && (batch_stride % 8 == 0);
   const Layout L = layout(n_seq, m_max);
   char* ws = static_cast<char*>(workspace);

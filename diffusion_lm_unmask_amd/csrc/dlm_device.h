@@ -121,6 +121,29 @@ __device__ void bitonic_sort(uint64_t* keys, int n) {
   }
 }
 
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, DLM_WAVE);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, DLM_WAVE);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Ascending bitonic sort of the first n (a power of two <= 64) lanes' keys
+// of one wave, in registers: lane l ends with the key of rank l.  Lanes >= n
+// must hold keys no smaller than any of the first n (they sort among
+// themselves).  Call with all 64 lanes active.
+__device__ __forceinline__ uint64_t wave_sort_asc(uint64_t v, int n) {
+  const int l = threadIdx.x % DLM_WAVE;
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t o = shfl_xor64(v, j);
+      // the lower lane of a pair keeps the min in an ascending run
+      const bool keep_min = ((l & j) == 0) == ((l & k) == 0);
+      v = keep_min ? (v < o ? v : o) : (v < o ? o : v);
+    }
+  }
+  return v;
+}
+
 // Workgroup reductions. `sh` must hold NT/64 elements; every thread gets the
 // result.  Each call ends with a barrier-protected read, so `sh` may be
 // reused by the next call after it returns (the leading barrier covers it).

@@ -1,0 +1,278 @@
+// fused.hip — dlm_decide_step: the small-batch decision step in three
+// launches, built from the same device code as the individual entry points
+// (stats_impl.h, rules_impl.h, cap_impl.h, dapd_impl.h), so its outputs are
+// bitwise theirs.
+//
+//  launch 1  k_step_stream: workgroups [0, n_rows) each stream one row's
+//            statistics; the rest average one DAPD attention tile.  Both are
+//            HBM streams with the same 512-thread workgroup, so one grid
+//            keeps the memory system busy through each other's ramp-up and
+//            tail instead of paying two.
+//  launch 2  k_step_rules: Fast-dLLM, DepCap and CAP one workgroup per
+//            sequence each, and the DAPD scores four rows per workgroup
+//            (its first wave), side by side.
+//  launch 3  k_step_select: the DAPD greedy, one workgroup per sequence.
+//
+// No part waits for another inside a launch: the dependencies (statistics
+// before the rules, scores before the greedy) are the launch boundaries.
+#include "cap_impl.h"
+#include "checks.h"
+#include "dapd_impl.h"
+#include "rules_impl.h"
+#include "stats_impl.h"
+
+namespace {
+
+constexpr int kStepNT = 512;
+static_assert(kAvgNT == kStepNT, "an attention tile must use the statistics workgroup size");
+static_assert(kRuleNT == 256 && kCapNT == 256 && kSymNT <= 256, "rules run with 256 threads");
+constexpr int kRulesNT = 256;
+
+struct StreamArgs {
+  StatsArgs st;
+  int64_t n_rows;
+  const void* attn;
+  int n_lh, m_max, n_tc, vec_ok, tiles_per_seq;
+  int64_t S, batch_stride;
+  const int32_t* masked_pos;
+  const int32_t* seq_offsets;
+  float* ws_a;
+  Policy P;
+};
+
+template <bool BF16, bool PREV, bool ABF16>
+__global__ __launch_bounds__(kStepNT) void k_step_stream(const StreamArgs a) {
+  const int64_t g = blockIdx.x;
+  if (g < a.n_rows) {
+    stats_block<kStepNT, BF16, PREV>(a.st, g, 0);
+    return;
+  }
+  const int64_t t = g - a.n_rows;
+  dapd_avg_tile<ABF16>(static_cast<int>(t / a.tiles_per_seq), static_cast<int>(t % a.tiles_per_seq),
+                       a.attn, a.n_lh, a.S, a.batch_stride, a.masked_pos, a.seq_offsets, a.m_max,
+                       a.n_tc, a.vec_ok, a.ws_a, a.P);
+}
+
+struct RulesArgs {
+  const int32_t* seq_offsets;
+  const float *conf, *ent, *kl, *lse;
+  const int32_t* argmax;
+  int nf, nd, nc, ns;  // workgroups of each part (0 = off)
+  // Fast-dLLM
+  const uint8_t* f_el;
+  float f_tau;
+  uint8_t* f_commit;
+  int32_t* f_n;
+  // DepCap
+  const uint8_t* d_has_prev;
+  double d_lambda, d_eps;
+  int d_lmin, d_lmax, d_radius;
+  int32_t* d_block_len;
+  float* d_score;
+  // CAP
+  const void* logits;
+  int64_t ld, vocab;
+  const int64_t* row_index;
+  const uint8_t* c_el;
+  float c_tau_low, c_tau_high, c_gamma;
+  int c_kmax;
+  uint8_t* c_commit;
+  int32_t* c_n;
+  // DAPD scores
+  int m_max, rb_per_seq;
+  float tau;
+  const char* ws;
+  Layout L;
+  Policy P;
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(kRulesNT) void k_step_rules(const RulesArgs a) {
+  int g = blockIdx.x;
+  if (g < a.nf) {
+    fastdllm_seq(g, a.conf, a.f_el, a.seq_offsets, a.f_tau, a.f_commit, a.f_n);
+    return;
+  }
+  g -= a.nf;
+  if (g < a.nd) {
+    depcap_seq(g, a.kl, a.ent, a.seq_offsets, a.d_has_prev, a.d_lambda, a.d_lmin, a.d_lmax,
+               a.d_radius, a.d_eps, a.d_block_len, a.d_score);
+    return;
+  }
+  g -= a.nd;
+  if (g < a.nc) {
+    cap_seq<BF16>(g, a.logits, a.ld, a.vocab, a.row_index, a.seq_offsets, a.conf, a.argmax,
+                  a.lse, a.c_el, a.c_tau_low, a.c_tau_high, a.c_gamma, a.c_kmax, a.c_commit,
+                  a.c_n, nullptr, nullptr);
+    return;
+  }
+  g -= a.nc;
+  if (threadIdx.x >= kSymNT) return;  // the scores use one wave: four 16-lane teams
+  dapd_sym_rows(g / a.rb_per_seq, g % a.rb_per_seq, a.seq_offsets, a.m_max, a.conf, a.tau, a.ws,
+                a.L, nullptr, nullptr, nullptr, a.P);
+}
+
+struct SelectArgs {
+  const int32_t* masked_pos;
+  int64_t S;
+  const int32_t* seq_offsets;
+  int m_max;
+  const char* ws;
+  Layout L;
+  const float* conf;
+  uint8_t* commit;
+  int32_t* n_commit;
+  Policy P;
+};
+
+__global__ __launch_bounds__(kSelNT) void k_step_select(const SelectArgs a) {
+  dapd_select_seq(blockIdx.x, a.masked_pos, a.S, a.seq_offsets, a.m_max, a.ws, a.L, a.conf,
+                  a.commit, a.n_commit, nullptr, nullptr, nullptr, a.P);
+}
+
+template <bool BF16, bool PREV>
+void launch_stream(bool abf16, dim3 grid, hipStream_t s, const StreamArgs& a) {
+  if (abf16)
+    hipLaunchKernelGGL((k_step_stream<BF16, PREV, true>), grid, dim3(kStepNT), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_step_stream<BF16, PREV, false>), grid, dim3(kStepNT), 0, s, a);
+}
+
+}  // namespace
+
+extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
+  if (!d) return DLM_ERR_ARG;
+  int rc = dlmh::check_stats(d->logits, d->prev_logits, d->dtype, d->vocab, d->ld, d->row_index,
+                             d->n_rows, d->conf, d->argmax, d->entropy, d->kl, d->lse);
+  if (rc != DLM_OK) return rc;
+  const bool fast = d->fast_commit != nullptr, dep = d->depcap_block_len != nullptr;
+  const bool cap = d->cap_commit != nullptr, dapd = d->dapd_commit != nullptr;
+  if ((fast || dep || cap || dapd) && (!d->seq_offsets || d->n_seq <= 0)) return DLM_ERR_ARG;
+  if (fast &&
+      (rc = dlmh::check_fastdllm(d->conf, d->seq_offsets, d->n_seq, d->fast_tau, d->fast_commit,
+                                 d->fast_n_commit)) != DLM_OK)
+    return rc;
+  if (dep && (rc = dlmh::check_depcap(d->kl, d->entropy, d->seq_offsets, d->n_seq,
+                                      d->depcap_lambda, d->depcap_l_min, d->depcap_l_max,
+                                      d->depcap_radius, d->depcap_eps, d->depcap_block_len)) !=
+                 DLM_OK)
+    return rc;
+  if (cap && (rc = dlmh::check_cap(d->logits, d->dtype, d->vocab, d->ld, d->row_index,
+                                   d->seq_offsets, d->n_seq, d->conf, d->argmax, d->lse,
+                                   d->cap_tau_low, d->cap_tau_high, d->cap_gamma, d->cap_k_max,
+                                   d->cap_commit, d->cap_n_commit)) != DLM_OK)
+    return rc;
+  if (dapd && (rc = dlmh::check_dapd(d->attn, d->attn_dtype, d->n_lh, d->S, d->batch_stride,
+                                     d->masked_pos, d->seq_offsets, d->n_seq, d->m_max, d->conf,
+                                     d->dapd_tau, 0.f, 0.f, d->dapd_commit, d->dapd_n_commit,
+                                     d->dapd_workspace, d->dapd_workspace_bytes)) != DLM_OK)
+    return rc;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = d->dtype == DLM_BF16, prev = d->prev_logits != nullptr;
+  const int es = bf16 ? 2 : 4;
+  const uintptr_t la = reinterpret_cast<uintptr_t>(d->logits);
+  const uintptr_t lb = reinterpret_cast<uintptr_t>(d->prev_logits);
+  const int aligned = (la % 16 == 0) && (lb % 16 == 0) && ((d->ld * es) % 16 == 0);
+  const Policy P{nullptr, 0.f, 0.f, 0, nullptr};
+
+  // ---- launch 1: statistics rows, then attention tiles
+  StreamArgs sa{};
+  sa.st = StatsArgs{d->logits, d->prev_logits, d->vocab, d->ld, d->row_index, d->conf, d->entropy,
+                    d->kl, d->lse, d->argmax, aligned, 1, nullptr, nullptr};
+  sa.n_rows = d->n_rows;
+  sa.P = P;
+  int64_t n_tiles = 0;
+  Layout L{};
+  char* ws = nullptr;
+  if (dapd) {
+    L = layout(d->n_seq, d->m_max);
+    ws = static_cast<char*>(d->dapd_workspace);
+    const uintptr_t ab = reinterpret_cast<uintptr_t>(d->attn);
+    sa.attn = d->attn;
+    sa.n_lh = d->n_lh;
+    sa.m_max = d->m_max;
+    sa.n_tc = (d->m_max + 8 * kTileChunks - 1) / (8 * kTileChunks);
+    sa.vec_ok = (ab % 16 == 0) && (d->S % 8 == 0) && (d->batch_stride % 8 == 0);
+    sa.tiles_per_seq = ((d->m_max + kTileRows - 1) / kTileRows) * sa.n_tc;
+    sa.S = d->S;
+    sa.batch_stride = d->batch_stride;
+    sa.masked_pos = d->masked_pos;
+    sa.seq_offsets = d->seq_offsets;
+    sa.ws_a = reinterpret_cast<float*>(ws + L.a);
+    n_tiles = static_cast<int64_t>(sa.tiles_per_seq) * d->n_seq;
+  }
+  const int64_t g1 = d->n_rows + n_tiles;
+  if (g1 > 2147483647LL) return DLM_ERR_UNSUPPORTED;
+  const dim3 grid1(static_cast<unsigned>(g1));
+  const bool abf16 = !dapd || d->attn_dtype == DLM_BF16;
+  if (bf16) {
+    if (prev) launch_stream<true, true>(abf16, grid1, s, sa);
+    else launch_stream<true, false>(abf16, grid1, s, sa);
+  } else {
+    if (prev) launch_stream<false, true>(abf16, grid1, s, sa);
+    else launch_stream<false, false>(abf16, grid1, s, sa);
+  }
+  DLM_CHECK_LAUNCH();
+
+  // ---- launch 2: the per-sequence rules and the DAPD scores
+  RulesArgs ra{};
+  ra.seq_offsets = d->seq_offsets;
+  ra.conf = d->conf;
+  ra.ent = d->entropy;
+  ra.kl = d->kl;
+  ra.lse = d->lse;
+  ra.argmax = d->argmax;
+  ra.nf = fast ? d->n_seq : 0;
+  ra.nd = dep ? d->n_seq : 0;
+  ra.nc = cap ? d->n_seq : 0;
+  ra.rb_per_seq = dapd ? (d->m_max + kSymRows - 1) / kSymRows : 0;
+  ra.ns = dapd ? ra.rb_per_seq * d->n_seq : 0;
+  ra.f_el = d->fast_eligible;
+  ra.f_tau = d->fast_tau;
+  ra.f_commit = d->fast_commit;
+  ra.f_n = d->fast_n_commit;
+  ra.d_has_prev = d->depcap_has_prev;
+  ra.d_lambda = d->depcap_lambda;
+  ra.d_eps = d->depcap_eps;
+  ra.d_lmin = d->depcap_l_min;
+  ra.d_lmax = d->depcap_l_max;
+  ra.d_radius = d->depcap_radius;
+  ra.d_block_len = d->depcap_block_len;
+  ra.d_score = d->depcap_score;
+  ra.logits = d->logits;
+  ra.ld = d->ld;
+  ra.vocab = d->vocab;
+  ra.row_index = d->row_index;
+  ra.c_el = d->cap_eligible;
+  ra.c_tau_low = d->cap_tau_low;
+  ra.c_tau_high = d->cap_tau_high;
+  ra.c_gamma = d->cap_gamma;
+  ra.c_kmax = d->cap_k_max;
+  ra.c_commit = d->cap_commit;
+  ra.c_n = d->cap_n_commit;
+  ra.m_max = d->m_max;
+  ra.tau = d->dapd_tau;
+  ra.ws = ws;
+  ra.L = L;
+  ra.P = P;
+  const int64_t g2 = static_cast<int64_t>(ra.nf) + ra.nd + ra.nc + ra.ns;
+  if (g2 > 0) {
+    if (bf16)
+      hipLaunchKernelGGL(k_step_rules<true>, dim3(static_cast<unsigned>(g2)), dim3(kRulesNT), 0, s,
+                         ra);
+    else
+      hipLaunchKernelGGL(k_step_rules<false>, dim3(static_cast<unsigned>(g2)), dim3(kRulesNT), 0,
+                         s, ra);
+    DLM_CHECK_LAUNCH();
+  }
+
+  // ---- launch 3: the DAPD greedy
+  if (dapd) {
+    const SelectArgs sel{d->masked_pos, d->S, d->seq_offsets, d->m_max, ws, L, d->conf,
+                         d->dapd_commit, d->dapd_n_commit, P};
+    hipLaunchKernelGGL(k_step_select, dim3(d->n_seq), dim3(kSelNT), 0, s, sel);
+    DLM_CHECK_LAUNCH();
+  }
+  return DLM_OK;
+}

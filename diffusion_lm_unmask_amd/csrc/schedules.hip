@@ -32,12 +32,6 @@ constexpr int kBlockNT = 256;
 
 enum Mode { kTopK = 0, kFactor = 1 };
 
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, DLM_WAVE);
-  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, DLM_WAVE);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
 template <int MODE>
 __global__ __launch_bounds__(kRankNT) void k_rank_select(
     const float* __restrict__ conf, const uint8_t* __restrict__ eligible,
@@ -78,15 +72,7 @@ __global__ __launch_bounds__(kRankNT) void k_rank_select(
   __syncthreads();
   if (n2 <= DLM_WAVE) {
     if (tid < DLM_WAVE) {  // one wave, in registers: lane l holds key l
-      uint64_t v = tid < n2 ? keys[tid] : ~0ull;
-      for (int kk = 2; kk <= n2; kk <<= 1) {
-        for (int j = kk >> 1; j > 0; j >>= 1) {
-          const uint64_t o = shfl_xor64(v, j);
-          // the lower lane of a pair keeps the min in an ascending run
-          const bool keep_min = ((tid & j) == 0) == ((tid & kk) == 0);
-          v = keep_min ? (v < o ? v : o) : (v < o ? o : v);
-        }
-      }
+      const uint64_t v = dlm::wave_sort_asc(tid < n2 ? keys[tid] : ~0ull, n2);
       if (tid < n2) keys[tid] = v;
     }
     __syncthreads();

@@ -1,592 +1,14 @@
-// stats.hip — dlm_step_stats: one streaming pass over each logits row (and
-// the previous step's row) computing confidence, argmax, entropy, KL and
-// log-normaliser.
-//
-// Definitions: DepCap summary, Methodology (H_k = H(p_curr^k),
-// I_k = KL(p_curr^k || p_prev^k), c_i = max_v p_i(v)); Fast-dLLM review,
-// Method (max-softmax confidence and argmax commit).
-//
-// Design (gfx950):
-//  * one workgroup per row; each lane owns 16-byte chunks tid, tid+NT, ...
-//    so every wave load is a contiguous 1 KiB (global_load_dwordx4);
-//  * a lane processes U chunks per segment: segment maxima first, then one
-//    exp2 per element, t = x*log2(e) - h, with the lane reference
-//    h = ceil(max*log2(e)) an integer, so a rescale of the running sums when
-//    the max grows is an exact power of two (ldexp) and adds no rounding;
-//  * the previous step's row is summed against the same reference, so KL
-//    needs no second maximum: KL = B/Z + log(Z2/Z);
-//  * sums are fp32 per segment and per lane; lanes are combined exactly
-//    (ldexp) in fp64 relative to the row's integer reference, and the
-//    fractional offset between that reference and the row max is applied
-//    once, in fp64, when the statistics are formed;
-//  * the argmax costs one compare and a register copy per chunk in the hot
-//    loop: a lane keeps the raw bits of the first chunk where its running max
-//    strictly grew, and finds the element in it after the stream, without a
-//    second memory access;
-//  * lanes are merged per wave on the DPP crossbar, waves through one LDS
-//    record each and a single barrier;
-//  * any non-finite total (NaN/inf entries, -inf logits, empty rows) sends
-//    the row to an element-wise path that applies the definitions'
-//    conventions exactly (0 log 0 = 0, q = 0 with p > 0 gives KL = +inf).
-#include "dlm_device.h"
+// stats.hip — dlm_step_stats: the kernel (one workgroup per row or row split;
+// the device code and its design notes are in stats_impl.h) and the host
+// entry points: launch shape, split-row workspace, validation.
+#include "checks.h"
+#include "stats_impl.h"
 
 namespace {
 
-constexpr float kL2E = 1.4426950408889634f;  // log2(e) in fp32
-constexpr double kL2Ed = static_cast<double>(kL2E);  // the same value, widened
-constexpr double kLN2 = 0.6931471805599453;
-constexpr float kLow = -1e30f;  // running-max sentinel: no finite data seen yet
-
-__device__ __forceinline__ float ex2(float t) { return __builtin_amdgcn_exp2f(t); }
-
-// Tuning: 16-byte chunks per lane per segment, and whether row loads carry the
-// non-temporal hint (streamed once, not worth caching).
-#ifndef DLM_STATS_U_BF16
-#define DLM_STATS_U_BF16 2
-#endif
-#ifndef DLM_STATS_NT_LOADS
-#define DLM_STATS_NT_LOADS 1
-#endif
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load16(const uint4* p) {
-#if DLM_STATS_NT_LOADS
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-#else
-  return *p;
-#endif
-}
-
-template <bool BF16>
-__device__ __forceinline__ void unpack(const uint4 q, float* x) {
-  if constexpr (BF16) {
-    x[0] = dlm::bf16_lo(q.x);
-    x[1] = dlm::bf16_hi(q.x);
-    x[2] = dlm::bf16_lo(q.y);
-    x[3] = dlm::bf16_hi(q.y);
-    x[4] = dlm::bf16_lo(q.z);
-    x[5] = dlm::bf16_hi(q.z);
-    x[6] = dlm::bf16_lo(q.w);
-    x[7] = dlm::bf16_hi(q.w);
-  } else {
-    x[0] = __uint_as_float(q.x);
-    x[1] = __uint_as_float(q.y);
-    x[2] = __uint_as_float(q.z);
-    x[3] = __uint_as_float(q.w);
-  }
-}
-
-template <bool BF16>
-__device__ __forceinline__ float load_elem(const char* row, int64_t v) {
-  if constexpr (BF16) return dlm::bf16_at(reinterpret_cast<const uint16_t*>(row), v);
-  return reinterpret_cast<const float*>(row)[v];
-}
-
-// Element k of a 16-byte chunk (k is a compile-time constant after unrolling).
-template <bool BF16>
-__device__ __forceinline__ float elem_of(const uint4 q, int k) {
-  if constexpr (BF16) {
-    const uint32_t w = (k >> 1) == 0 ? q.x : (k >> 1) == 1 ? q.y : (k >> 1) == 2 ? q.z : q.w;
-    return (k & 1) ? dlm::bf16_hi(w) : dlm::bf16_lo(w);
-  } else {
-    return __uint_as_float(k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w);
-  }
-}
-
-// Per-lane running state.  Both rows' sums use the current row's reference
-// h = ceil(m * log2 e) (m = the lane's running max of the current row): the
-// previous row only needs sum 2^(y*log2e - h), and KL = B/Z + log(Z2/Z) then
-// involves no reference at all.  A previous row far above or below the
-// current one overflows or underflows Z2 and is sent to the element-wise path.
-struct LaneState {
-  float m, h;       // running max of the current row, integer reference
-  float Z, A, B;    // sum e, sum e*t (log2 units), sum e*(x - y)
-  float Z2;         // sum 2^(y*log2e - h)
-  int best;         // first element index of the chunk holding the lane max
-  int bestw;        // width of that chunk (VEC, or 1 for a tail element)
-  uint4 bq;         // raw bits of that chunk (VEC > 1)
-};
-
-// Fold NSUB sub-blocks of W values into the lane state.  qc/qp hold the raw
-// chunks (W values each; qc is unused for W == 1); x is the unpacked current
-// row; `valid` masks whole sub-blocks; start[u] is the element index of
-// sub-block u (argmax record).
-template <int NSUB, int W, bool BF16, bool PREV>
-__device__ __forceinline__ void fold(LaneState& c, const float (*x)[W], const uint4* qc,
-                                     const uint4* qp, const float* ys, const bool* valid,
-                                     const int* start) {
-  // segment maxima and the first-strict-increase chunk record
-  float mr = c.m;
-#pragma unroll
-  for (int u = 0; u < NSUB; ++u) {
-    float cm = x[u][0];
-#pragma unroll
-    for (int k = 1; k < W; ++k) cm = fmaxf(cm, x[u][k]);
-    if (valid[u]) {
-      if (cm > mr) {
-        c.best = start[u];
-        c.bestw = W;
-        if constexpr (W > 1) c.bq = qc[u];
-      }
-      mr = fmaxf(mr, cm);
-    }
-  }
-  {  // rescale running sums to the new integer reference (exact: a power of two)
-    const float hn = ceilf(mr * kL2E);
-    const float dh = c.h - hn;  // integer <= 0 (or a huge negative from the sentinel)
-    const int di = static_cast<int>(fmaxf(dh, -256.f));
-    c.A = ldexpf(fmaf(dh, c.Z, c.A), di);
-    c.Z = ldexpf(c.Z, di);
-    if constexpr (PREV) {
-      c.B = ldexpf(c.B, di);
-      c.Z2 = ldexpf(c.Z2, di);
-    }
-    c.h = hn;
-    c.m = mr;
-  }
-  float z = 0.f, a = 0.f, b = 0.f, z2 = 0.f;
-#pragma unroll
-  for (int u = 0; u < NSUB; ++u) {
-    if (!valid[u]) continue;
-#pragma unroll
-    for (int k = 0; k < W; ++k) {
-      const float t = fmaf(x[u][k], kL2E, -c.h);
-      const float e = ex2(t);
-      z += e;
-      a = fmaf(e, t, a);
-      if constexpr (PREV) {
-        const float y = ys ? ys[u * W + k] : elem_of<BF16>(qp[u], k);
-        b = fmaf(e, x[u][k] - y, b);
-        z2 += ex2(fmaf(y, kL2E, -c.h));
-      }
-    }
-  }
-  c.Z += z;
-  c.A += a;
-  if constexpr (PREV) {
-    c.B += b;
-    c.Z2 += z2;
-  }
-}
-
-// Sum four doubles over the workgroup in a fixed order.  Only thread 0
-// receives the totals (the only consumer); its loop over the per-wave
-// partials is kept rolled so the other waves' partials are not all held in
-// registers at once.
-template <int NT>
-__device__ __forceinline__ void block_sum4_to0(double& a, double& b, double& c, double& d,
-                                               double (*sh)[NT / DLM_WAVE]) {
-  constexpr int NW = NT / DLM_WAVE;
-  a = dlm::wave_sum(a);
-  b = dlm::wave_sum(b);
-  c = dlm::wave_sum(c);
-  d = dlm::wave_sum(d);
-  const int w = threadIdx.x / DLM_WAVE, l = threadIdx.x % DLM_WAVE;
-  __syncthreads();
-  if (l == 0) {
-    sh[0][w] = a;
-    sh[1][w] = b;
-    sh[2][w] = c;
-    sh[3][w] = d;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    a = sh[0][0];
-    b = sh[1][0];
-    c = sh[2][0];
-    d = sh[3][0];
-#pragma unroll 1
-    for (int i = 1; i < NW; ++i) {
-      a += sh[0][i];
-      b += sh[1][i];
-      c += sh[2][i];
-      d += sh[3][i];
-    }
-  }
-}
-
-// Partial statistics of one wave, workgroup or split of a row: its max m,
-// the lowest index holding m, and sums relative to its integer reference
-// h = ceil(m * log2 e).
-struct Partial {
-  double Z, A, B, Z2;
-  float m, h;
-  int cand, pad;
-};
-
-template <int NT>
-struct Shared {
-  float f[NT / DLM_WAVE];
-  int i[NT / DLM_WAVE];
-  double d[4][NT / DLM_WAVE];
-  Partial rec[NT / DLM_WAVE];
-  int flag;
-};
-
-// Element-wise path with the definitions' conventions applied term by term.
-template <int NT, bool BF16, bool PREV>
-__device__ void careful_row(const char* cur, const char* prv, int64_t V, Shared<NT>& sh,
-                            int64_t r, float* conf, int32_t* argmax, float* ent, float* kl,
-                            float* lse) {
-  const int tid = threadIdx.x;
-  // pass 1: maxima over non-NaN entries, lowest index, NaN presence
-  float m = -INFINITY, m2 = -INFINITY;
-  int idx = INT32_MAX, nan1 = 0, nan2 = 0;
-  for (int64_t v = tid; v < V; v += NT) {
-    const float x = load_elem<BF16>(cur, v);
-    if (x != x) {
-      nan1 = 1;
-    } else if (idx == INT32_MAX || x > m) {
-      m = x;
-      idx = static_cast<int>(v);
-    }
-    if constexpr (PREV) {
-      const float y = load_elem<BF16>(prv, v);
-      if (y != y) nan2 = 1;
-      else m2 = fmaxf(m2, y);
-    }
-  }
-  const float M = dlm::block_max<NT>(m, sh.f);
-  const int cidx = (idx != INT32_MAX && m == M) ? idx : INT32_MAX;
-  int yhat = dlm::block_min_i<NT>(cidx, sh.i);
-  if (yhat == INT32_MAX) yhat = 0;
-  const int any_nan1 = dlm::block_max_i<NT>(nan1, sh.i);
-  float M2 = 0.f;
-  int any_nan2 = 0;
-  if constexpr (PREV) {
-    M2 = dlm::block_max<NT>(m2, sh.f);
-    any_nan2 = dlm::block_max_i<NT>(nan2, sh.i);
-  }
-  const bool ok1 = !any_nan1 && isfinite(M);
-  const bool ok2 = !any_nan2 && isfinite(M2);
-  if (!ok1) {
-    if (tid == 0) {
-      argmax[r] = yhat;
-      conf[r] = ent[r] = lse[r] = NAN;
-      if constexpr (PREV) kl[r] = NAN;
-    }
-    return;
-  }
-  // pass 2: sums, skipping zero-probability terms
-  float z = 0.f, a = 0.f, b = 0.f, z2 = 0.f;
-  int inf_kl = 0;
-  for (int64_t v = tid; v < V; v += NT) {
-    const float x = load_elem<BF16>(cur, v);
-    float y = 0.f;
-    if constexpr (PREV) {
-      y = load_elem<BF16>(prv, v);
-      if (ok2 && y != -INFINITY) z2 += expf(y - M2);
-    }
-    if (x == -INFINITY) continue;
-    const float d = x - M;
-    const float e = expf(d);
-    z += e;
-    a = fmaf(e, d, a);
-    if constexpr (PREV) {
-      if (y == -INFINITY) inf_kl = 1;
-      else b = fmaf(e, x - y, b);
-    }
-  }
-  double Z = z, A = a, B = b, Z2 = z2;
-  block_sum4_to0<NT>(Z, A, B, Z2, sh.d);
-  if constexpr (PREV) inf_kl = dlm::block_max_i<NT>(inf_kl, sh.i);
-  if (tid == 0) {
-    const double lz = log(Z);
-    argmax[r] = yhat;
-    lse[r] = static_cast<float>(static_cast<double>(M) + lz);
-    conf[r] = static_cast<float>(1.0 / Z);
-    ent[r] = static_cast<float>(lz - A / Z);
-    if constexpr (PREV) {
-      double k;
-      if (!ok2) k = NAN;
-      else if (inf_kl) k = INFINITY;
-      else k = B / Z + (static_cast<double>(M2) - static_cast<double>(M)) + log(Z2) - lz;
-      kl[r] = static_cast<float>(k);
-    }
-  }
-}
-
-struct StatsArgs {
-  const void* logits;
-  const void* prev;
-  int64_t V, ld;
-  const int64_t* row_index;
-  float *conf, *ent, *kl, *lse;
-  int32_t* argmax;
-  int aligned, splits;
-  int* counters;     // [rows], zero between calls
-  Partial* parts;    // [rows][splits]
-};
-
-// Sums taken relative to the integer reference h, moved to the reference
-// hn >= h: an exact power-of-two scaling (terms that fall below the double
-// range, such as those of lanes that saw no finite data, become zero).
-__device__ __forceinline__ void rebase(double& Z, double& A, double& B, double& Z2, float h,
-                                       float hn) {
-  const double d = static_cast<double>(h) - static_cast<double>(hn);  // integer <= 0
-  const int di = static_cast<int>(fmax(d, -1100.0));
-  A = ldexp(fma(d, Z, A), di);
-  Z = ldexp(Z, di);
-  B = ldexp(B, di);
-  Z2 = ldexp(Z2, di);
-}
-
-// Merge n partial records (got in index order 0..n-1, a fixed order) into
-// one: the max, the lowest index among records holding it, and the sums
-// relative to the max's integer reference.
-template <bool PREV, typename Get>
-__device__ __forceinline__ Partial merge(int n, Get get) {
-  Partial t;
-  t.m = kLow;
-  for (int k = 0; k < n; ++k) t.m = fmaxf(t.m, get(k).m);
-  t.h = ceilf(t.m * kL2E);
-  t.cand = INT32_MAX;
-  t.Z = t.A = t.B = t.Z2 = 0.0;
-  for (int k = 0; k < n; ++k) {
-    const Partial q = get(k);
-    double Z = q.Z, A = q.A, B = q.B, Z2 = q.Z2;
-    rebase(Z, A, B, Z2, q.h, t.h);
-    t.Z += Z;
-    t.A += A;
-    if constexpr (PREV) {
-      t.B += B;
-      t.Z2 += Z2;
-    }
-    if (q.m == t.m && q.cand < t.cand) t.cand = q.cand;
-  }
-  return t;
-}
-
-// log2 of a positive finite double: exact exponent plus an fp32 log2 of the
-// mantissa in [0.5, 1) (absolute error about 1e-7).
-__device__ __forceinline__ double log2_split(double v) {
-  int e;
-  const double f = frexp(v, &e);
-  return static_cast<double>(e) + static_cast<double>(log2f(static_cast<float>(f)));
-}
-
-// Turn row totals (relative to the integer reference t.h) into the outputs.
-// Returns false when a total is not finite (or the previous row's mass is out
-// of the reference's range): the caller then runs the element-wise path.
-template <bool PREV>
-__device__ __forceinline__ bool finalize(const StatsArgs& p, int64_t r, const Partial& t) {
-  const float M = t.m;
-  bool ok = isfinite(t.Z) && t.Z > 0.0 && isfinite(t.A) && M > kLow && isfinite(M) &&
-            t.cand >= 0 && t.cand != INT32_MAX;
-  // Z2 below 2^-60 would mean the previous row's mass sits far below the
-  // current row's reference, where fp32 terms lose precision: exact path.
-  if constexpr (PREV) ok = ok && isfinite(t.B) && isfinite(t.Z2) && t.Z2 >= 0x1p-60;
-  if (!ok) return false;
-  // Z_true = Z * 2^cM with cM = h - M*log2e in [0, 1]: conf and lse need it;
-  // entropy does not (it cancels) and KL uses a common reference.
-  const double cM = static_cast<double>(t.h) - static_cast<double>(M) * kL2Ed;
-  const double iz = 1.0 / t.Z;
-  const double l2z = log2_split(t.Z);
-  p.argmax[r] = t.cand;
-  p.lse[r] = static_cast<float>(static_cast<double>(M) + kLN2 * (l2z + cM));
-  p.conf[r] = static_cast<float>(static_cast<double>(exp2f(static_cast<float>(-cM))) * iz);
-  p.ent[r] = static_cast<float>(kLN2 * (l2z - t.A * iz));
-  if constexpr (PREV) p.kl[r] = static_cast<float>(t.B * iz + kLN2 * log2_split(t.Z2 * iz));
-  return true;
-}
-
-template <typename T>
-__device__ __forceinline__ void st_agent(T* a, T v) {
-  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T ld_agent(T* a) {
-  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// One workgroup per (row, split).  With splits == 1 the workgroup owns the
-// whole row.  Otherwise each split streams a contiguous range of the row's
-// chunks and publishes a Partial; the row's last-arriving workgroup (atomic
-// counter) merges the partials in split order — the same order whichever
-// workgroup arrives last — and resets the counter to zero.
 template <int NT, bool BF16, bool PREV>
 __global__ __launch_bounds__(NT) void k_stats(const StatsArgs p) {
-  constexpr int ES = BF16 ? 2 : 4;
-  constexpr int VEC = 16 / ES;          // elements per 16-byte chunk
-  constexpr int U = BF16 ? DLM_STATS_U_BF16 : 4;  // chunks per lane per segment
-  __shared__ Shared<NT> sh;
-
-  const int S = p.splits;
-  const int64_t r = blockIdx.x / S;
-  const int s = static_cast<int>(blockIdx.x % S);
-  const int64_t V = p.V;
-  const int64_t off = p.row_index[r] * p.ld;
-  const char* cur = static_cast<const char*>(p.logits) + off * ES;
-  const char* prv = PREV ? static_cast<const char*>(p.prev) + off * ES : nullptr;
-  const int tid = threadIdx.x;
-
-  if (!p.aligned) {  // the host never splits unaligned rows
-    careful_row<NT, BF16, PREV>(cur, prv, V, sh, r, p.conf, p.argmax, p.ent, p.kl, p.lse);
-    return;
-  }
-
-  const uint4* cur4 = reinterpret_cast<const uint4*>(cur);
-  const uint4* prv4 = reinterpret_cast<const uint4*>(prv);
-  const int64_t nC = V / VEC;
-  const int tail = static_cast<int>(V - nC * VEC);
-  const int64_t c_lo = nC * s / S, c_hi = nC * (s + 1) / S;  // this split's chunks
-  const int64_t n_c = c_hi - c_lo;
-  constexpr int64_t SEG = static_cast<int64_t>(U) * NT;
-  const int64_t n_full = n_c / SEG;
-
-  LaneState c{kLow, kLow * kL2E, 0.f, 0.f, 0.f, 0.f, -1, VEC, make_uint4(0u, 0u, 0u, 0u)};
-  // (the sentinel's h is integral)
-  bool allv[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) allv[u] = true;
-
-  // software-pipelined full segments: the loads of segment it+1 are issued
-  // before segment it is folded
-  uint4 qc[U], qp[U];
-  if (n_full > 0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      qc[u] = load16(cur4 + c_lo + u * NT + tid);
-      if constexpr (PREV) qp[u] = load16(prv4 + c_lo + u * NT + tid);
-    }
-  }
-  for (int64_t it = 0; it < n_full; ++it) {
-    float x[U][VEC];
-    uint4 xq[U], yq[U];
-    int st[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      unpack<BF16>(qc[u], x[u]);
-      xq[u] = qc[u];
-      if constexpr (PREV) yq[u] = qp[u];
-      st[u] = static_cast<int>((c_lo + it * SEG + u * NT + tid) * VEC);
-    }
-    if (it + 1 < n_full) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t ch = c_lo + (it + 1) * SEG + u * NT + tid;
-        qc[u] = load16(cur4 + ch);
-        if constexpr (PREV) qp[u] = load16(prv4 + ch);
-      }
-    }
-    fold<U, VEC, BF16, PREV>(c, x, xq, yq, nullptr, allv, st);
-  }
-  // last, partial segment of this split
-  if (n_full * SEG < n_c) {
-    float x[U][VEC];
-    uint4 xq[U], yq[U];
-    int st[U];
-    bool val[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t ch = c_lo + n_full * SEG + u * NT + tid;
-      val[u] = ch < c_hi;
-      uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
-      if (val[u]) {
-        a = load16(cur4 + ch);
-        if constexpr (PREV) b = load16(prv4 + ch);
-      }
-      unpack<BF16>(a, x[u]);
-      xq[u] = a;
-      yq[u] = b;
-      st[u] = static_cast<int>(ch * VEC);
-    }
-    fold<U, VEC, BF16, PREV>(c, x, xq, yq, nullptr, val, st);
-  }
-  // scalar tail elements (vocab not a multiple of the chunk width): last split
-  if (s == S - 1 && tid < tail) {
-    const int64_t v = nC * VEC + tid;
-    float x[1][1];
-    x[0][0] = load_elem<BF16>(cur, v);
-    const float y = PREV ? load_elem<BF16>(prv, v) : 0.f;
-    const bool val[1] = {true};
-    const int st[1] = {static_cast<int>(v)};
-    fold<1, 1, BF16, PREV>(c, x, nullptr, nullptr, &y, val, st);
-  }
-
-  // ---- this lane's argmax candidate, from the chunk kept in registers
-  int cand = INT32_MAX;
-  if (c.best >= 0) {
-    if (c.bestw == 1) {
-      cand = c.best;
-    } else {
-#pragma unroll
-      for (int k = VEC - 1; k >= 0; --k)
-        if (elem_of<BF16>(c.bq, k) == c.m) cand = c.best + k;
-    }
-  }
-
-  // ---- wave merge (DPP): max, lowest index holding it, and the sums moved
-  // to the wave's integer reference hw = ceil(Mw*log2e)
-  Partial w;
-  w.m = dlm::wave_reduce(c.m, dlm::OpMaxF{});
-  w.cand = dlm::wave_reduce(c.m == w.m ? cand : INT32_MAX, dlm::OpMinI{});
-  w.h = ceilf(w.m * kL2E);
-  {
-    double Z = c.Z, A = c.A, B = c.B, Z2 = c.Z2;
-    rebase(Z, A, B, Z2, c.h, w.h);
-    w.Z = dlm::wave_reduce(Z, dlm::OpAdd{});
-    w.A = dlm::wave_reduce(A, dlm::OpAdd{});
-    if constexpr (PREV) {
-      w.B = dlm::wave_reduce(B, dlm::OpAdd{});
-      w.Z2 = dlm::wave_reduce(Z2, dlm::OpAdd{});
-    } else {
-      w.B = w.Z2 = 0.0;
-    }
-  }
-  // ---- workgroup merge: one record per wave, one barrier, thread 0 merges
-  if (tid % DLM_WAVE == 0) sh.rec[tid / DLM_WAVE] = w;
-  __syncthreads();
-
-  if (S == 1) {
-    if (tid == 0) {
-      const Partial t = merge<PREV>(NT / DLM_WAVE, [&](int k) { return sh.rec[k]; });
-      sh.flag = finalize<PREV>(p, r, t);
-    }
-    __syncthreads();
-    if (!sh.flag)
-      careful_row<NT, BF16, PREV>(cur, prv, V, sh, r, p.conf, p.argmax, p.ent, p.kl, p.lse);
-    return;
-  }
-
-  // ---- publish this split; the last workgroup of the row merges
-  if (tid == 0) {
-    const Partial t = merge<PREV>(NT / DLM_WAVE, [&](int k) { return sh.rec[k]; });
-    Partial* mine = p.parts + r * S + s;
-    st_agent(&mine->Z, t.Z);
-    st_agent(&mine->A, t.A);
-    st_agent(&mine->B, t.B);
-    st_agent(&mine->Z2, t.Z2);
-    st_agent(&mine->m, t.m);
-    st_agent(&mine->h, t.h);
-    st_agent(&mine->cand, t.cand);
-    __threadfence();  // release the partial before counting in
-    const int arrived = atomicAdd(p.counters + r, 1);
-    sh.flag = arrived == S - 1 ? 1 : 0;
-  }
-  __syncthreads();
-  if (!sh.flag) return;  // not the last split of this row (uniform)
-  if (tid == 0) {
-    __threadfence();  // acquire the other splits' partials
-    Partial* row = p.parts + r * S;
-    const Partial t = merge<PREV>(S, [&](int k) {  // split order: deterministic
-      Partial q;
-      q.Z = ld_agent(&row[k].Z);
-      q.A = ld_agent(&row[k].A);
-      q.B = ld_agent(&row[k].B);
-      q.Z2 = ld_agent(&row[k].Z2);
-      q.m = ld_agent(&row[k].m);
-      q.h = ld_agent(&row[k].h);
-      q.cand = ld_agent(&row[k].cand);
-      return q;
-    });
-    st_agent(p.counters + r, 0);  // ready for the next call
-    sh.flag = finalize<PREV>(p, r, t);
-  }
-  __syncthreads();
-  if (!sh.flag)
-    careful_row<NT, BF16, PREV>(cur, prv, V, sh, r, p.conf, p.argmax, p.ent, p.kl, p.lse);
+  stats_block<NT, BF16, PREV>(p, blockIdx.x / p.splits, static_cast<int>(blockIdx.x % p.splits));
 }
 
 template <int NT, bool BF16>
@@ -670,15 +92,12 @@ extern "C" int dlm_step_stats(const void* logits, const void* prev_logits, int d
                               int64_t n_rows, float* conf, int32_t* argmax, float* entropy,
                               float* kl, float* lse, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  if (!logits || !row_index || !conf || !argmax || !entropy || !lse) return DLM_ERR_ARG;
-  if ((prev_logits == nullptr) != (kl == nullptr)) return DLM_ERR_ARG;
-  if (dtype != DLM_BF16 && dtype != DLM_F32) return DLM_ERR_UNSUPPORTED;
-  if (vocab <= 0 || n_rows <= 0 || ld < vocab) return DLM_ERR_ARG;
-  if (vocab > DLM_MAX_VOCAB || n_rows > 2147483647LL) return DLM_ERR_UNSUPPORTED;
+  const int rc = dlmh::check_stats(logits, prev_logits, dtype, vocab, ld, row_index, n_rows, conf,
+                                   argmax, entropy, kl, lse);
+  if (rc != DLM_OK) return rc;
   const int es = dtype == DLM_BF16 ? 2 : 4;
   const uintptr_t a = reinterpret_cast<uintptr_t>(logits);
   const uintptr_t b = reinterpret_cast<uintptr_t>(prev_logits);
-  if (a % es || b % es) return DLM_ERR_ARG;
   if (workspace) {
     if (reinterpret_cast<uintptr_t>(workspace) % 16) return DLM_ERR_ARG;
     if (workspace_bytes < dlm_step_stats_workspace_bytes(n_rows)) return DLM_ERR_ARG;

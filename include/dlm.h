@@ -304,6 +304,73 @@ int dlm_fixed_block_eligible(const int32_t* masked_pos, const int32_t* seq_offse
                              int32_t n_seq, const int32_t* gen_start, int32_t block_len,
                              uint8_t* eligible, void* stream);
 
+/*
+ * dlm_decide_step — the whole small-batch decision step in three launches
+ * (Fast-dLLM review, Limitations: the gains are small-batch; DepCap summary,
+ * Applications: profile the decision for large batches).
+ *   launch 1: the statistics of every row and, when DAPD is on, the
+ *             attention average, side by side in one grid;
+ *   launch 2: Fast-dLLM, the DepCap boundary, CAP and the DAPD scores, each
+ *             part in its own workgroups;
+ *   launch 3: the DAPD selection.
+ * Each part computes exactly what its own entry point computes: the outputs
+ * are bitwise those of dlm_step_stats without a workspace (one workgroup
+ * per row) followed by dlm_fastdllm_select, dlm_depcap_boundary,
+ * dlm_cap_select and dlm_dapd_select on the same arguments.  A part is
+ * skipped when its output pointer below is NULL.  The statistics part is
+ * required.  Rows are the statistics rows in seq_offsets order (the same
+ * CSR for every part, n_rows = seq_offsets[n_seq] by the caller's contract).
+ * Arguments, limits and errors are those of the individual entry points;
+ * the first invalid part makes the call return its error before any launch.
+ */
+typedef struct dlm_step_desc {
+  /* statistics (dlm_step_stats) */
+  const void* logits;
+  const void* prev_logits; /* NULL: no KL */
+  int32_t dtype;
+  int64_t vocab, ld;
+  const int64_t* row_index;
+  int64_t n_rows;
+  float* conf;
+  int32_t* argmax;
+  float* entropy;
+  float* kl; /* NULL iff prev_logits is NULL */
+  float* lse;
+  const int32_t* seq_offsets;
+  int32_t n_seq;
+  /* Fast-dLLM (dlm_fastdllm_select); skipped when fast_commit is NULL */
+  const uint8_t* fast_eligible;
+  float fast_tau;
+  uint8_t* fast_commit;
+  int32_t* fast_n_commit;
+  /* DepGA-Block boundary (dlm_depcap_boundary); skipped when depcap_block_len is NULL */
+  const uint8_t* depcap_has_prev;
+  double depcap_lambda;
+  int32_t depcap_l_min, depcap_l_max, depcap_radius;
+  double depcap_eps;
+  int32_t* depcap_block_len;
+  float* depcap_score;
+  /* CAP (dlm_cap_select); skipped when cap_commit is NULL */
+  const uint8_t* cap_eligible;
+  float cap_tau_low, cap_tau_high, cap_gamma;
+  int32_t cap_k_max;
+  uint8_t* cap_commit;
+  int32_t* cap_n_commit;
+  /* DAPD (dlm_dapd_select); skipped when dapd_commit is NULL */
+  const void* attn;
+  int32_t attn_dtype, n_lh;
+  int64_t S, batch_stride;
+  const int32_t* masked_pos;
+  int32_t m_max;
+  float dapd_tau;
+  uint8_t* dapd_commit;
+  int32_t* dapd_n_commit;
+  void* dapd_workspace;
+  size_t dapd_workspace_bytes;
+} dlm_step_desc;
+
+int dlm_decide_step(const dlm_step_desc* desc, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* dlm_status_string(int status);
 

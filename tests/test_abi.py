@@ -129,6 +129,44 @@ def test_schedule_validation(L):
         assert f(*bad) == code, (i, v)
 
 
+def test_step_desc_layout_matches_the_header(tmp_path):
+    # compile the header with the host C compiler and compare every field's
+    # offset and the struct size with the ctypes mirror used by the binding
+    import os
+    import subprocess
+    fields = [f for f, _ in _lib.StepDesc._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "dlm.h"\nint main(void){\n' +
+                   "".join(f'printf("%zu\\n", offsetof(dlm_step_desc, {f}));\n' for f in fields) +
+                   'printf("%zu\\n", sizeof(dlm_step_desc));\nreturn 0;}\n')
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(_lib.HEADER))
+    subprocess.run(["gcc", "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    want = [getattr(_lib.StepDesc, f).offset for f in fields] + [ctypes.sizeof(_lib.StepDesc)]
+    assert got == want
+
+
+def test_decide_step_validation(L):
+    d = _lib.StepDesc()
+    assert L.dlm_decide_step(None, None) == _lib.ERR_ARG
+    assert L.dlm_decide_step(ctypes.byref(d), None) == _lib.ERR_ARG     # no logits
+    d.logits = d.row_index = d.conf = d.argmax = d.entropy = d.lse = FAKE
+    d.dtype, d.vocab, d.ld, d.n_rows = _lib.BF16, 1000, 1000, 4
+    d.fast_commit, d.fast_n_commit, d.fast_tau = FAKE, FAKE, math.nan
+    d.seq_offsets, d.n_seq = FAKE, 1
+    assert L.dlm_decide_step(ctypes.byref(d), None) == _lib.ERR_ARG     # NaN tau
+    d.fast_tau = 0.9
+    d.depcap_block_len, d.depcap_l_min, d.depcap_l_max = FAKE, 8, 128
+    assert L.dlm_decide_step(ctypes.byref(d), None) == _lib.ERR_ARG     # DepCap without KL
+    d.depcap_block_len = None
+    d.dapd_commit, d.dapd_n_commit = FAKE, FAKE
+    d.attn, d.attn_dtype, d.n_lh, d.S, d.masked_pos, d.m_max = FAKE, _lib.BF16, 4, 96, FAKE, 2000
+    d.dapd_workspace = FAKE
+    assert L.dlm_decide_step(ctypes.byref(d), None) == _lib.ERR_UNSUPPORTED  # m_max > 1024
+
+
 def test_binding_fails_loudly_without_device_tensors():
     torch = pytest.importorskip("torch")
     import diffusion_lm_unmask_amd as d

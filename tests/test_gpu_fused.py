@@ -1,0 +1,128 @@
+"""GPU tests of dlm_decide_step (marked gpu): its outputs must be bitwise those
+of the individual entry points on the same inputs (statistics without a
+workspace, i.e. one workgroup per row), which the other GPU tests compare with
+the oracle; the statistics are also checked against the oracle here."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _parity import assert_close, host
+from diffusion_lm_unmask_amd import api, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _individual(cur, prev, so, ri, fast, depcap, cap, dapd, vocab=None):
+    g = api.step_stats(cur, prev, row_index=ri, vocab=vocab, split=False)
+    out = dict(g)
+    if fast is not None:
+        out["fast"] = api.fastdllm_select(g["conf"], so, fast["tau"], eligible=fast["eligible"])
+    if depcap is not None:
+        out["depcap"] = api.depcap_boundary(g["kl"], g["entropy"], so, lam=depcap["lam"],
+                                            l_min=depcap["l_min"], l_max=depcap["l_max"])
+    if cap is not None:
+        r = api.cap_select(cur, ri, so, g["conf"], g["argmax"], g["lse"],
+                           eligible=cap["eligible"], tau_low=cap["tau_low"],
+                           tau_high=cap["tau_high"], gamma=cap["gamma"], k_max=cap["k_max"],
+                           vocab=vocab)
+        out["cap"] = (r["commit"], r["n_commit"])
+    if dapd is not None:
+        r = api.dapd_select(dapd["attn"], dapd["masked_pos"], so, g["conf"], dapd["tau"],
+                            m_max=dapd["m_max"])
+        out["dapd"] = (r["commit"], r["n_commit"])
+    return out
+
+
+def _same(a, b, name):
+    if a is None or b is None:
+        assert a is None and b is None, name
+        return
+    av = a.view(torch.int32) if a.dtype == torch.float32 else a
+    bv = b.view(torch.int32) if b.dtype == torch.float32 else b
+    assert torch.equal(av, bv), f"{name}: fused differs from the individual call"
+
+
+def _check(cur, prev, so, ri, fast=None, depcap=None, cap=None, dapd=None, tag="", vocab=None):
+    f = api.decide_step(cur, prev, so, row_index=ri, vocab=vocab, fast=fast, depcap=depcap,
+                        cap=cap, dapd=dapd)
+    i = _individual(cur, prev, so, ri, fast, depcap, cap, dapd, vocab)
+    torch.cuda.synchronize()
+    for k in ("conf", "argmax", "entropy", "kl", "lse"):
+        _same(f[k], i[k], f"{tag} {k}")
+    for part in ("fast", "depcap", "cap", "dapd"):
+        if part in i:
+            for x, y in zip(f[part], i[part]):
+                _same(x, y, f"{tag} {part}")
+        else:
+            assert part not in f
+    ref = oracle.step_stats(host(cur), None if prev is None else host(prev),
+                            row_index=host(ri).numpy(), vocab=vocab)
+    for k in ("conf", "entropy", "lse") + (("kl",) if prev is not None else ()):
+        assert_close(f[k], ref[k], f"{tag} {k}")
+    assert np.array_equal(host(f["argmax"]).numpy(), ref["argmax"])
+    print(f"[fused] {tag}: " + ", ".join(f"{p} {int(host(f[p][0]).sum())}" for p in
+                                         ("fast", "cap", "dapd") if p in f))
+    return f
+
+
+def _llada_parts(cur, R, attn=None):
+    n = cur.shape[0]
+    block = torch.zeros(n, device=DEV, dtype=torch.uint8)
+    block[R["fast_block"][0]:R["fast_block"][1]] = 1
+    fast = dict(eligible=block, tau=R["tau"])
+    depcap = dict(lam=R["lam"], l_min=R["l_min"], l_max=R["l_max"])
+    cap = dict(eligible=block, tau_low=R["tau_low"], tau_high=R["tau_high"], gamma=R["gamma"],
+               k_max=R["k_max"])
+    return fast, depcap, cap
+
+
+@pytest.mark.parametrize("variant", ["peak", "cov"])
+def test_fused_llada_step_equals_individual_calls(variant):
+    cur, prev, so, ri = synth.logits("llada", DEV, variant=variant)
+    R = synth.RULES["llada"]
+    pos, offs = synth.gen_positions("llada", DEV)
+    attn = synth.attention("llada", DEV, batch=1, variant=variant, masked_pos=pos)
+    fast, depcap, cap = _llada_parts(cur, R)
+    dapd = dict(attn=attn, masked_pos=pos, m_max=256, tau=R["dapd_tau"])
+    _check(cur, prev, so, ri, fast, depcap, cap, dapd, f"llada/{variant}")
+
+
+def test_fused_parts_on_and_off():
+    cur, prev, so, ri = synth.logits("tiny", DEV)
+    R = synth.RULES["tiny"]
+    attn = synth.attention("tiny", DEV)
+    pos, offs = synth.gen_positions("tiny", DEV)
+    fast, depcap, cap = _llada_parts(cur, R)
+    dapd = dict(attn=attn, masked_pos=pos, m_max=32, tau=R["dapd_tau"])
+    _check(cur, prev, so, ri, tag="tiny stats only")
+    _check(cur, None, so, ri, fast=fast, tag="tiny no prev + fast")
+    _check(cur, prev, so, ri, depcap=depcap, dapd=dapd, tag="tiny depcap + dapd")
+    _check(cur, prev, so, ri, fast, depcap, cap, dapd, "tiny all")
+
+
+def test_fused_many_sequences_row_gather_and_f32():
+    # a dapd-shaped batch (8 sequences, no prev) with CAP over every row, rows
+    # gathered through a permuted row_index, then f32 logits with a padded ld
+    spec = synth.SPECS["dapd"]
+    cur, prev, so, ri = synth.logits("dapd", DEV)
+    pos, offs = synth.gen_positions("dapd", DEV)
+    attn = synth.attention("dapd", DEV, variant="cov", masked_pos=pos[:spec.rows])
+    cap = dict(eligible=None, tau_low=0.7, tau_high=0.95, gamma=-16.0, k_max=64)
+    dapd = dict(attn=attn, masked_pos=pos, m_max=256, tau=0.01)
+    fast = dict(eligible=None, tau=0.9)
+    _check(cur, None, offs, ri, fast=fast, cap=cap, dapd=dapd, tag="dapd x8")
+    g = torch.Generator().manual_seed(5)
+    ri2 = torch.randperm(spec.rows * spec.batch, generator=g).to(DEV)
+    _check(cur, None, offs, ri2, fast=fast, cap=cap, tag="dapd x8 permuted rows")
+    small = synth.Spec("f32", 21, 3, 40, 5000, torch.float32, 2.0, 0.6, 12.0, 0.5,
+                       n_lh=4, seq_len=64, attn_sigma=2.0, attn_dtype=torch.float32)
+    c32, p32, so32, ri32 = synth.logits(small, DEV, vocab=5003)
+    pos32 = torch.cat([torch.arange(24, 64, device=DEV, dtype=torch.int32)] * 3)
+    att32 = synth.attention(small, DEV)
+    d = dict(depcap=dict(lam=1.2, l_min=4, l_max=32),
+             cap=dict(eligible=None, tau_low=0.5, tau_high=0.95, gamma=-16.0, k_max=16),
+             dapd=dict(attn=att32, masked_pos=pos32, m_max=48, tau=0.02))
+    # ld 5003 f32 rows are not 16-byte aligned: the element-wise statistics path
+    _check(c32, p32, so32, ri32, **d, tag="f32 padded ld", vocab=5000)

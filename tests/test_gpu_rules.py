@@ -372,3 +372,20 @@ def test_dapd_reports_out_of_range_position():
         assert bool(torch.all(torch.isnan(out["sym"][1])))
         for lo, hi, b in ((0, 10, 0), (20, 30, 2)):
             assert torch.equal(out["commit"][lo:hi], ref["commit"][lo:hi])
+
+
+def test_dapd_nan_keys_never_chosen():
+    # NaN confidences give NaN keys: such nodes sort after every finite key
+    # and are never chosen; the rest follows the oracle (decision-only and
+    # end to end)
+    cur, prev, so, ri, g, o = _stats("tiny")
+    attn = synth.attention("tiny", DEV)
+    pos, offs = synth.gen_positions("tiny", DEV)
+    conf_g = g["conf"].clone()
+    conf_o = np.array(o["conf"], copy=True)
+    for r in (3, 17, 31):
+        conf_g[r] = float("nan")
+        conf_o[r] = np.nan
+    for tau in (0.01, 0.05):
+        out = _dapd_case(attn, pos, offs, conf_g, conf_o, tau, 32, f"nan keys tau={tau}")
+        assert host(out["commit"])[[3, 17, 31]].sum() == 0
