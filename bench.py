@@ -13,12 +13,20 @@ vocabulary 126464, bf16 current and previous-step logits):
   dlm_dapd_select      DAPD graph over the 256 rows from [1, 320, 768, 768] bf16
                        attention (prompt 512 + generation 256), tau 0.01
 
+By default (`--mode fused`) the step is the one call dlm_decide_step, which
+runs the same decisions in three launches (statistics rows and attention
+averaging in one streaming kernel, then the four rules, then the DAPD
+selection), issued back to back on one stream; the host stays ahead of the
+GPU, so the launches queue without gaps (a graph per step measured slower:
+each graph launch adds a few microseconds).  Its decisions equal the five
+calls' (checked on every run and reported).
+
 Inputs are resident in HBM before timing starts; `--replicas` independent
 copies are rotated so that consecutive steps do not hit the 256 MB Infinity
-Cache.  Prints one JSON line (rank 0, N = 1): decisions/s, ms/step, the stats
-kernel's achieved HBM bandwidth against the 8 TB/s peak (HIP events on the
-launch stream, averaged over the timed steps), and the CPU oracle's rate on
-the same step.
+Cache.  Prints one JSON line (rank 0, N = 1): decisions/s, ms/step, the
+dominant kernel's achieved HBM bandwidth against the 8 TB/s peak (HIP events
+on its launch stream, averaged over the timed steps), and the CPU oracle's
+rate on the same step.
 """
 from __future__ import annotations
 
@@ -34,30 +42,86 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "stats_llada_traffic.json")
-STATS_SOURCES = [os.path.join(ROOT, "diffusion_lm_unmask_amd", "csrc", f)
-                 for f in ("stats.hip", "dlm_device.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llada_step_traffic.json")
+# the device sources each timed kernel is built from: a counter reading is
+# only reported while they are unchanged since it was taken
+KERNEL_SOURCES = {
+    "k_step_stream": ("fused.hip", "stats_impl.h", "dapd_impl.h", "dlm_device.h"),
+    "k_stats": ("stats.hip", "stats_impl.h", "dlm_device.h"),
+}
 
 
-def stats_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for p in STATS_SOURCES:
-        with open(p, "rb") as f:
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "diffusion_lm_unmask_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(nbytes_alg: int):
-    """HBM bytes per stats launch from the committed rocprofv3 counter runs,
-    only while the kernel source is unchanged since they were taken."""
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    runs (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
+            t = json.load(f).get(kernel, {})
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != stats_source_hash():
+    if t.get("kernel_source_sha256") != kernel_source_hash(kernel):
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+class TimingEvents:
+    """Pairs of HIP timing events created without the system-scope fence
+    (hipEventDisableSystemFence), so that recording one adds no cache
+    write-back to the interval it brackets; recorded on the launch stream.
+    They come from the HIP runtime already loaded into the process (torch's),
+    so they are valid on torch's streams."""
+
+    NO_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n: int):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.pairs = []
+        for _ in range(n):
+            pair = []
+            for _ in range(2):
+                e = ctypes.c_void_p()
+                if self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.NO_SYSTEM_FENCE):
+                    raise RuntimeError("hipEventCreateWithFlags failed")
+                pair.append(e.value)
+            self.pairs.append(tuple(pair))
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(self.ct.c_void_p(ev), self.ct.c_void_p(stream)):
+            raise RuntimeError("hipEventRecord failed")
+
+    def mean_us(self):
+        """Average interval in microseconds (call after the device is synchronized)."""
+        ms, acc = self.ct.c_float(), 0.0
+        for a, b in self.pairs:
+            if self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ct.c_void_p(a),
+                                            self.ct.c_void_p(b)):
+                raise RuntimeError("hipEventElapsedTime failed")
+            acc += ms.value
+        return acc / len(self.pairs) * 1000.0
+
+    def close(self):
+        for pair in self.pairs:
+            for e in pair:
+                self.hip.hipEventDestroy(self.ct.c_void_p(e))
+        self.pairs = []
 
 
 def torch_int_view(t):
@@ -106,6 +170,48 @@ class LladaStep:
         self.stream = self.torch_stream.cuda_stream
         self.n_lh, self.S = attn.shape[1], attn.shape[2]
         self.bytes_stats = n * self.V * 2 * 2          # cur + prev rows, bf16
+        # the DAPD average reads the masked rows x masked columns of every
+        # attention map (bf16) and writes the fp32 average a
+        self.bytes_avg = self.n_lh * n * n * 2 + n * n * 4
+        self.desc = [self._desc(r) for r in range(replicas)]
+
+    def _desc(self, r):
+        """dlm_decide_step descriptor of the same step on input replica r."""
+        from diffusion_lm_unmask_amd import _lib
+        R, d = self.R, _lib.StepDesc()
+        d.logits, d.prev_logits, d.dtype = self.cur[r].data_ptr(), self.prev[r].data_ptr(), 0
+        d.vocab, d.ld, d.row_index, d.n_rows = self.V, self.V, self.ri.data_ptr(), self.rows
+        d.conf, d.argmax, d.entropy = self.conf.data_ptr(), self.arg.data_ptr(), self.ent.data_ptr()
+        d.kl, d.lse, d.seq_offsets, d.n_seq = self.kl.data_ptr(), self.lse.data_ptr(), \
+            self.so.data_ptr(), 1
+        d.fast_eligible, d.fast_tau = self.block.data_ptr(), R["tau"]
+        d.fast_commit, d.fast_n_commit = self.commit_f.data_ptr(), self.nf.data_ptr()
+        d.depcap_lambda, d.depcap_l_min, d.depcap_l_max = R["lam"], R["l_min"], R["l_max"]
+        d.depcap_radius, d.depcap_eps = 1, 1e-12
+        d.depcap_block_len, d.depcap_score = self.blen.data_ptr(), self.score.data_ptr()
+        d.cap_eligible, d.cap_tau_low, d.cap_tau_high = self.block.data_ptr(), R["tau_low"], \
+            R["tau_high"]
+        d.cap_gamma, d.cap_k_max = R["gamma"], R["k_max"]
+        d.cap_commit, d.cap_n_commit = self.commit_c.data_ptr(), self.nc.data_ptr()
+        d.attn, d.attn_dtype, d.n_lh, d.S = self.attn[r].data_ptr(), 0, self.n_lh, self.S
+        d.batch_stride, d.masked_pos, d.m_max = self.n_lh * self.S * self.S, \
+            self.pos.data_ptr(), self.rows
+        d.dapd_tau, d.dapd_commit, d.dapd_n_commit = R["dapd_tau"], self.commit_d.data_ptr(), \
+            self.nd.data_ptr()
+        d.dapd_workspace, d.dapd_workspace_bytes = self.ws.data_ptr(), self.ws_bytes
+        return d
+
+    def fused(self, r, ev=None):
+        """The same step as one dlm_decide_step call (three launches); with
+        `ev` (a pair of raw HIP events), the library records them around its
+        streaming launch."""
+        import ctypes
+        d = self.desc[r]
+        d.launch1_begin_event = ev[0] if ev is not None else None
+        d.launch1_end_event = ev[1] if ev is not None else None
+        st = self.L.dlm_decide_step(ctypes.byref(d), self.stream)
+        if st:
+            self.check(st, "dlm_decide_step")
 
     def outputs(self):
         """Copies of every output, as raw bits (so NaN compares equal to NaN)."""
@@ -160,12 +266,12 @@ class LladaStep:
         if st:
             self.check(st, "dlm_dapd_select")
 
-    def step(self, r, ev=None):
+    def step(self, r, ev=None, events=None):
         if ev is not None:
-            ev[0].record()
+            events.record(ev[0], self.stream)
         self.stats(r)
         if ev is not None:
-            ev[1].record()
+            events.record(ev[1], self.stream)
         self.fastdllm(r)
         self.depcap(r)
         self.cap(r)
@@ -321,7 +427,17 @@ def _per_call_body(dev, timed, stats_of, schedules, res):
     timed("dapd_select/llada", lambda r: api.dapd_select(attn[r], pos, offs, st["conf"], 0.01,
                                                          m_max=256, workspace=ws), 4, nb,
           "1 x [320, 768, 768] bf16 maps, 256 masked")
-    del cur, prev, curs, attn, st
+    # the whole step as one call (three launches)
+    prevs = [prev] + [prev.clone() for _ in range(3)]
+    parts = dict(fast=dict(eligible=block, tau=R["tau"]),
+                 depcap=dict(lam=R["lam"], l_min=R["l_min"], l_max=R["l_max"]),
+                 cap=dict(eligible=block, tau_low=R["tau_low"], tau_high=R["tau_high"],
+                          gamma=R["gamma"], k_max=R["k_max"]))
+    timed("decide_step/llada", lambda r: api.decide_step(
+        curs[r], prevs[r], so, row_index=ri, **parts,
+        dapd=dict(attn=attn[r], masked_pos=pos, m_max=256, tau=R["dapd_tau"], workspace=ws)),
+          4, cur.numel() * 2 * 2 + nb, "statistics, Fast-dLLM, DepCap, CAP and DAPD in one call")
+    del cur, prev, curs, prevs, attn, st
     torch.cuda.empty_cache()
     # dream: CAP with K_max 64 over every row
     spec, cur, prev, so, ri, st, _ = stats_of("dream", 1)
@@ -345,6 +461,10 @@ def _per_call_body(dev, timed, stats_of, schedules, res):
     timed("dapd_step/dapd", lambda r: api.dapd_step(attn[0], pos, offs, st["conf"], 0.01,
                                                     gen_len=gen_len, m_max=256, workspace=ws),
           1, None, "same, 3 of 8 sequences in the late stage")
+    timed("decide_step/dapd", lambda r: api.decide_step(
+        cur, None, offs, row_index=ri, fast=dict(tau=0.9), cap=dict(k_max=64),
+        dapd=dict(attn=attn[0], masked_pos=pos, m_max=256, tau=0.01, workspace=ws)),
+          1, cur.numel() * 2 + nb, "statistics, Fast-dLLM, CAP (every row) and DAPD, 8 sequences")
     del cur, attn, st
     torch.cuda.empty_cache()
     # stress: 64 x 1024 rows with prev (33 GB)
@@ -371,8 +491,12 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 10 plain device-to-device copies of MIB MiB (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
-    ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
-                    help="graph: the step is captured once per input replica and replayed")
+    ap.add_argument("--mode", choices=("fused", "fused-graph", "graph", "eager"),
+                    default="fused",
+                    help="fused: one dlm_decide_step call (three launches) per step; "
+                         "fused-graph: that call captured once per input replica and "
+                         "replayed; graph: the five individual calls captured and replayed; "
+                         "eager: the five calls launched one by one")
     ap.add_argument("--calls", action="store_true",
                     help="only time every entry point on its workloads and print one JSON line")
     ap.add_argument("--call-iters", type=int, default=20)
@@ -407,42 +531,74 @@ def main() -> int:
     sm = step.torch_stream
     torch.cuda.synchronize()
 
-    def timed_eager(n_steps, with_stats_events):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n_steps)] if with_stats_events else None
+    def timed_eager(n_steps, fused):
+        """Eager run of n_steps steps with HIP events around the dominant
+        launch of each step (the fused streaming launch, else the statistics
+        call), on the launch stream."""
+        events = TimingEvents(n_steps)
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         with torch.cuda.stream(sm):
             t0.record()
             for i in range(n_steps):
-                step.step(i % R, ev[i] if ev else None)
+                if fused:
+                    step.fused(i % R, events.pairs[i])
+                else:
+                    step.step(i % R, events.pairs[i], events)
             t1.record()
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / n_steps
-        st_us = (sum(a.elapsed_time(b) for a, b in ev) / n_steps * 1000.0) if ev else None
-        return ms, st_us
+        us = events.mean_us()
+        events.close()
+        return ms, us
 
+    fused = args.mode in ("fused", "fused-graph")
+    run = step.fused if fused else step.step
     with torch.cuda.stream(sm):
         for i in range(args.warmup):
-            step.step(i % R)
+            run(i % R)
     torch.cuda.synchronize()
 
+    # the fused step's decisions against the individual calls' on replica 0
+    with torch.cuda.stream(sm):
+        step.step(0)
+    torch.cuda.synchronize()
+    calls_out = step.outputs()
+    with torch.cuda.stream(sm):
+        step.fused(0)
+    torch.cuda.synchronize()
+    fused_out = step.outputs()
+    decisions_idx = (1, 5, 6, 7, 9, 10, 11, 12)     # argmax, every commit, count and length
+    fused_match = all(torch.equal(calls_out[i], fused_out[i]) for i in decisions_idx)
+
+    def timed_plain(fn):
+        """K steps back to back on the launch stream, bracketed by events."""
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(sm):
+            t0.record()
+            for i in range(args.steps):
+                fn(i % R)
+            t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
     graph_ok = None
-    if args.mode == "graph":
-        # one captured step per input replica; replays run the seven kernels
-        # back to back without host launch overhead
+    if args.mode in ("graph", "fused-graph"):
+        # one captured step per input replica; replays run its kernels back
+        # to back without host launch overhead
         graphs = []
         for r in range(R):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=sm):
-                step.step(r)
+                run(r)
             graphs.append(g)
         torch.cuda.synchronize()
         # replay correctness: each replica's replay equals its eager step
         graph_ok = True
         for r in range(R):
             with torch.cuda.stream(sm):
-                step.step(r)
+                run(r)
             torch.cuda.synchronize()
             want = step.outputs()
             graphs[r].replay()
@@ -451,21 +607,15 @@ def main() -> int:
             graph_ok = graph_ok and all(torch.equal(a, b) for a, b in zip(want, got))
         for i in range(args.warmup):
             graphs[i % R].replay()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(sm):
-            t0.record()
-            for i in range(args.steps):
-                graphs[i % R].replay()
-            t1.record()
-        torch.cuda.synchronize()
-        ms_per_step = t0.elapsed_time(t1) / args.steps
-        # the stats kernel's live duration: HIP events on its launch stream over
-        # an eager run of the same steps (events cannot sit inside the graphs)
-        eager_ms, stats_us = timed_eager(args.steps, True)
+        ms_per_step = timed_plain(lambda r: graphs[r].replay())
     else:
-        ms_per_step, stats_us = timed_eager(args.steps, True)
-        eager_ms = ms_per_step
+        ms_per_step = timed_plain(run)
+    # the dominant kernel's live duration: fence-free HIP events recorded on
+    # its launch stream right around it, over a second run of the same steps
+    # (kept out of the timed run: each record adds a little to the step)
+    events_ms, dom_us = timed_eager(args.steps, fused)
+    # the statistics call on its own (the five calls, eager), for reference
+    calls_events_ms, stats_us = timed_eager(args.steps, False)
 
     # per-call breakdown (untimed region, same rotation)
     breakdown = {}
@@ -486,8 +636,14 @@ def main() -> int:
                 step.step((i + 1) % R)          # keep the inputs cold in cache
         breakdown[name] = round(acc / args.breakdown_iters * 1000.0, 2)
 
-    achieved = step.bytes_stats / (stats_us * 1e-6) / 1e9
-    traffic = measured_traffic(step.bytes_stats)
+    if fused:
+        dom, dom_label = "k_step_stream", "dlm_decide_step launch 1 (k_step_stream)"
+        dom_bytes = step.bytes_stats + step.bytes_avg
+    else:
+        dom, dom_label = "k_stats", "dlm_step_stats (k_stats)"
+        dom_bytes = step.bytes_stats
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    st_achieved = step.bytes_stats / (stats_us * 1e-6) / 1e9
     decisions = step.rows
     value = decisions / (ms_per_step * 1e-3)
     line = {
@@ -509,15 +665,23 @@ def main() -> int:
             "rows": step.rows, "vocab": step.V, "attention": [1, step.n_lh, step.S, step.S],
             "replicas": args.replicas, "mode": args.mode,
         },
-        "eager_ms_per_step": round(eager_ms, 5),
+        "events_run_ms_per_step": round(events_ms, 5),
         "graph_replay_matches_eager": graph_ok,
+        "fused_decisions_match_calls": fused_match,
+        "calls_events_run_ms_per_step": round(calls_events_ms, 5),
         "roofline": {
-            "bound": "hbm", "kernel": "dlm_step_stats (k_stats)",
+            "bound": "hbm", "kernel": dom_label,
             "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": traffic, "traffic_unit": "bytes/launch",
+            "traffic": measured_traffic(dom), "traffic_unit": "bytes/launch",
+            "algorithmic_bytes_per_launch": dom_bytes,
+            "avg_launch_us": round(dom_us, 3),
+        },
+        "stats_call_roofline": {
+            "kernel": "dlm_step_stats (k_stats)", "achieved": round(st_achieved, 1),
+            "frac": round(st_achieved / PEAK_HBM_GBS, 4), "avg_launch_us": round(stats_us, 3),
             "algorithmic_bytes_per_launch": step.bytes_stats,
-            "avg_launch_us": round(stats_us, 3),
+            "traffic": measured_traffic("k_stats"),
         },
         "breakdown_us": breakdown,
     }

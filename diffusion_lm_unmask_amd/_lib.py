@@ -60,6 +60,7 @@ class StepDesc(ctypes.Structure):
         ("attn", _P), ("attn_dtype", _I32), ("n_lh", _I32), ("S", _I64), ("batch_stride", _I64),
         ("masked_pos", _P), ("m_max", _I32), ("dapd_tau", _F), ("dapd_commit", _P),
         ("dapd_n_commit", _P), ("dapd_workspace", _P), ("dapd_workspace_bytes", _SZ),
+        ("launch1_begin_event", _P), ("launch1_end_event", _P),
     ]
 
 

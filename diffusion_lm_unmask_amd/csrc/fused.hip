@@ -206,6 +206,9 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
   if (g1 > 2147483647LL) return DLM_ERR_UNSUPPORTED;
   const dim3 grid1(static_cast<unsigned>(g1));
   const bool abf16 = !dapd || d->attn_dtype == DLM_BF16;
+  if (d->launch1_begin_event &&
+      hipEventRecord(static_cast<hipEvent_t>(d->launch1_begin_event), s) != hipSuccess)
+    return DLM_ERR_HIP;
   if (bf16) {
     if (prev) launch_stream<true, true>(abf16, grid1, s, sa);
     else launch_stream<true, false>(abf16, grid1, s, sa);
@@ -214,6 +217,9 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
     else launch_stream<false, false>(abf16, grid1, s, sa);
   }
   DLM_CHECK_LAUNCH();
+  if (d->launch1_end_event &&
+      hipEventRecord(static_cast<hipEvent_t>(d->launch1_end_event), s) != hipSuccess)
+    return DLM_ERR_HIP;
 
   // ---- launch 2: the per-sequence rules and the DAPD scores
   RulesArgs ra{};
