@@ -14,15 +14,17 @@
 //                sequence already fills every CU.  A lane keeps 5 maps in
 //                flight (more only queues up behind the memory system).  Map
 //                groups are summed in LDS in a fixed order.
-//  k_dapd_sym    grid-wide: s = (a + aT)/2 for 16 rows per workgroup, one
-//                16-lane team per row, lane l taking columns l, l+16, ...; the
-//                transposed half a[j][i] is read from a itself (the four teams
-//                of a wave share its cache lines), so no transposed copy is
-//                written; each step's 16 edge bits are one ballot slice; fp64
-//                proxy degree and the ordering key.
+//  k_dapd_sym    grid-wide: s = (a + aT)/2 for 4 rows per workgroup (one
+//                wave), one 16-lane team per row, lane l taking columns l,
+//                l+16, ...; the transposed half a[j][i] is read from a itself
+//                (the four teams of a wave share its cache lines), so no
+//                transposed copy is written; each step's 16 edge bits are one
+//                ballot slice; fp64 proxy degree and the ordering key.
 //  k_dapd_select one workgroup (1024 threads) per sequence:
 //                1. the adjacency bitset and keys into LDS;
-//                2. rank sort of the 64-bit keys (key desc, position asc);
+//                2. order by the 64-bit keys (key desc, position asc): each
+//                   wave sorts a run of 64 in registers, and a key's rank is
+//                   its lane plus a binary search in every other run;
 //                3. greedy over blocks of 64 nodes in that order: a node is
 //                   blocked by an earlier block's chosen node (bitset AND) or by
 //                   an earlier node of its own block (ballots), which gives the
@@ -214,7 +216,7 @@ __host__ __device__ inline Layout layout(int n_seq, int m_max) {
 constexpr int kSymRows = DLM_DAPD_SYM_ROWS;  // rows per k_dapd_sym workgroup (16 lanes each)
 constexpr int kSymNT = kSymRows * 16;
 
-// s = (a + aT)/2 for 16 rows per workgroup: adjacency bits (ballot slices),
+// s = (a + aT)/2 for kSymRows rows per workgroup: adjacency bits (ballot slices),
 // fp64 proxy degree (fixed-pattern 16-lane reduction), ordering key.
 __device__ __forceinline__ void dapd_sym_rows(int b, int rb,
     const int32_t* __restrict__ seq_offsets, int m_max, const float* __restrict__ conf, float tau,
