@@ -3,7 +3,10 @@
 //
 // One workgroup per sequence:
 //   1. pool = eligible rows with conf >= tau_low, as 64-bit keys
-//      (conf descending, row ascending) in LDS, bitonic-sorted;
+//      (conf descending, row ascending) in LDS, sorted (one wave in registers
+//      up to 64 keys, else the LDS bitonic sort).  Each row's argmax, lse and
+//      row offset are read in the same pass as its confidence, so the
+//      candidates need no second dependent trip to memory;
 //   2. the first k_max become candidates; empty pool -> top-1 eligible row;
 //   3. G[a][b] = logit_a[yhat_b] - lse_a gathered from HBM into LDS
 //      (k_max^2 two-byte gathers), D_ab = G[a][b] + G[b][a] (bit-symmetric),
@@ -35,6 +38,10 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
     float tau_high, float gamma, int k_max, uint8_t* __restrict__ commit,
     int32_t* __restrict__ n_commit, int32_t* __restrict__ cand_out, float* __restrict__ dmat_out) {
   __shared__ uint64_t keys[kMaxRows];
+  __shared__ float rc[kMaxRows];      // by local row (pool rows only): conf
+  __shared__ int32_t ry[kMaxRows];    // argmax
+  __shared__ float rlse[kMaxRows];    // lse
+  __shared__ int64_t rri[kMaxRows];   // row_index
   __shared__ float G[kKM][kKM + 1];
   __shared__ uint64_t cw[kKM][2];
   __shared__ int64_t coff[kKM];
@@ -69,12 +76,16 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
   for (int w = tid; w < kMaxRows / 32; w += kCapNT) sel[w] = 0u;
   __syncthreads();
 
-  // 1. pool (arrival order is irrelevant: the sort makes it deterministic)
+  // 1. pool (arrival order is irrelevant: the sort makes it deterministic).
+  // The per-row reads do not depend on each other (one trip to memory).
   float best = 0.f;
   int bidx = INT32_MAX;
   for (int r = tid; r < n; r += kCapNT) {
     const float c = conf[lo + r];
     const bool el = eligible ? eligible[lo + r] != 0 : true;
+    const int32_t y = argmax[lo + r];
+    const float l = lse[lo + r];
+    const int64_t ri = row_index[lo + r];
     if (!el || c != c) continue;
     if (bidx == INT32_MAX || c > best) {
       best = c;
@@ -83,15 +94,27 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
     if (c >= tau_low) {
       const int slot = atomicAdd(&npool, 1);
       keys[slot] = (static_cast<uint64_t>(dlm::desc_bits(c)) << 32) | static_cast<uint32_t>(r);
+      rc[r] = c;
+      ry[r] = y;
+      rlse[r] = l;
+      rri[r] = ri;
     }
   }
   __syncthreads();
   const int P = npool;
   int n2 = 1;
   while (n2 < P) n2 <<= 1;
-  for (int i = P + tid; i < n2; i += kCapNT) keys[i] = ~0ull;
-  __syncthreads();
-  if (P > 1) dlm::bitonic_sort<kCapNT>(keys, n2);
+  if (n2 <= DLM_WAVE) {
+    if (tid < DLM_WAVE && P > 1) {  // one wave, in registers: lane l holds key l
+      const uint64_t v = dlm::wave_sort_asc(tid < P ? keys[tid] : ~0ull, n2);
+      if (tid < P) keys[tid] = v;
+    }
+    __syncthreads();
+  } else {
+    for (int i = P + tid; i < n2; i += kCapNT) keys[i] = ~0ull;
+    __syncthreads();
+    dlm::bitonic_sort<kCapNT>(keys, n2);
+  }
   const int K = min(P, k_max);
 
   if (K == 0) {  // 2. no candidate: top-1 eligible row
@@ -106,14 +129,14 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
   }
 
   for (int a = tid; a < K; a += kCapNT) {
-    const int r = lo + static_cast<int>(keys[a] & 0xffffffffu);
-    crow[a] = r;
-    cconf[a] = conf[r];
-    cy[a] = argmax[r];
-    clse[a] = lse[r];
-    coff[a] = row_index[r] * ld;
+    const int r = static_cast<int>(keys[a] & 0xffffffffu);
+    crow[a] = lo + r;
+    cconf[a] = rc[r];
+    cy[a] = ry[r];
+    clse[a] = rlse[r];
+    coff[a] = rri[r] * ld;
     // every gather below is at coff[.] + cy[.]: check the indices first
-    if (cy[a] < 0 || cy[a] >= vocab || row_index[r] < 0) bad = 1;
+    if (ry[r] < 0 || ry[r] >= vocab || rri[r] < 0) bad = 1;
   }
   __syncthreads();
   if (bad) {  // an argmax outside [0, vocab) or a negative row index

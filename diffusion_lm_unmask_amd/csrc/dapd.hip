@@ -16,11 +16,11 @@ __global__ __launch_bounds__(kAvgNT) void k_dapd_avg(
 }
 
 __global__ __launch_bounds__(kSymNT) void k_dapd_sym(
-    const int32_t* __restrict__ seq_offsets, int m_max, const float* __restrict__ conf,
-    float tau, const char* __restrict__ ws, Layout L, float* __restrict__ degree,
-    float* __restrict__ sym, float* __restrict__ key_out, Policy P) {
-  dapd_sym_rows(blockIdx.y, blockIdx.x, seq_offsets, m_max, conf, tau, ws, L, degree, sym,
-                key_out, P);
+    const int32_t* __restrict__ seq_offsets, const int32_t* __restrict__ masked_pos, int64_t S,
+    int m_max, const float* __restrict__ conf, float tau, const char* __restrict__ ws, Layout L,
+    float* __restrict__ degree, float* __restrict__ sym, float* __restrict__ key_out, Policy P) {
+  dapd_sym_rows(blockIdx.y, blockIdx.x, seq_offsets, masked_pos, S, m_max, conf, tau, ws, L,
+                degree, sym, key_out, P);
 }
 
 __global__ __launch_bounds__(kSelNT) void k_dapd_select(
@@ -67,7 +67,7 @@ int dapd_run(const void* attn, int dtype, int32_t n_lh, int64_t S, int64_t batch
                        masked_pos, seq_offsets, m_max, n_tc, vec_ok, ws_a, P);
   DLM_CHECK_LAUNCH();
   hipLaunchKernelGGL(k_dapd_sym, dim3((m_max + kSymRows - 1) / kSymRows, n_seq), dim3(kSymNT), 0,
-                     s, seq_offsets, m_max, conf, tau, ws, L, degree, sym, key, P);
+                     s, seq_offsets, masked_pos, S, m_max, conf, tau, ws, L, degree, sym, key, P);
   DLM_CHECK_LAUNCH();
   hipLaunchKernelGGL(k_dapd_select, dim3(n_seq), dim3(kSelNT), 0, s, masked_pos, S, seq_offsets,
                      m_max, ws, L, conf, commit, n_commit, degree, sym, key, P);

@@ -191,7 +191,7 @@ __device__ __forceinline__ void dapd_avg_tile(int b, int tile, const void* __res
 //   a          f32 [n_seq][m_max][ws_ld]     averaged maps
 //   adj        u64 [n_seq][m_max][words]     adjacency bitsets, words = ceil(m_max/64)
 //   keys       u64 [n_seq][m_max]            (order key, position)
-//   has_edge   u8  [n_seq][m_max]
+//   has_edge   u8  [n_seq][m_max]            bit 0: an edge; bit 1: position out of range
 struct Layout {
   size_t a, adj, keys, has_edge, total;
   int ld, words;
@@ -217,9 +217,12 @@ constexpr int kSymRows = DLM_DAPD_SYM_ROWS;  // rows per k_dapd_sym workgroup (1
 constexpr int kSymNT = kSymRows * 16;
 
 // s = (a + aT)/2 for kSymRows rows per workgroup: adjacency bits (ballot slices),
-// fp64 proxy degree (fixed-pattern 16-lane reduction), ordering key.
+// fp64 proxy degree (fixed-pattern 16-lane reduction), ordering key.  Each
+// row's masked position is checked here too: has_edge carries bit 1 for a
+// position outside [0, S), which the selection reports.
 __device__ __forceinline__ void dapd_sym_rows(int b, int rb,
-    const int32_t* __restrict__ seq_offsets, int m_max, const float* __restrict__ conf, float tau,
+    const int32_t* __restrict__ seq_offsets, const int32_t* __restrict__ masked_pos, int64_t S,
+    int m_max, const float* __restrict__ conf, float tau,
     const char* __restrict__ ws, Layout L, float* __restrict__ degree, float* __restrict__ sym,
     float* __restrict__ key_out, Policy P) {
   const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
@@ -236,6 +239,7 @@ __device__ __forceinline__ void dapd_sym_rows(int b, int rb,
       for (int j = tl; j < m_max; j += 16) sym[sbase + static_cast<int64_t>(i) * m_max + j] = NAN;
     return;
   }
+  const int pos_i = masked_pos[lo + i];
   const float* A = reinterpret_cast<const float*>(ws + L.a) + static_cast<int64_t>(b) * m_max * L.ld;
   const float* ar = A + static_cast<int64_t>(i) * L.ld;
   uint16_t* adj16 = reinterpret_cast<uint16_t*>(
@@ -296,8 +300,9 @@ __device__ __forceinline__ void dapd_sym_rows(int b, int rb,
     // NaN keys sort last; every other key maps below 0xffffffff
     reinterpret_cast<uint64_t*>(const_cast<char*>(ws) + L.keys)[static_cast<int64_t>(b) * m_max + i] =
         (hi << 32) | static_cast<uint32_t>(i);
+    const uint32_t bad = pos_i < 0 || pos_i >= S;
     reinterpret_cast<uint8_t*>(const_cast<char*>(ws) + L.has_edge)[static_cast<int64_t>(b) * m_max + i] =
-        static_cast<uint8_t>(anyb);
+        static_cast<uint8_t>(anyb | (bad << 1));
   }
 }
 
@@ -321,13 +326,7 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
   const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
   const int64_t sbase = static_cast<int64_t>(b) * m_max * m_max;
 
-  int bad_pos = 0;  // a masked position outside [0, S): the sequence is reported
-  for (int r = tid; r < M && M <= m_max; r += kSelNT) {
-    const int p = masked_pos[lo + r];
-    bad_pos |= p < 0 || p >= S;
-  }
-  bad_pos = dlm::block_max_i<kSelNT>(bad_pos, shi);
-  if (M > m_max || M < 0 || bad_pos) {
+  auto report = [&]() {  // nothing committed, n_commit = -1
     for (int r = tid; r < M; r += kSelNT) {
       commit[lo + r] = 0;
       if (degree) degree[lo + r] = NAN;
@@ -340,9 +339,46 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
       n_commit[b] = -1;
       if (P.stage) P.stage[b] = 0;
     }
+  };
+  if (M > m_max || M < 0) {  // over-long sequence
+    report();
     return;
   }
   const bool late = late_stage(P, b, M);  // uniform over the workgroup
+  // a masked position outside [0, S) reports the sequence.  In the graph
+  // stage the scores kernel has checked every row (bit 1 of has_edge), so
+  // the graph's loads below are the only trip to memory before the check.
+  int bad_pos = 0;
+  const int nw = (M + 63) / 64;  // adjacency words in use
+  if (late) {
+    for (int r = tid; r < M; r += kSelNT) {
+      const int p = masked_pos[lo + r];
+      bad_pos |= p < 0 || p >= S;
+    }
+  } else {
+    const uint64_t* gadj = reinterpret_cast<const uint64_t*>(ws + L.adj) +
+                           static_cast<int64_t>(b) * m_max * L.words;
+    const uint64_t* gkeys = reinterpret_cast<const uint64_t*>(ws + L.keys) +
+                            static_cast<int64_t>(b) * m_max;
+    const uint8_t* gedge = reinterpret_cast<const uint8_t*>(ws + L.has_edge) +
+                           static_cast<int64_t>(b) * m_max;
+    for (int e = tid; e < M * nw; e += kSelNT) {
+      const int i = e / nw, w = e - i * nw;
+      adj[i][w] = gadj[static_cast<int64_t>(i) * L.words + w];
+    }
+    for (int e = tid; e < M; e += kSelNT) {
+      const uint8_t he = gedge[e];
+      keys[e] = gkeys[e];
+      has_edge[e] = he & 1u;
+      bad_pos |= he >> 1;
+    }
+    if (tid < kWords) chosen[tid] = 0ull;
+  }
+  bad_pos = dlm::block_max_i<kSelNT>(bad_pos, shi);  // ends with a barrier
+  if (bad_pos) {
+    report();
+    return;
+  }
   if (tid == 0 && P.stage) P.stage[b] = static_cast<uint8_t>(late);
   if (late) {  // no graph: conf > late_tau, else the most confident row
     int above = 0, bi = INT32_MAX;
@@ -368,28 +404,12 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
     if (tid == 0) n_commit[b] = cnt;
     return;
   }
-  const int nw = (M + 63) / 64;  // adjacency words in use
-  const uint64_t* gadj = reinterpret_cast<const uint64_t*>(ws + L.adj) +
-                         static_cast<int64_t>(b) * m_max * L.words;
-  for (int e = tid; e < M * nw; e += kSelNT) {
-    const int i = e / nw, w = e - i * nw;
-    adj[i][w] = gadj[static_cast<int64_t>(i) * L.words + w];
-  }
-  const uint64_t* gkeys = reinterpret_cast<const uint64_t*>(ws + L.keys) +
-                          static_cast<int64_t>(b) * m_max;
-  const uint8_t* gedge = reinterpret_cast<const uint8_t*>(ws + L.has_edge) +
-                         static_cast<int64_t>(b) * m_max;
-  for (int e = tid; e < M; e += kSelNT) {
-    keys[e] = gkeys[e];
-    has_edge[e] = gedge[e];
-  }
-  if (tid < kWords) chosen[tid] = 0ull;
-  __syncthreads();
 
-  // ---- order the nodes (keys are unique: they carry the position).  Wave w
+  // ---- order the nodes (keys are unique: they carry the node).  Wave w
   // sorts keys 64w .. 64w+63 in registers; a key's rank is its lane plus, for
-  // every other wave's sorted run, the number of keys below it (a binary
-  // search).  Padding keys (~0) sort after every node and get no rank.
+  // every other wave's sorted run, the number of keys below it (binary
+  // searches, four runs side by side).  Padding keys (~0) sort after every
+  // node and get no rank.
   const int n_runs = (M + 63) / 64;
   uint64_t v_sorted = ~0ull;
   if (wv < n_runs) {  // whole waves: every lane of the wave takes part
@@ -400,18 +420,25 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
   __syncthreads();
   if (wv < n_runs && v_sorted != ~0ull) {
     int rank = ln;
-    for (int r = 0; r < n_runs; ++r) {
-      if (r == wv) continue;
-      const uint64_t* run = keys + r * 64;
-      int c;  // keys of run r below v_sorted
-      if (run[63] < v_sorted) {
-        c = 64;
-      } else {
-        c = 0;
-        for (int step = 32; step > 0; step >>= 1)
-          if (run[c + step - 1] < v_sorted) c += step;
+    for (int r0 = 0; r0 < n_runs; r0 += 4) {
+      int c[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = r0 + q;
+        // keys of run r below v_sorted (its own run: the lane counts them)
+        c[q] = (r < n_runs && r != wv && keys[r * 64 + 63] < v_sorted) ? 64 : 0;
       }
-      rank += c;
+#pragma unroll
+      for (int step = 32; step > 0; step >>= 1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = r0 + q;
+          if (r < n_runs && r != wv && c[q] < 64 && keys[r * 64 + c[q] + step - 1] < v_sorted)
+            c[q] += step;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rank += c[q];
     }
     // a NaN key (it sorts after every finite key) is stored as -1 - node:
     // such a node is never chosen

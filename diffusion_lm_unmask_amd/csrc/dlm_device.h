@@ -121,25 +121,72 @@ __device__ void bitonic_sort(uint64_t* keys, int n) {
   }
 }
 
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, DLM_WAVE);
-  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, DLM_WAVE);
+// The value of lane (l xor J) for every lane l.  Inside a row of 16 lanes
+// this is DPP on the VALU (no LDS crossbar): xor 1 and xor 2 are quad
+// permutations; xor 4 is the half-row mirror (xor 7) followed by the quad
+// reversal (xor 3); xor 8 is the row mirror (xor 15) followed by the half-row
+// mirror (xor 7).  Across rows it is a shuffle.
+template <int J>
+__device__ __forceinline__ int xor_lane(int v) {
+  if constexpr (J == 1) return dpp<0xB1>(v);                  // quad_perm [1,0,3,2]
+  else if constexpr (J == 2) return dpp<0x4E>(v);             // quad_perm [2,3,0,1]
+  else if constexpr (J == 4) return dpp<0x1B>(dpp<0x141>(v));  // quad_perm [3,2,1,0]
+  else if constexpr (J == 8) return dpp<0x141>(dpp<0x140>(v));
+  else return __shfl_xor(v, J, DLM_WAVE);
+}
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(xor_lane<J>(static_cast<int>(v)));
+  const uint32_t hi = static_cast<uint32_t>(xor_lane<J>(static_cast<int>(v >> 32)));
   return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// One compare-exchange step of the bitonic network (pair distance J, merge
+// size k) on one wave's registers.
+template <int J>
+__device__ __forceinline__ uint64_t bitonic_step(uint64_t v, int k, int l) {
+  const uint64_t o = xor_lane64<J>(v);
+  // the lower lane of a pair keeps the min in an ascending run
+  const bool keep_min = ((l & J) == 0) == ((l & k) == 0);
+  return keep_min ? (v < o ? v : o) : (v < o ? o : v);
 }
 
 // Ascending bitonic sort of the first n (a power of two <= 64) lanes' keys
 // of one wave, in registers: lane l ends with the key of rank l.  Lanes >= n
 // must hold keys no smaller than any of the first n (they sort among
-// themselves).  Call with all 64 lanes active.
+// themselves).  Call with all 64 lanes active (n wave-uniform).
 __device__ __forceinline__ uint64_t wave_sort_asc(uint64_t v, int n) {
   const int l = threadIdx.x % DLM_WAVE;
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t o = shfl_xor64(v, j);
-      // the lower lane of a pair keeps the min in an ascending run
-      const bool keep_min = ((l & j) == 0) == ((l & k) == 0);
-      v = keep_min ? (v < o ? v : o) : (v < o ? o : v);
-    }
+  if (n >= 2) v = bitonic_step<1>(v, 2, l);
+  if (n >= 4) {
+    v = bitonic_step<2>(v, 4, l);
+    v = bitonic_step<1>(v, 4, l);
+  }
+  if (n >= 8) {
+    v = bitonic_step<4>(v, 8, l);
+    v = bitonic_step<2>(v, 8, l);
+    v = bitonic_step<1>(v, 8, l);
+  }
+  if (n >= 16) {
+    v = bitonic_step<8>(v, 16, l);
+    v = bitonic_step<4>(v, 16, l);
+    v = bitonic_step<2>(v, 16, l);
+    v = bitonic_step<1>(v, 16, l);
+  }
+  if (n >= 32) {
+    v = bitonic_step<16>(v, 32, l);
+    v = bitonic_step<8>(v, 32, l);
+    v = bitonic_step<4>(v, 32, l);
+    v = bitonic_step<2>(v, 32, l);
+    v = bitonic_step<1>(v, 32, l);
+  }
+  if (n >= 64) {
+    v = bitonic_step<32>(v, 64, l);
+    v = bitonic_step<16>(v, 64, l);
+    v = bitonic_step<8>(v, 64, l);
+    v = bitonic_step<4>(v, 64, l);
+    v = bitonic_step<2>(v, 64, l);
+    v = bitonic_step<1>(v, 64, l);
   }
   return v;
 }

@@ -79,6 +79,8 @@ struct RulesArgs {
   uint8_t* c_commit;
   int32_t* c_n;
   // DAPD scores
+  const int32_t* masked_pos;
+  int64_t S;
   int m_max, rb_per_seq;
   float tau;
   const char* ws;
@@ -108,8 +110,8 @@ __global__ __launch_bounds__(kRulesNT) void k_step_rules(const RulesArgs a) {
   }
   g -= a.nc;
   if (threadIdx.x >= kSymNT) return;  // the scores use one wave: four 16-lane teams
-  dapd_sym_rows(g / a.rb_per_seq, g % a.rb_per_seq, a.seq_offsets, a.m_max, a.conf, a.tau, a.ws,
-                a.L, nullptr, nullptr, nullptr, a.P);
+  dapd_sym_rows(g / a.rb_per_seq, g % a.rb_per_seq, a.seq_offsets, a.masked_pos, a.S, a.m_max,
+                a.conf, a.tau, a.ws, a.L, nullptr, nullptr, nullptr, a.P);
 }
 
 struct SelectArgs {
@@ -257,6 +259,8 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
   ra.c_kmax = d->cap_k_max;
   ra.c_commit = d->cap_commit;
   ra.c_n = d->cap_n_commit;
+  ra.masked_pos = d->masked_pos;
+  ra.S = d->S;
   ra.m_max = d->m_max;
   ra.tau = d->dapd_tau;
   ra.ws = ws;
