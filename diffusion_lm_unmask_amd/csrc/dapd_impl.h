@@ -348,7 +348,7 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
   // a masked position outside [0, S) reports the sequence.  In the graph
   // stage the scores kernel has checked every row (bit 1 of has_edge), so
   // the graph's loads below are the only trip to memory before the check.
-  int bad_pos = 0;
+  int bad_pos = 0, any_edge = 0;
   const int nw = (M + 63) / 64;  // adjacency words in use
   if (late) {
     for (int r = tid; r < M; r += kSelNT) {
@@ -370,12 +370,13 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
       const uint8_t he = gedge[e];
       keys[e] = gkeys[e];
       has_edge[e] = he & 1u;
+      any_edge |= he & 1u;
       bad_pos |= he >> 1;
     }
     if (tid < kWords) chosen[tid] = 0ull;
   }
-  bad_pos = dlm::block_max_i<kSelNT>(bad_pos, shi);  // ends with a barrier
-  if (bad_pos) {
+  const int flags = dlm::block_or_i<kSelNT>(bad_pos | (any_edge << 1), shi);  // ends with a barrier
+  if (flags & 1) {
     report();
     return;
   }
@@ -405,6 +406,21 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
     return;
   }
 
+  if (!(flags & 2)) {
+    // no edge anywhere: the independent set is every node whatever the
+    // order, except a NaN key (never chosen)
+    int cnt = 0;
+    for (int r = tid; r < M; r += kSelNT) {
+      const int c = static_cast<int>((keys[r] >> 32) != 0xffffffffull) |
+                    (P.pre_unmask && conf[lo + r] == 1.0f);  // pre-unmask
+      commit[lo + r] = static_cast<uint8_t>(c);
+      cnt += c;
+    }
+    cnt = dlm::block_sum<kSelNT>(cnt, shi);
+    if (tid == 0) n_commit[b] = cnt;
+    return;
+  }
+
   // ---- order the nodes (keys are unique: they carry the node).  Wave w
   // sorts keys 64w .. 64w+63 in registers; a key's rank is its lane plus, for
   // every other wave's sorted run, the number of keys below it (binary
@@ -421,24 +437,29 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
   if (wv < n_runs && v_sorted != ~0ull) {
     int rank = ln;
     for (int r0 = 0; r0 < n_runs; r0 += 4) {
+      // keys of run r below v_sorted, four runs side by side, without
+      // branches (a run that is this wave's own, or past the last, is
+      // searched as this wave's run and not counted)
+      const uint64_t* run[4];
+      bool use[4];
       int c[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = r0 + q;
-        // keys of run r below v_sorted (its own run: the lane counts them)
-        c[q] = (r < n_runs && r != wv && keys[r * 64 + 63] < v_sorted) ? 64 : 0;
+        use[q] = r < n_runs && r != wv;
+        run[q] = keys + (use[q] ? r : wv) * 64;
+        c[q] = 0;
       }
 #pragma unroll
       for (int step = 32; step > 0; step >>= 1) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = r0 + q;
-          if (r < n_runs && r != wv && c[q] < 64 && keys[r * 64 + c[q] + step - 1] < v_sorted)
-            c[q] += step;
-        }
+        for (int q = 0; q < 4; ++q) c[q] += run[q][c[q] + step - 1] < v_sorted ? step : 0;
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) rank += c[q];
+      for (int q = 0; q < 4; ++q) {
+        c[q] += run[q][c[q]] < v_sorted ? 1 : 0;  // c <= 63 before: 0..64 after
+        rank += use[q] ? c[q] : 0;
+      }
     }
     // a NaN key (it sorts after every finite key) is stored as -1 - node:
     // such a node is never chosen
@@ -485,16 +506,20 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
             }
           }
         }
-        uint64_t cand = __ballot(v >= 0 && !blocked);
+        const uint64_t cand = __ballot(v >= 0 && !blocked);
         if (__ballot(local != 0ull) == 0ull) {
           sel = cand;  // no conflicts inside the block
         } else {
+          // in rounds: a candidate whose earlier in-block neighbours are all
+          // decided decides now (taken unless one of them was taken).  The
+          // lowest undecided candidate is always ready, and each decision is
+          // the one the node-by-node scan makes.
           sel = 0ull;
-          while (cand) {
-            const int p = __builtin_ctzll(cand);
-            sel |= 1ull << p;
-            cand &= ~(1ull << p);
-            cand &= ~__ballot(((local >> p) & 1ull) != 0ull);  // later nodes adjacent to p
+          uint64_t open = cand;
+          while (open) {
+            const bool ready = ((open >> ln) & 1ull) && (local & open) == 0ull;
+            sel |= __ballot(ready && (local & sel) == 0ull);
+            open &= ~__ballot(ready);
           }
         }
       }

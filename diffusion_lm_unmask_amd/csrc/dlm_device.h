@@ -90,6 +90,9 @@ struct OpMaxF {
 struct OpMinI {
   __device__ int operator()(int a, int b) const { return min(a, b); }
 };
+struct OpOrI {
+  __device__ int operator()(int a, int b) const { return a | b; }
+};
 
 // Order-preserving key of a float for a descending sort: a larger value gives
 // a smaller key (NaN is the caller's to exclude); -0 and +0 share a key, so
@@ -244,6 +247,23 @@ __device__ __forceinline__ int block_max_i(int v, int* sh) {
   int r = sh[0];
 #pragma unroll
   for (int i = 1; i < NW; ++i) r = max(r, sh[i]);
+  return r;
+}
+
+// Bitwise OR over a workgroup (DPP within each wave); every thread must call
+// it, and every thread gets the result.  `sh` holds NT/64 ints and may be
+// reused once it returns.
+template <int NT>
+__device__ __forceinline__ int block_or_i(int v, int* sh) {
+  constexpr int NW = NT / DLM_WAVE;
+  v = wave_reduce(v, OpOrI{});
+  const int w = threadIdx.x / DLM_WAVE, l = threadIdx.x % DLM_WAVE;
+  __syncthreads();
+  if (l == 0) sh[w] = v;
+  __syncthreads();
+  int r = sh[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r |= sh[i];
   return r;
 }
 
