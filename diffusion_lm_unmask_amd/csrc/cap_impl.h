@@ -11,8 +11,9 @@
 //   3. G[a][b] = logit_a[yhat_b] - lse_a gathered from HBM into LDS
 //      (k_max^2 two-byte gathers), D_ab = G[a][b] + G[b][a] (bit-symmetric),
 //      conflict bits (D_ab > gamma) as two 64-bit words per candidate;
-//   4. one lane runs the greedy: tau_high members unconditionally, the rest
-//      when their conflict words do not meet the chosen set.
+//   4. the greedy in candidate order on one wave (readlane of each
+//      candidate's conflict words): tau_high members unconditionally, the
+//      rest when their conflict words do not meet the chosen set.
 #include <math.h>
 
 #pragma once
@@ -190,21 +191,44 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
   }
   __syncthreads();
 
-  // 4. greedy pick, one lane
-  if (tid == 0) {
+  // 4. greedy pick on wave 0: lane l holds the conflict words of candidates
+  // l and l + 64, and the scan reads them with readlane (no memory trip per
+  // step).  s0 / s1 are the chosen candidates as a bitset.
+  if (tid < DLM_WAVE) {
+    uint64_t w00 = 0, w01 = 0, w10 = 0, w11 = 0;
+    bool f0 = false, f1 = false;  // forced: conf > tau_high
+    if (tid < K) {
+      w00 = cw[tid][0];
+      w01 = cw[tid][1];
+      f0 = cconf[tid] > tau_high;
+    }
+    if (tid + DLM_WAVE < K) {
+      w10 = cw[tid + DLM_WAVE][0];
+      w11 = cw[tid + DLM_WAVE][1];
+      f1 = cconf[tid + DLM_WAVE] > tau_high;
+    }
+    const uint64_t forced0 = __ballot(f0), forced1 = __ballot(f1);
     uint64_t s0 = 0, s1 = 0;
-    int cnt = 0;
     for (int a = 0; a < K; ++a) {
-      const bool ok = cconf[a] > tau_high || ((cw[a][0] & s0) == 0 && (cw[a][1] & s1) == 0);
-      if (ok) {
-        if (a < 64) s0 |= 1ull << a;
-        else s1 |= 1ull << (a - 64);
-        const int lr = crow[a] - lo;
-        sel[lr >> 5] |= 1u << (lr & 31);
-        ++cnt;
+      const int l = a & (DLM_WAVE - 1);
+      const bool hi = a >= DLM_WAVE;
+      const uint64_t c0 = dlm::rdlane64(hi ? w10 : w00, l);
+      const uint64_t c1 = dlm::rdlane64(hi ? w11 : w01, l);
+      const bool forced = (((hi ? forced1 : forced0) >> l) & 1ull) != 0;
+      if (forced || ((c0 & s0) == 0 && (c1 & s1) == 0)) {
+        if (hi) s1 |= 1ull << l;
+        else s0 |= 1ull << l;
       }
     }
-    n_commit[b] = cnt;
+    if ((s0 >> tid) & 1ull) {
+      const int lr = crow[tid] - lo;
+      atomicOr(&sel[lr >> 5], 1u << (lr & 31));
+    }
+    if ((s1 >> tid) & 1ull) {
+      const int lr = crow[tid + DLM_WAVE] - lo;
+      atomicOr(&sel[lr >> 5], 1u << (lr & 31));
+    }
+    if (tid == 0) n_commit[b] = __popcll(s0) + __popcll(s1);
   }
   __syncthreads();
   for (int r = tid; r < n; r += kCapNT) commit[lo + r] = (sel[r >> 5] >> (r & 31)) & 1u;

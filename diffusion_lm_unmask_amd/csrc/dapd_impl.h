@@ -239,7 +239,9 @@ __device__ __forceinline__ void dapd_sym_rows(int b, int rb,
       for (int j = tl; j < m_max; j += 16) sym[sbase + static_cast<int64_t>(i) * m_max + j] = NAN;
     return;
   }
+  // read now, used at the end: their latency hides behind the row reads
   const int pos_i = masked_pos[lo + i];
+  const float conf_i = conf[lo + i];
   const float* A = reinterpret_cast<const float*>(ws + L.a) + static_cast<int64_t>(b) * m_max * L.ld;
   const float* ar = A + static_cast<int64_t>(i) * L.ld;
   uint16_t* adj16 = reinterpret_cast<uint16_t*>(
@@ -293,7 +295,7 @@ __device__ __forceinline__ void dapd_sym_rows(int b, int rb,
   for (int o = 8; o > 0; o >>= 1) anyb |= __shfl_xor(anyb, o, 16);
   if (tl == 0) {
     const float df = static_cast<float>(dsum);
-    const float kk = df * conf[lo + i];
+    const float kk = df * conf_i;
     if (degree) degree[lo + i] = df;
     if (key_out) key_out[lo + i] = kk;
     const uint64_t hi = (kk != kk) ? 0xffffffffull : static_cast<uint64_t>(dlm::desc_bits(kk));

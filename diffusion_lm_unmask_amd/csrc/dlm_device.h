@@ -24,21 +24,6 @@ __device__ __forceinline__ T wave_sum(T v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, DLM_WAVE);
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, DLM_WAVE));
-  return v;
-}
-__device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, DLM_WAVE));
-  return v;
-}
-__device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, DLM_WAVE));
-  return v;
-}
 
 // Wave reductions on the DPP crossbar (no LDS traffic).  Inside each row of
 // 16 lanes, four steps pair every lane with one lane of the other half of its
@@ -72,6 +57,11 @@ __device__ __forceinline__ double rdlane(double v, int l) {
   const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), l);
   return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
 }
+__device__ __forceinline__ uint64_t rdlane64(uint64_t v, int l) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), l));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
 template <typename T, typename Op>
 __device__ __forceinline__ T wave_reduce(T v, Op op) {
   v = op(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
@@ -89,6 +79,9 @@ struct OpMaxF {
 };
 struct OpMinI {
   __device__ int operator()(int a, int b) const { return min(a, b); }
+};
+struct OpMaxI {
+  __device__ int operator()(int a, int b) const { return max(a, b); }
 };
 struct OpOrI {
   __device__ int operator()(int a, int b) const { return a | b; }
@@ -194,13 +187,15 @@ __device__ __forceinline__ uint64_t wave_sort_asc(uint64_t v, int n) {
   return v;
 }
 
-// Workgroup reductions. `sh` must hold NT/64 elements; every thread gets the
+// Workgroup reductions (every thread of the workgroup must call them, so each
+// wave is whole). `sh` must hold NT/64 elements; every thread gets the
 // result.  Each call ends with a barrier-protected read, so `sh` may be
 // reused by the next call after it returns (the leading barrier covers it).
 template <int NT, typename T>
 __device__ __forceinline__ T block_sum(T v, T* sh) {
   constexpr int NW = NT / DLM_WAVE;
-  v = wave_sum(v);
+  if constexpr (__is_integral(T)) v = wave_reduce(v, OpAdd{});  // exact: DPP
+  else v = wave_sum(v);  // floating point: the shuffle tree's fixed order
   const int w = threadIdx.x / DLM_WAVE, l = threadIdx.x % DLM_WAVE;
   __syncthreads();
   if (l == 0) sh[w] = v;
@@ -213,7 +208,7 @@ __device__ __forceinline__ T block_sum(T v, T* sh) {
 template <int NT>
 __device__ __forceinline__ float block_max(float v, float* sh) {
   constexpr int NW = NT / DLM_WAVE;
-  v = wave_max(v);
+  v = wave_reduce(v, OpMaxF{});
   const int w = threadIdx.x / DLM_WAVE, l = threadIdx.x % DLM_WAVE;
   __syncthreads();
   if (l == 0) sh[w] = v;
@@ -226,7 +221,7 @@ __device__ __forceinline__ float block_max(float v, float* sh) {
 template <int NT>
 __device__ __forceinline__ int block_min_i(int v, int* sh) {
   constexpr int NW = NT / DLM_WAVE;
-  v = wave_min_i(v);
+  v = wave_reduce(v, OpMinI{});
   const int w = threadIdx.x / DLM_WAVE, l = threadIdx.x % DLM_WAVE;
   __syncthreads();
   if (l == 0) sh[w] = v;
@@ -239,7 +234,7 @@ __device__ __forceinline__ int block_min_i(int v, int* sh) {
 template <int NT>
 __device__ __forceinline__ int block_max_i(int v, int* sh) {
   constexpr int NW = NT / DLM_WAVE;
-  v = wave_max_i(v);
+  v = wave_reduce(v, OpMaxI{});
   const int w = threadIdx.x / DLM_WAVE, l = threadIdx.x % DLM_WAVE;
   __syncthreads();
   if (l == 0) sh[w] = v;
