@@ -559,17 +559,28 @@ def main() -> int:
             run(i % R)
     torch.cuda.synchronize()
 
-    # the fused step's decisions against the individual calls' on replica 0
-    with torch.cuda.stream(sm):
-        step.step(0)
-    torch.cuda.synchronize()
-    calls_out = step.outputs()
+    # on replica 0: the fused step's decisions against the four rule calls run
+    # on the fused statistics (bitwise), and its statistics against the
+    # statistics call (argmax identical, floats to the last bits)
     with torch.cuda.stream(sm):
         step.fused(0)
     torch.cuda.synchronize()
     fused_out = step.outputs()
-    decisions_idx = (1, 5, 6, 7, 9, 10, 11, 12)     # argmax, every commit, count and length
-    fused_match = all(torch.equal(calls_out[i], fused_out[i]) for i in decisions_idx)
+    with torch.cuda.stream(sm):
+        for name in ("fastdllm", "depcap", "cap", "dapd"):
+            getattr(step, name)(0)
+    torch.cuda.synchronize()
+    rules_out = step.outputs()
+    decisions_idx = (5, 6, 7, 8, 9, 10, 11, 12)     # every commit, count, length and score
+    fused_match = all(torch.equal(rules_out[i], fused_out[i]) for i in decisions_idx)
+    with torch.cuda.stream(sm):
+        step.stats(0)
+    torch.cuda.synchronize()
+    calls_out = step.outputs()
+    fused_match = fused_match and torch.equal(calls_out[1], fused_out[1])
+    stats_diff = max(float((calls_out[i].view(torch.float32).double() -
+                            fused_out[i].view(torch.float32).double()).abs().max())
+                     for i in (0, 2, 3, 4))
 
     def timed_plain(fn):
         """K steps back to back on the launch stream, bracketed by events."""
@@ -667,7 +678,8 @@ def main() -> int:
         },
         "events_run_ms_per_step": round(events_ms, 5),
         "graph_replay_matches_eager": graph_ok,
-        "fused_decisions_match_calls": fused_match,
+        "fused_decisions_match_rule_calls": fused_match,
+        "fused_stats_max_abs_diff_vs_stats_call": stats_diff,
         "calls_events_run_ms_per_step": round(calls_events_ms, 5),
         "roofline": {
             "bound": "hbm", "kernel": dom_label,

@@ -1,7 +1,9 @@
 // fused.hip — dlm_decide_step: the small-batch decision step in three
 // launches, built from the same device code as the individual entry points
-// (stats_impl.h, rules_impl.h, cap_impl.h, dapd_impl.h), so its outputs are
-// bitwise theirs.
+// (stats_impl.h, rules_impl.h, cap_impl.h, dapd_impl.h).  The statistics run
+// with four 16-byte chunks per lane and segment (the statistics call uses
+// two), so they may differ from that call's in the last bits; every rule's
+// outputs are bitwise those of its entry point on these statistics.
 //
 //  launch 1  k_step_stream: workgroups [0, n_rows) each stream one row's
 //            statistics; the rest average one DAPD attention tile.  Both are
@@ -44,7 +46,10 @@ template <bool BF16, bool PREV, bool ABF16>
 __global__ __launch_bounds__(kStepNT) void k_step_stream(const StreamArgs a) {
   const int64_t g = blockIdx.x;
   if (g < a.n_rows) {
-    stats_block<kStepNT, BF16, PREV>(a.st, g, 0);
+    // four chunks per lane: beside the attention tiles a row needs more
+    // bytes in flight than the statistics call alone (measured: 30.0 against
+    // 31.2 us for this launch on the 256-row step; alone, two are faster)
+    stats_block<kStepNT, BF16, PREV, 4>(a.st, g, 0);
     return;
   }
   const int64_t t = g - a.n_rows;

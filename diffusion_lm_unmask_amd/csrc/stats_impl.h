@@ -406,11 +406,14 @@ __device__ __forceinline__ T ld_agent(T* a) {
 // chunks and publishes a Partial; the row's last-arriving workgroup (atomic
 // counter) merges the partials in split order — the same order whichever
 // workgroup arrives last — and resets the counter to zero.
-template <int NT, bool BF16, bool PREV>
+// UB: 16-byte chunks per lane per segment for bf16 rows (fp32 rows use 4).
+// More chunks keep more bytes in flight per workgroup at the cost of
+// registers; the value changes the summation order, not the definitions.
+template <int NT, bool BF16, bool PREV, int UB = DLM_STATS_U_BF16>
 __device__ __forceinline__ void stats_block(const StatsArgs& p, int64_t r, int s) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int VEC = 16 / ES;          // elements per 16-byte chunk
-  constexpr int U = BF16 ? DLM_STATS_U_BF16 : 4;  // chunks per lane per segment
+  constexpr int U = BF16 ? UB : 4;      // chunks per lane per segment
   __shared__ Shared<NT> sh;
 
   const int S = p.splits;

@@ -313,10 +313,12 @@ int dlm_fixed_block_eligible(const int32_t* masked_pos, const int32_t* seq_offse
  *   launch 2: Fast-dLLM, the DepCap boundary, CAP and the DAPD scores, each
  *             part in its own workgroups;
  *   launch 3: the DAPD selection.
- * Each part computes exactly what its own entry point computes: the outputs
- * are bitwise those of dlm_step_stats without a workspace (one workgroup
- * per row) followed by dlm_fastdllm_select, dlm_depcap_boundary,
- * dlm_cap_select and dlm_dapd_select on the same arguments.  A part is
+ * Each part computes what its own entry point computes.  The statistics are
+ * those of dlm_step_stats to its stated accuracy (argmax identical; the
+ * streaming order differs, so the floats may differ in the last bits), and
+ * the outputs of each rule are bitwise those of dlm_fastdllm_select,
+ * dlm_depcap_boundary, dlm_cap_select and dlm_dapd_select called on these
+ * statistics with the same arguments.  A part is
  * skipped when its output pointer below is NULL.  The statistics part is
  * required.  Rows are the statistics rows in seq_offsets order (the same
  * CSR for every part, n_rows = seq_offsets[n_seq] by the caller's contract).

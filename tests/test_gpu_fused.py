@@ -1,7 +1,9 @@
-"""GPU tests of dlm_decide_step (marked gpu): its outputs must be bitwise those
-of the individual entry points on the same inputs (statistics without a
-workspace, i.e. one workgroup per row), which the other GPU tests compare with
-the oracle; the statistics are also checked against the oracle here."""
+"""GPU tests of dlm_decide_step (marked gpu).  Its statistics are checked
+against the oracle and against dlm_step_stats (argmax identical, floats within
+1e-6 plus two ulps: the streaming launch reads wider segments per lane, so the summation
+order differs); every rule's outputs must be bitwise those of the rule's own
+entry point called on the fused statistics, which the other GPU tests compare
+with the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -14,9 +16,9 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _individual(cur, prev, so, ri, fast, depcap, cap, dapd, vocab=None):
-    g = api.step_stats(cur, prev, row_index=ri, vocab=vocab, split=False)
-    out = dict(g)
+def _individual(g, cur, so, ri, fast, depcap, cap, dapd, vocab=None):
+    """The rule entry points on the statistics g."""
+    out = {}
     if fast is not None:
         out["fast"] = api.fastdllm_select(g["conf"], so, fast["tau"], eligible=fast["eligible"])
     if depcap is not None:
@@ -47,10 +49,17 @@ def _same(a, b, name):
 def _check(cur, prev, so, ri, fast=None, depcap=None, cap=None, dapd=None, tag="", vocab=None):
     f = api.decide_step(cur, prev, so, row_index=ri, vocab=vocab, fast=fast, depcap=depcap,
                         cap=cap, dapd=dapd)
-    i = _individual(cur, prev, so, ri, fast, depcap, cap, dapd, vocab)
+    i = _individual(f, cur, so, ri, fast, depcap, cap, dapd, vocab)
+    g = api.step_stats(cur, prev, row_index=ri, vocab=vocab, split=False)
     torch.cuda.synchronize()
-    for k in ("conf", "argmax", "entropy", "kl", "lse"):
-        _same(f[k], i[k], f"{tag} {k}")
+    _same(f["argmax"], g["argmax"], f"{tag} argmax")
+    for k in ("conf", "entropy", "kl", "lse"):
+        if g[k] is None:
+            assert f[k] is None
+            continue
+        # 1e-6 absolute plus two fp32 ulps of the value (lse reaches ~20)
+        d = float(((f[k].double() - g[k].double()).abs() - 2.4e-7 * g[k].double().abs()).max())
+        assert d <= 1e-6, f"{tag} {k}: fused and the statistics call differ by {d:.2e}"
     for part in ("fast", "depcap", "cap", "dapd"):
         if part in i:
             for x, y in zip(f[part], i[part]):
