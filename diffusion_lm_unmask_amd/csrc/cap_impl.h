@@ -39,6 +39,7 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
     float tau_high, float gamma, int k_max, uint8_t* __restrict__ commit,
     int32_t* __restrict__ n_commit, int32_t* __restrict__ cand_out, float* __restrict__ dmat_out) {
   __shared__ uint64_t keys[kMaxRows];
+  __shared__ uint64_t top[kKM];       // the first k_max keys in order (runs path)
   __shared__ float rc[kMaxRows];      // by local row (pool rows only): conf
   __shared__ int32_t ry[kMaxRows];    // argmax
   __shared__ float rlse[kMaxRows];    // lse
@@ -103,20 +104,38 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
   }
   __syncthreads();
   const int P = npool;
+  const int K = min(P, k_max);
   int n2 = 1;
   while (n2 < P) n2 <<= 1;
+  const uint64_t* order = keys;  // the candidates' keys in order
   if (n2 <= DLM_WAVE) {
     if (tid < DLM_WAVE && P > 1) {  // one wave, in registers: lane l holds key l
       const uint64_t v = dlm::wave_sort_asc(tid < P ? keys[tid] : ~0ull, n2);
       if (tid < P) keys[tid] = v;
     }
     __syncthreads();
+  } else if (P <= kCapNT) {
+    // each wave sorts a run of 64 keys in registers; a key's rank is its lane
+    // plus binary searches in the other runs; ranks below k_max go to top
+    const int wv = tid / DLM_WAVE, ln = tid % DLM_WAVE;
+    const int n_runs = (P + DLM_WAVE - 1) / DLM_WAVE;
+    uint64_t v = ~0ull;
+    if (wv < n_runs) {  // whole waves
+      v = dlm::wave_sort_asc(tid < P ? keys[tid] : ~0ull, DLM_WAVE);
+      keys[tid] = v;  // run wv, sorted (a wave rewrites only its own run)
+    }
+    __syncthreads();
+    if (wv < n_runs && v != ~0ull) {
+      const int rank = ln + dlm::count_below_in_runs(keys, n_runs, wv, v);
+      if (rank < K) top[rank] = v;
+    }
+    __syncthreads();
+    order = top;
   } else {
     for (int i = P + tid; i < n2; i += kCapNT) keys[i] = ~0ull;
     __syncthreads();
     dlm::bitonic_sort<kCapNT>(keys, n2);
   }
-  const int K = min(P, k_max);
 
   if (K == 0) {  // 2. no candidate: top-1 eligible row
     const int top = dlm::block_argmax<kCapNT>(bidx == INT32_MAX ? NAN : best, bidx, shf, shi);
@@ -130,7 +149,7 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
   }
 
   for (int a = tid; a < K; a += kCapNT) {
-    const int r = static_cast<int>(keys[a] & 0xffffffffu);
+    const int r = static_cast<int>(order[a] & 0xffffffffu);
     crow[a] = lo + r;
     cconf[a] = rc[r];
     cy[a] = ry[r];
@@ -146,11 +165,12 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
   }
 
   // 3. gathers G[a][b] = log p_a(yhat_b), eight in flight per lane
+  constexpr int kGU = 8;
   const int KK = K * K;
-  for (int base = tid; base < KK; base += 8 * kCapNT) {
-    float v[8];
+  for (int base = tid; base < KK; base += kGU * kCapNT) {
+    float v[kGU];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kGU; ++u) {
       const int p = base + u * kCapNT;
       v[u] = 0.f;
       if (p < KK) {
@@ -159,7 +179,7 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
       }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kGU; ++u) {
       const int p = base + u * kCapNT;
       if (p < KK) {
         const int a = p / K, e = p - a * K;
@@ -169,17 +189,22 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
   }
   __syncthreads();
 
-  // conflict words: wave w handles candidates a = w, w + 4, ...
-  const int wv = tid / DLM_WAVE, ln = tid % DLM_WAVE;
-  for (int a = wv; a < K; a += kCapNT / DLM_WAVE) {
+  // conflict words: item (a, h, q) sets bits 16q .. 16q + 15 of word h of
+  // candidate a (e = 64h + 16q + i), stored as one 16-bit piece
+  for (int item = tid; item < K * 8; item += kCapNT) {
+    const int a = item >> 3, h = (item >> 2) & 1, q = item & 3;
+    const int e0 = h * DLM_WAVE + q * 16;
+    uint32_t piece = 0u;
+    if (e0 < K) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int e = h * DLM_WAVE + ln;
-      bool c = false;
-      if (e < K && e != a) c = (G[a][e] + G[e][a]) > gamma;
-      const uint64_t bits = __ballot(c);
-      if (ln == 0) cw[a][h] = bits;
+      for (int i = 0; i < 16; ++i) {
+        const int e = e0 + i;
+        const int ec = min(e, K - 1);  // read unconditionally: the 32 reads overlap
+        const float d = G[a][ec] + G[ec][a];
+        if (e < K && e != a && d > gamma) piece |= 1u << i;
+      }
     }
+    reinterpret_cast<uint16_t*>(&cw[a][h])[q] = static_cast<uint16_t>(piece);
   }
   if (dmat_out) {
     for (int idx = tid; idx < k_max * k_max; idx += kCapNT) {
@@ -209,7 +234,21 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
     }
     const uint64_t forced0 = __ballot(f0), forced1 = __ballot(f1);
     uint64_t s0 = 0, s1 = 0;
-    for (int a = 0; a < K; ++a) {
+    if (K <= DLM_WAVE) {
+      // in rounds: a candidate decides once every earlier candidate it
+      // conflicts with has decided (a forced one at once); it is taken when
+      // forced or when none of those was taken.  The lowest undecided
+      // candidate is always ready, and each decision is the scan's.
+      const uint64_t earlier = w00 & ((1ull << tid) - 1ull);
+      uint64_t open = K == DLM_WAVE ? ~0ull : (1ull << K) - 1ull;
+      while (open) {
+        const bool mine = (open >> tid) & 1ull;
+        const bool ready = mine && (f0 || (earlier & open) == 0ull);
+        s0 |= __ballot(ready && (f0 || (earlier & s0) == 0ull));
+        open &= ~__ballot(ready);
+      }
+    }
+    for (int a = K <= DLM_WAVE ? K : 0; a < K; ++a) {
       const int l = a & (DLM_WAVE - 1);
       const bool hi = a >= DLM_WAVE;
       const uint64_t c0 = dlm::rdlane64(hi ? w10 : w00, l);

@@ -437,32 +437,7 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
   }
   __syncthreads();
   if (wv < n_runs && v_sorted != ~0ull) {
-    int rank = ln;
-    for (int r0 = 0; r0 < n_runs; r0 += 4) {
-      // keys of run r below v_sorted, four runs side by side, without
-      // branches (a run that is this wave's own, or past the last, is
-      // searched as this wave's run and not counted)
-      const uint64_t* run[4];
-      bool use[4];
-      int c[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = r0 + q;
-        use[q] = r < n_runs && r != wv;
-        run[q] = keys + (use[q] ? r : wv) * 64;
-        c[q] = 0;
-      }
-#pragma unroll
-      for (int step = 32; step > 0; step >>= 1) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) c[q] += run[q][c[q] + step - 1] < v_sorted ? step : 0;
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        c[q] += run[q][c[q]] < v_sorted ? 1 : 0;  // c <= 63 before: 0..64 after
-        rank += use[q] ? c[q] : 0;
-      }
-    }
+    const int rank = ln + dlm::count_below_in_runs(keys, n_runs, wv, v_sorted);
     // a NaN key (it sorts after every finite key) is stored as -1 - node:
     // such a node is never chosen
     const int node = static_cast<int>(v_sorted & 0xffffffffu);

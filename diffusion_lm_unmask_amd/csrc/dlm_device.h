@@ -187,6 +187,38 @@ __device__ __forceinline__ uint64_t wave_sort_asc(uint64_t v, int n) {
   return v;
 }
 
+// Number of keys below v in the sorted runs of 64 keys at runs + 64 r,
+// r < n_runs, other than run `mine` (a key's own run gives its lane).  Four
+// runs are searched side by side, without branches (a run that is `mine`
+// or past the last is searched as run `mine` and not counted).
+__device__ __forceinline__ int count_below_in_runs(const uint64_t* runs, int n_runs, int mine,
+                                                   uint64_t v) {
+  int rank = 0;
+  for (int r0 = 0; r0 < n_runs; r0 += 4) {
+    const uint64_t* run[4];
+    bool use[4];
+    int c[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = r0 + q;
+      use[q] = r < n_runs && r != mine;
+      run[q] = runs + (use[q] ? r : mine) * DLM_WAVE;
+      c[q] = 0;
+    }
+#pragma unroll
+    for (int step = 32; step > 0; step >>= 1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) c[q] += run[q][c[q] + step - 1] < v ? step : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[q] += run[q][c[q]] < v ? 1 : 0;  // c <= 63 before: 0..64 after
+      rank += use[q] ? c[q] : 0;
+    }
+  }
+  return rank;
+}
+
 // Workgroup reductions (every thread of the workgroup must call them, so each
 // wave is whole). `sh` must hold NT/64 elements; every thread gets the
 // result.  Each call ends with a barrier-protected read, so `sh` may be
