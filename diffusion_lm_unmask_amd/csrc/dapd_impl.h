@@ -318,8 +318,9 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
   __shared__ uint64_t keys[kMaxM];         // by node, then sorted runs of 64
   __shared__ int16_t order[kMaxM];         // node of rank t (-1 - node: NaN key)
   __shared__ uint64_t chosen[kWords];
-  __shared__ uint64_t bmask[kWords];       // the greedy's current block, as a bitset
-  __shared__ uint8_t bpos[kMaxM];          // lane of each node of that block
+  __shared__ int16_t rank_of[kMaxM];       // rank of each node
+  __shared__ uint64_t bmk[kWords][kWords]; // block k (ranks 64k..64k+63): its nodes as a bitset
+  __shared__ uint64_t lmask[kMaxM];        // by rank: lanes of the earlier neighbours in its block
   __shared__ uint8_t has_edge[kMaxM];
   __shared__ int shi[kSelNT / DLM_WAVE];
   __shared__ float shf[kSelNT / DLM_WAVE];
@@ -376,6 +377,7 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
       bad_pos |= he >> 1;
     }
     if (tid < kWords) chosen[tid] = 0ull;
+    for (int e = tid; e < kWords * kWords; e += kSelNT) bmk[e / kWords][e % kWords] = 0ull;
   }
   const int flags = dlm::block_or_i<kSelNT>(bad_pos | (any_edge << 1), shi);  // ends with a barrier
   if (flags & 1) {
@@ -442,6 +444,28 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
     // such a node is never chosen
     const int node = static_cast<int>(v_sorted & 0xffffffffu);
     order[rank] = static_cast<int16_t>((v_sorted >> 32) == 0xffffffffull ? -1 - node : node);
+    rank_of[node] = static_cast<int16_t>(rank);
+    atomicOr(reinterpret_cast<unsigned long long*>(&bmk[rank >> 6][node >> 6]), 1ull << (node & 63));
+  }
+  __syncthreads();
+
+  // ---- each node's earlier neighbours inside its block of 64 ranks, as lane
+  // bits.  They do not depend on what earlier blocks chose, so every node is
+  // done at once here rather than inside the sequential greedy.
+  for (int v = tid; v < M; v += kSelNT) {
+    const int t = rank_of[v], k = t >> 6;
+    uint64_t loc = 0ull;
+    if (has_edge[v]) {
+      for (int w = 0; w < nw; ++w) {
+        uint64_t m = adj[v][w] & bmk[k][w];
+        while (m) {
+          const int ru = rank_of[w * 64 + __builtin_ctzll(m)];
+          m &= m - 1;
+          if (ru < t) loc |= 1ull << (ru & 63);
+        }
+      }
+    }
+    lmask[t] = loc;
   }
   __syncthreads();
 
@@ -450,9 +474,11 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
     for (int base = 0; base < M; base += 64) {
       const int t = base + ln;
       int v = -1;
+      uint64_t local = 0ull;  // earlier neighbours in this block (lane bits)
       if (t < M) {
         const int cand = order[t];
         if (cand >= 0) v = cand;  // NaN keys never chosen
+        local = lmask[t];
       }
       uint64_t sel;
       if (__ballot(v >= 0 && has_edge[v]) == 0ull) {
@@ -462,27 +488,6 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
         bool blocked = false;
         if (v >= 0)
           for (int w = 0; w < nw; ++w) blocked |= (adj[v][w] & chosen[w]) != 0ull;
-        // conflicts with earlier nodes of this block: bit q set when node q < ln
-        // is adjacent.  The block's nodes as a bitset (and each node's lane)
-        // let a lane visit only its actual neighbours inside the block.
-        if (ln < nw) bmask[ln] = 0ull;
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        if (v >= 0) {
-          atomicOr(reinterpret_cast<unsigned long long*>(&bmask[v >> 6]), 1ull << (v & 63));
-          bpos[v] = static_cast<uint8_t>(ln);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        uint64_t local = 0ull;
-        if (v >= 0) {
-          for (int w = 0; w < nw; ++w) {
-            uint64_t m = adj[v][w] & bmask[w];
-            while (m) {
-              const int q = bpos[w * 64 + __builtin_ctzll(m)];
-              m &= m - 1;
-              if (q < ln) local |= 1ull << q;
-            }
-          }
-        }
         const uint64_t cand = __ballot(v >= 0 && !blocked);
         if (__ballot(local != 0ull) == 0ull) {
           sel = cand;  // no conflicts inside the block
