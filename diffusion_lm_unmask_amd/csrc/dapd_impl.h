@@ -50,10 +50,10 @@ namespace {
 #define DLM_DAPD_UNR_BF16 5
 #endif
 constexpr int kGroups = DLM_DAPD_GROUPS;  // map groups per workgroup
-constexpr int kItems = 32;           // (row, chunk) items per workgroup
-constexpr int kAvgNT = kGroups * kItems;
+constexpr int kAvgNT = 512;
+constexpr int kItems = kAvgNT / kGroups;  // (row, 8-column chunk) items per workgroup
 constexpr int kTileRows = 1;
-constexpr int kTileChunks = kItems / kTileRows;  // 32 chunks of 8 columns = 256 columns
+constexpr int kTileChunks = kItems / kTileRows;  // 8-column chunks per tile
 constexpr int kSelNT = 1024;
 constexpr int kMaxM = DLM_MAX_SEQ_ROWS;
 constexpr int kWords = kMaxM / 64;
@@ -80,7 +80,10 @@ __device__ __forceinline__ float ld1(const void* base, int64_t idx) {
   return static_cast<const float*>(base)[idx];
 }
 
-template <bool BF16>
+// UNR_BF16: bf16 maps a lane keeps in flight.  It changes no summation
+// order (each lane adds its maps in map order), only how hard one tile
+// presses on the memory system.
+template <bool BF16, int UNR_BF16 = DLM_DAPD_UNR_BF16>
 __device__ __forceinline__ void dapd_avg_tile(int b, int tile, const void* __restrict__ attn,
     int n_lh, int64_t S, int64_t batch_stride, const int32_t* __restrict__ masked_pos,
     const int32_t* __restrict__ seq_offsets, int m_max, int n_tc, int vec_ok,
@@ -119,7 +122,7 @@ __device__ __forceinline__ void dapd_avg_tile(int b, int tile, const void* __res
     const int64_t map_stride = S * S;
     if (contig) {
       // UNR maps per lane in flight, then summed in map order
-      constexpr int UNR = BF16 ? DLM_DAPD_UNR_BF16 : 2;
+      constexpr int UNR = BF16 ? UNR_BF16 : 2;
       for (int lh0 = g; lh0 < n_lh; lh0 += kGroups * UNR) {
         uint4 q[UNR][BF16 ? 1 : 2];
 #pragma unroll

@@ -23,6 +23,20 @@
 #include "rules_impl.h"
 #include "stats_impl.h"
 
+// Launch 1's balance between a compute unit's statistics row and its
+// attention tile (same-process A/B on the 256-row step, launch 1 alone):
+// four 16-byte chunks per lane for the row (two: 31.2 us, three: 30.7, four:
+// 30.0; five and more exceed the registers for two workgroups per compute
+// unit) and two maps in flight per lane for the tile (five: 30.0 us, two:
+// 28.9, one: 29.3).  A tile that streams less greedily leaves the row more of
+// the compute unit's bandwidth, and the row is the long pole.
+#ifndef DLM_STEP_STATS_U
+#define DLM_STEP_STATS_U 4
+#endif
+#ifndef DLM_STEP_TILE_UNR
+#define DLM_STEP_TILE_UNR 2
+#endif
+
 namespace {
 
 constexpr int kStepNT = 512;
@@ -46,16 +60,13 @@ template <bool BF16, bool PREV, bool ABF16>
 __global__ __launch_bounds__(kStepNT) void k_step_stream(const StreamArgs a) {
   const int64_t g = blockIdx.x;
   if (g < a.n_rows) {
-    // four chunks per lane: beside the attention tiles a row needs more
-    // bytes in flight than the statistics call alone (measured: 30.0 against
-    // 31.2 us for this launch on the 256-row step; alone, two are faster)
-    stats_block<kStepNT, BF16, PREV, 4>(a.st, g, 0);
+    stats_block<kStepNT, BF16, PREV, DLM_STEP_STATS_U>(a.st, g, 0);
     return;
   }
   const int64_t t = g - a.n_rows;
-  dapd_avg_tile<ABF16>(static_cast<int>(t / a.tiles_per_seq), static_cast<int>(t % a.tiles_per_seq),
-                       a.attn, a.n_lh, a.S, a.batch_stride, a.masked_pos, a.seq_offsets, a.m_max,
-                       a.n_tc, a.vec_ok, a.ws_a, a.P);
+  dapd_avg_tile<ABF16, DLM_STEP_TILE_UNR>(
+      static_cast<int>(t / a.tiles_per_seq), static_cast<int>(t % a.tiles_per_seq), a.attn, a.n_lh,
+      a.S, a.batch_stride, a.masked_pos, a.seq_offsets, a.m_max, a.n_tc, a.vec_ok, a.ws_a, a.P);
 }
 
 struct RulesArgs {
