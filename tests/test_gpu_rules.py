@@ -232,6 +232,26 @@ def test_cap_stress_sampled_sequences():
         print(f"[cap] stress seq {b}: pool {n_pool}, committed {int(out['n_commit'][b])}")
 
 
+@pytest.mark.parametrize("k_max", [64, 128])
+def test_cap_pool_sizes_around_the_ordering_paths(k_max):
+    # one 1024-row sequence; tau_low set at the P-th largest confidence gives a
+    # pool of exactly P rows: up to 64 (one wave sorts), 65-256 (per-wave runs
+    # and rank searches), above 256 (the LDS sort); k_max 64 takes the greedy
+    # in rounds, 128 the candidate-order scan
+    cur, prev, so, ri, g, o = _stats("stress", batch=1)
+    R = dict(synth.RULES["stress"], k_max=k_max)
+    conf = np.sort(f64(g["conf"]))[::-1]
+    done = 0
+    for P in (1, 63, 64, 65, 128, 129, 255, 256, 257, 700):
+        if not conf[P - 1] > conf[P]:
+            continue                                   # a tie at the cut: pool size not exact
+        tl = float(conf[P - 1])
+        out = _cap_case(cur, ri, so, g, o, dict(R, tau_low=tl), None, f"pool {P} k_max {k_max}")
+        assert int(host(out["n_commit"])[0]) >= 1
+        done += 1
+    assert done >= 8
+
+
 def test_cap_edges():
     V = 64
     x = torch.randn(6, V, device=DEV).to(torch.bfloat16)
@@ -326,6 +346,21 @@ def test_dapd_scattered_positions_and_edges():
     # a sequence longer than m_max is reported
     out = api.dapd_select(attn, pos, so, g["conf"], 0.01, m_max=30)
     assert host(out["n_commit"]).tolist() == [-1, -1, -1]
+
+
+def test_dapd_ragged_blocks_with_edges():
+    # 150 and 90 nodes: the greedy's last block of 64 ranks is partial, and
+    # nodes are blocked both inside their block and by earlier blocks
+    cur, prev, so, ri, g, o = _stats("llada", "cov")
+    pos, offs = synth.gen_positions("llada", DEV)
+    attn = synth.attention("llada", DEV, batch=1, variant="cov", masked_pos=pos)
+    so2 = torch.tensor([0, 150], device=DEV, dtype=torch.int32)
+    out = _dapd_case(attn, pos[:150].contiguous(), so2, g["conf"][:150].contiguous(),
+                     o["conf"][:150], 0.01, 150, "150 nodes")
+    assert int(host(out["n_commit"])[0]) < 150
+    so3 = torch.tensor([0, 90], device=DEV, dtype=torch.int32)
+    _dapd_case(attn, pos[100:190].contiguous(), so3, g["conf"][100:190].contiguous(),
+               o["conf"][100:190], 0.01, 256, "90 nodes, m_max 256")
 
 
 def test_cap_reports_out_of_range_argmax():
