@@ -359,6 +359,59 @@ __device__ __forceinline__ Partial merge(int n, Get get) {
   return t;
 }
 
+template <int J>
+__device__ __forceinline__ double xor_lane_d(double v) {
+  return __longlong_as_double(static_cast<long long>(
+      dlm::xor_lane64<J>(static_cast<uint64_t>(__double_as_longlong(v)))));
+}
+
+// Merge the NW per-wave records on one wave (lane k < NW holds record k)
+// with a fixed butterfly over lane distances 1, 2, 4, ...: the max, the
+// lowest index holding it, and the sums moved to the max's integer
+// reference.  Every lane ends with the same total.  Call with the whole wave.
+template <int NW, bool PREV>
+__device__ __forceinline__ Partial merge_lanes(Partial q) {
+  const int l = threadIdx.x % DLM_WAVE;
+  const bool real = l < NW;
+  float m = real ? q.m : kLow;
+  if constexpr (NW > 1) m = fmaxf(m, __int_as_float(dlm::xor_lane<1>(__float_as_int(m))));
+  if constexpr (NW > 2) m = fmaxf(m, __int_as_float(dlm::xor_lane<2>(__float_as_int(m))));
+  if constexpr (NW > 4) m = fmaxf(m, __int_as_float(dlm::xor_lane<4>(__float_as_int(m))));
+  if constexpr (NW > 8) m = fmaxf(m, __int_as_float(dlm::xor_lane<8>(__float_as_int(m))));
+  Partial t;
+  t.m = m;
+  t.h = ceilf(m * kL2E);
+  double Z = 0.0, A = 0.0, B = 0.0, Z2 = 0.0;
+  int cand = INT32_MAX;
+  if (real) {
+    Z = q.Z;
+    A = q.A;
+    B = q.B;
+    Z2 = q.Z2;
+    rebase(Z, A, B, Z2, q.h, t.h);
+    if (q.m == m) cand = q.cand;
+  }
+#define DLM_MERGE_STEP(J)                                                 \
+  Z += xor_lane_d<J>(Z);                                                  \
+  A += xor_lane_d<J>(A);                                                  \
+  if constexpr (PREV) {                                                   \
+    B += xor_lane_d<J>(B);                                                \
+    Z2 += xor_lane_d<J>(Z2);                                              \
+  }                                                                       \
+  cand = min(cand, dlm::xor_lane<J>(cand));
+  if constexpr (NW > 1) { DLM_MERGE_STEP(1) }
+  if constexpr (NW > 2) { DLM_MERGE_STEP(2) }
+  if constexpr (NW > 4) { DLM_MERGE_STEP(4) }
+  if constexpr (NW > 8) { DLM_MERGE_STEP(8) }
+#undef DLM_MERGE_STEP
+  t.Z = Z;
+  t.A = A;
+  t.B = PREV ? B : 0.0;
+  t.Z2 = PREV ? Z2 : 0.0;
+  t.cand = cand;
+  return t;
+}
+
 // log2 of a positive finite double: exact exponent plus an fp32 log2 of the
 // mantissa in [0.5, 1) (absolute error about 1e-7).
 __device__ __forceinline__ double log2_split(double v) {
@@ -537,15 +590,19 @@ __device__ __forceinline__ void stats_block(const StatsArgs& p, int64_t r, int s
       w.B = w.Z2 = 0.0;
     }
   }
-  // ---- workgroup merge: one record per wave, one barrier, thread 0 merges
+  // ---- workgroup merge: one record per wave, one barrier, wave 0 merges
+  // the records across its lanes and thread 0 finalizes
   if (tid % DLM_WAVE == 0) sh.rec[tid / DLM_WAVE] = w;
   __syncthreads();
+  Partial t;
+  if (tid < DLM_WAVE) {
+    Partial q{};
+    if (tid < NT / DLM_WAVE) q = sh.rec[tid];
+    t = merge_lanes<NT / DLM_WAVE, PREV>(q);
+  }
 
   if (S == 1) {
-    if (tid == 0) {
-      const Partial t = merge<PREV>(NT / DLM_WAVE, [&](int k) { return sh.rec[k]; });
-      sh.flag = finalize<PREV>(p, r, t);
-    }
+    if (tid == 0) sh.flag = finalize<PREV>(p, r, t);
     __syncthreads();
     if (!sh.flag)
       careful_row<NT, BF16, PREV>(cur, prv, V, sh, r, p.conf, p.argmax, p.ent, p.kl, p.lse);
@@ -554,7 +611,6 @@ __device__ __forceinline__ void stats_block(const StatsArgs& p, int64_t r, int s
 
   // ---- publish this split; the last workgroup of the row merges
   if (tid == 0) {
-    const Partial t = merge<PREV>(NT / DLM_WAVE, [&](int k) { return sh.rec[k]; });
     Partial* mine = p.parts + r * S + s;
     st_agent(&mine->Z, t.Z);
     st_agent(&mine->A, t.A);
@@ -572,7 +628,7 @@ __device__ __forceinline__ void stats_block(const StatsArgs& p, int64_t r, int s
   if (tid == 0) {
     __threadfence();  // acquire the other splits' partials
     Partial* row = p.parts + r * S;
-    const Partial t = merge<PREV>(S, [&](int k) {  // split order: deterministic
+    const Partial u = merge<PREV>(S, [&](int k) {  // split order: deterministic
       Partial q;
       q.Z = ld_agent(&row[k].Z);
       q.A = ld_agent(&row[k].A);
@@ -584,7 +640,7 @@ __device__ __forceinline__ void stats_block(const StatsArgs& p, int64_t r, int s
       return q;
     });
     st_agent(p.counters + r, 0);  // ready for the next call
-    sh.flag = finalize<PREV>(p, r, t);
+    sh.flag = finalize<PREV>(p, r, u);
   }
   __syncthreads();
   if (!sh.flag)
