@@ -75,9 +75,11 @@ def measured_traffic(kernel: str):
 class TimingEvents:
     """Pairs of HIP timing events created without the system-scope fence
     (hipEventDisableSystemFence), so that recording one adds no cache
-    write-back to the interval it brackets; recorded on the launch stream.
-    They come from the HIP runtime already loaded into the process (torch's),
-    so they are valid on torch's streams."""
+    write-back to the interval it brackets.  The fused step hands them to its
+    streaming launch, which sets them to the kernel's start and end; the
+    five-call step records them on the launch stream around the statistics
+    call.  They come from the HIP runtime already loaded into the process
+    (torch's), so they are valid on torch's streams."""
 
     NO_SYSTEM_FENCE = 0x20000000
 
@@ -532,9 +534,9 @@ def main() -> int:
     torch.cuda.synchronize()
 
     def timed_eager(n_steps, fused):
-        """Eager run of n_steps steps with HIP events around the dominant
-        launch of each step (the fused streaming launch, else the statistics
-        call), on the launch stream."""
+        """Eager run of n_steps steps with HIP events on the dominant launch
+        of each step (set by the fused streaming launch itself, else recorded
+        around the statistics call), on the launch stream."""
         events = TimingEvents(n_steps)
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -621,9 +623,10 @@ def main() -> int:
         ms_per_step = timed_plain(lambda r: graphs[r].replay())
     else:
         ms_per_step = timed_plain(run)
-    # the dominant kernel's live duration: fence-free HIP events recorded on
-    # its launch stream right around it, over a second run of the same steps
-    # (kept out of the timed run: each record adds a little to the step)
+    # the dominant kernel's live duration over a second run of the same steps:
+    # HIP events on its launch stream, which the fused step's launch sets to
+    # the kernel's own start and end (the five-call step records them around
+    # the statistics call instead)
     events_ms, dom_us = timed_eager(args.steps, fused)
     # the statistics call on its own (the five calls, eager), for reference
     calls_events_ms, stats_us = timed_eager(args.steps, False)

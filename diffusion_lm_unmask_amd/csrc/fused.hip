@@ -17,6 +17,8 @@
 //
 // No part waits for another inside a launch: the dependencies (statistics
 // before the rules, scores before the greedy) are the launch boundaries.
+#include <hip/hip_ext.h>
+
 #include "cap_impl.h"
 #include "checks.h"
 #include "dapd_impl.h"
@@ -148,12 +150,21 @@ __global__ __launch_bounds__(kSelNT) void k_step_select(const SelectArgs a) {
                   a.commit, a.n_commit, nullptr, nullptr, nullptr, a.P);
 }
 
-template <bool BF16, bool PREV>
-void launch_stream(bool abf16, dim3 grid, hipStream_t s, const StreamArgs& a) {
-  if (abf16)
-    hipLaunchKernelGGL((k_step_stream<BF16, PREV, true>), grid, dim3(kStepNT), 0, s, a);
+// With events, the launch itself sets them to the kernel's start and end
+// (hipExtLaunchKernel), so they time the kernel and not the queue around it.
+template <bool BF16, bool PREV, bool ABF16>
+void launch_stream_k(dim3 grid, hipStream_t s, const StreamArgs& a, hipEvent_t e0, hipEvent_t e1) {
+  if (e0 || e1)
+    hipExtLaunchKernelGGL((k_step_stream<BF16, PREV, ABF16>), grid, dim3(kStepNT), 0, s, e0, e1,
+                          0, a);
   else
-    hipLaunchKernelGGL((k_step_stream<BF16, PREV, false>), grid, dim3(kStepNT), 0, s, a);
+    hipLaunchKernelGGL((k_step_stream<BF16, PREV, ABF16>), grid, dim3(kStepNT), 0, s, a);
+}
+template <bool BF16, bool PREV>
+void launch_stream(bool abf16, dim3 grid, hipStream_t s, const StreamArgs& a, hipEvent_t e0,
+                   hipEvent_t e1) {
+  if (abf16) launch_stream_k<BF16, PREV, true>(grid, s, a, e0, e1);
+  else launch_stream_k<BF16, PREV, false>(grid, s, a, e0, e1);
 }
 
 }  // namespace
@@ -224,20 +235,16 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
   if (g1 > 2147483647LL) return DLM_ERR_UNSUPPORTED;
   const dim3 grid1(static_cast<unsigned>(g1));
   const bool abf16 = !dapd || d->attn_dtype == DLM_BF16;
-  if (d->launch1_begin_event &&
-      hipEventRecord(static_cast<hipEvent_t>(d->launch1_begin_event), s) != hipSuccess)
-    return DLM_ERR_HIP;
+  const hipEvent_t e0 = static_cast<hipEvent_t>(d->launch1_begin_event);
+  const hipEvent_t e1 = static_cast<hipEvent_t>(d->launch1_end_event);
   if (bf16) {
-    if (prev) launch_stream<true, true>(abf16, grid1, s, sa);
-    else launch_stream<true, false>(abf16, grid1, s, sa);
+    if (prev) launch_stream<true, true>(abf16, grid1, s, sa, e0, e1);
+    else launch_stream<true, false>(abf16, grid1, s, sa, e0, e1);
   } else {
-    if (prev) launch_stream<false, true>(abf16, grid1, s, sa);
-    else launch_stream<false, false>(abf16, grid1, s, sa);
+    if (prev) launch_stream<false, true>(abf16, grid1, s, sa, e0, e1);
+    else launch_stream<false, false>(abf16, grid1, s, sa, e0, e1);
   }
   DLM_CHECK_LAUNCH();
-  if (d->launch1_end_event &&
-      hipEventRecord(static_cast<hipEvent_t>(d->launch1_end_event), s) != hipSuccess)
-    return DLM_ERR_HIP;
 
   // ---- launch 2: the per-sequence rules and the DAPD scores
   RulesArgs ra{};

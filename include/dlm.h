@@ -369,10 +369,9 @@ typedef struct dlm_step_desc {
   int32_t* dapd_n_commit;
   void* dapd_workspace;
   size_t dapd_workspace_bytes;
-  /* optional hipEvent_t handles recorded on `stream` right before and right
-   * after launch 1, to time it (events created with hipEventDisableSystemFence
-   * add no cache write-back to the interval); NULL: not recorded.  A failed
-   * record returns DLM_ERR_HIP. */
+  /* optional hipEvent_t handles (created, timing enabled) that launch 1 sets
+   * to its own start and end (hipExtLaunchKernel's start and stop events), to
+   * time it; NULL: not set.  A failed launch returns DLM_ERR_HIP. */
   void* launch1_begin_event;
   void* launch1_end_event;
 } dlm_step_desc;
