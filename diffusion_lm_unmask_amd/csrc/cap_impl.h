@@ -189,9 +189,25 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
   }
   __syncthreads();
 
-  // conflict words: item (a, h, q) sets bits 16q .. 16q + 15 of word h of
-  // candidate a (e = 64h + 16q + i), stored as one 16-bit piece
-  for (int item = tid; item < K * 8; item += kCapNT) {
+  // conflict words.  Up to 32 candidates: wave w builds the words of
+  // candidates w, w + 4, ... with one ballot per word (lane e tests pair
+  // (a, e)).  More: item (a, h, q) sets bits 16q .. 16q + 15 of word h of
+  // candidate a (e = 64h + 16q + i), stored as one 16-bit piece, which keeps
+  // more reads in flight (measured: 0.5 against 0.9 us at K = 32, 2.8
+  // against 1.7 us at K = 64).
+  if (K <= 32) {
+    const int wv = tid / DLM_WAVE, ln = tid % DLM_WAVE;
+    for (int a = wv; a < K; a += kCapNT / DLM_WAVE) {
+      bool c = false;
+      if (ln < K && ln != a) c = (G[a][ln] + G[ln][a]) > gamma;
+      const uint64_t bits = __ballot(c);
+      if (ln == 0) {
+        cw[a][0] = bits;
+        cw[a][1] = 0ull;
+      }
+    }
+  }
+  for (int item = tid; K > 32 && item < K * 8; item += kCapNT) {
     const int a = item >> 3, h = (item >> 2) & 1, q = item & 3;
     const int e0 = h * DLM_WAVE + q * 16;
     uint32_t piece = 0u;
