@@ -3,8 +3,9 @@
 //
 // One workgroup per sequence:
 //   1. pool = eligible rows with conf >= tau_low, as 64-bit keys
-//      (conf descending, row ascending) in LDS, sorted (one wave in registers
-//      up to 64 keys, else the LDS bitonic sort).  Each row's argmax, lse and
+//      (conf descending, row ascending) in LDS, ordered (one wave in
+//      registers up to 64 keys; else runs of 64 sorted in registers and
+//      ranked by binary search, keeping the first k_max).  Each row's argmax, lse and
 //      row offset are read in the same pass as its confidence, so the
 //      candidates need no second dependent trip to memory;
 //   2. the first k_max become candidates; empty pool -> top-1 eligible row;
@@ -114,27 +115,11 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
       if (tid < P) keys[tid] = v;
     }
     __syncthreads();
-  } else if (P <= kCapNT) {
-    // each wave sorts a run of 64 keys in registers; a key's rank is its lane
-    // plus binary searches in the other runs; ranks below k_max go to top
-    const int wv = tid / DLM_WAVE, ln = tid % DLM_WAVE;
-    const int n_runs = (P + DLM_WAVE - 1) / DLM_WAVE;
-    uint64_t v = ~0ull;
-    if (wv < n_runs) {  // whole waves
-      v = dlm::wave_sort_asc(tid < P ? keys[tid] : ~0ull, DLM_WAVE);
-      keys[tid] = v;  // run wv, sorted (a wave rewrites only its own run)
-    }
-    __syncthreads();
-    if (wv < n_runs && v != ~0ull) {
-      const int rank = ln + dlm::count_below_in_runs(keys, n_runs, wv, v);
-      if (rank < K) top[rank] = v;
-    }
-    __syncthreads();
-    order = top;
   } else {
-    for (int i = P + tid; i < n2; i += kCapNT) keys[i] = ~0ull;
-    __syncthreads();
-    dlm::bitonic_sort<kCapNT>(keys, n2);
+    // runs of 64 keys sorted in registers, ranks by binary search; only the
+    // k_max first ranks are kept, in top
+    dlm::sort_runs<kCapNT>(keys, top, P, K);
+    order = top;
   }
 
   if (K == 0) {  // 2. no candidate: top-1 eligible row
@@ -232,15 +217,18 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
   }
   __syncthreads();
 
-  // 4. greedy pick on wave 0: lane l holds the conflict words of candidates
-  // l and l + 64, and the scan reads them with readlane (no memory trip per
-  // step).  s0 / s1 are the chosen candidates as a bitset.
+  // 4. greedy on wave 0, in rounds: lane l holds candidates l and l + 64
+  // (their conflict words and forced flags, conf > tau_high).  A candidate
+  // decides once every earlier candidate it conflicts with has decided (a
+  // forced one at once), and is taken when forced or when none of those was
+  // taken.  The lowest undecided candidate is always ready, and each
+  // decision is the candidate-order scan's.  s0 / s1: chosen candidates
+  // 0..63 / 64..127 as bitsets.
   if (tid < DLM_WAVE) {
-    uint64_t w00 = 0, w01 = 0, w10 = 0, w11 = 0;
-    bool f0 = false, f1 = false;  // forced: conf > tau_high
+    uint64_t w00 = 0, w10 = 0, w11 = 0;
+    bool f0 = false, f1 = false;
     if (tid < K) {
       w00 = cw[tid][0];
-      w01 = cw[tid][1];
       f0 = cconf[tid] > tau_high;
     }
     if (tid + DLM_WAVE < K) {
@@ -248,32 +236,27 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
       w11 = cw[tid + DLM_WAVE][1];
       f1 = cconf[tid + DLM_WAVE] > tau_high;
     }
-    const uint64_t forced0 = __ballot(f0), forced1 = __ballot(f1);
+    const uint64_t below = (1ull << tid) - 1ull;
+    const uint64_t e0 = w00 & below;  // candidate l: earlier conflicts (all in word 0)
+    const uint64_t e1 = w11 & below;  // candidate 64 + l: earlier conflicts in word 1 (plus w10)
+    uint64_t open0 = K >= DLM_WAVE ? ~0ull : (1ull << K) - 1ull;
+    uint64_t open1 = K <= DLM_WAVE ? 0ull : (K >= 2 * DLM_WAVE ? ~0ull : (1ull << (K - DLM_WAVE)) - 1ull);
     uint64_t s0 = 0, s1 = 0;
-    if (K <= DLM_WAVE) {
-      // in rounds: a candidate decides once every earlier candidate it
-      // conflicts with has decided (a forced one at once); it is taken when
-      // forced or when none of those was taken.  The lowest undecided
-      // candidate is always ready, and each decision is the scan's.
-      const uint64_t earlier = w00 & ((1ull << tid) - 1ull);
-      uint64_t open = K == DLM_WAVE ? ~0ull : (1ull << K) - 1ull;
-      while (open) {
-        const bool mine = (open >> tid) & 1ull;
-        const bool ready = mine && (f0 || (earlier & open) == 0ull);
-        s0 |= __ballot(ready && (f0 || (earlier & s0) == 0ull));
-        open &= ~__ballot(ready);
-      }
+    while (K <= DLM_WAVE && open0) {  // one word: half the ballots per round
+      const bool r0 = ((open0 >> tid) & 1ull) && (f0 || (e0 & open0) == 0ull);
+      s0 |= __ballot(r0 && (f0 || (e0 & s0) == 0ull));
+      open0 &= ~__ballot(r0);
     }
-    for (int a = K <= DLM_WAVE ? K : 0; a < K; ++a) {
-      const int l = a & (DLM_WAVE - 1);
-      const bool hi = a >= DLM_WAVE;
-      const uint64_t c0 = dlm::rdlane64(hi ? w10 : w00, l);
-      const uint64_t c1 = dlm::rdlane64(hi ? w11 : w01, l);
-      const bool forced = (((hi ? forced1 : forced0) >> l) & 1ull) != 0;
-      if (forced || ((c0 & s0) == 0 && (c1 & s1) == 0)) {
-        if (hi) s1 |= 1ull << l;
-        else s0 |= 1ull << l;
-      }
+    while (open0 | open1) {
+      const bool r0 = ((open0 >> tid) & 1ull) && (f0 || (e0 & open0) == 0ull);
+      const bool r1 = ((open1 >> tid) & 1ull) &&
+                      (f1 || ((w10 & open0) == 0ull && (e1 & open1) == 0ull));
+      const bool t0 = r0 && (f0 || (e0 & s0) == 0ull);
+      const bool t1 = r1 && (f1 || ((w10 & s0) == 0ull && (e1 & s1) == 0ull));
+      s0 |= __ballot(t0);
+      s1 |= __ballot(t1);
+      open0 &= ~__ballot(r0);
+      open1 &= ~__ballot(r1);
     }
     if ((s0 >> tid) & 1ull) {
       const int lr = crow[tid] - lo;

@@ -1,6 +1,7 @@
 // dlm_device.h — small device helpers shared by the library's kernels:
 // bf16 unpacking, 64-wide wavefront reductions (shuffle and DPP), sort keys,
-// an LDS bitonic sort and workgroup reductions.
+// register sorts of 64-key runs with rank placement, and workgroup
+// reductions.
 // gfx950 only (wave64).
 #pragma once
 #include <hip/hip_runtime.h>
@@ -94,27 +95,6 @@ __device__ __forceinline__ uint32_t desc_bits(float f) {
   const uint32_t u = f == 0.f ? 0u : __float_as_uint(f);
   const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ~asc;
-}
-
-// Bitonic sort of n (a power of two) 64-bit keys in LDS, ascending; every
-// thread of the NT-thread workgroup must call it.
-template <int NT>
-__device__ void bitonic_sort(uint64_t* keys, int n) {
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int t = threadIdx.x; t < n / 2; t += NT) {
-        const int i = 2 * j * (t / j) + (t % j);
-        const int p = i + j;
-        const bool up = (i & k) == 0;
-        const uint64_t a = keys[i], b = keys[p];
-        if ((a > b) == up) {
-          keys[i] = b;
-          keys[p] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
 }
 
 // The value of lane (l xor J) for every lane l.  Inside a row of 16 lanes
@@ -217,6 +197,46 @@ __device__ __forceinline__ int count_below_in_runs(const uint64_t* runs, int n_r
     }
   }
   return rank;
+}
+
+// Sorts the first n (<= 1024) keys of `keys` (LDS) ascending: wave w of the
+// NT-thread workgroup sorts the runs of 64 keys w, w + NT/64, ... in
+// registers and writes them back in place (a wave touches only its own
+// runs); then every key of rank below `limit` is stored at out[rank], its
+// rank being its lane plus the keys below it in the other runs.  Keys must be
+// unique; slots n .. 64*ceil(n/64) - 1 of `keys` are overwritten with ~0.
+// Every thread of the workgroup must call it (it contains two barriers).
+template <int NT>
+__device__ __forceinline__ void sort_runs(uint64_t* keys, uint64_t* out, int n, int limit) {
+  constexpr int NW = NT / DLM_WAVE;
+  constexpr int kRunsPerWave = (1024 / DLM_WAVE + NW - 1) / NW;
+  const int wv = threadIdx.x / DLM_WAVE, ln = threadIdx.x % DLM_WAVE;
+  const int n_runs = (n + DLM_WAVE - 1) / DLM_WAVE;
+  uint64_t v[kRunsPerWave];
+#pragma unroll
+  for (int q = 0; q < kRunsPerWave; ++q) {
+    const int r = wv + q * NW;
+    v[q] = ~0ull;
+    if (r < n_runs) {  // wave-uniform: whole waves sort
+      const int i = r * DLM_WAVE + ln;
+      v[q] = wave_sort_asc(i < n ? keys[i] : ~0ull, DLM_WAVE);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kRunsPerWave; ++q) {
+    const int r = wv + q * NW;
+    if (r < n_runs) keys[r * DLM_WAVE + ln] = v[q];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kRunsPerWave; ++q) {
+    const int r = wv + q * NW;
+    if (r < n_runs && v[q] != ~0ull) {
+      const int rank = ln + count_below_in_runs(keys, n_runs, r, v[q]);
+      if (rank < limit) out[rank] = v[q];
+    }
+  }
+  __syncthreads();
 }
 
 // Workgroup reductions (every thread of the workgroup must call them, so each

@@ -14,8 +14,9 @@
 // k_rank_select: one workgroup (256 threads) per sequence.  The eligible
 // non-NaN rows are keyed (confidence descending, row ascending), gathered
 // into LDS (slot order is irrelevant: the sort decides) and sorted: up to 64
-// keys by one wave in registers (shuffle bitonic network, no barriers), more
-// with the LDS bitonic sort.  Position t of the sorted keys is the row of rank
+// keys by one wave in registers (bitonic network, no barriers); more as runs
+// of 64 sorted in registers, each key placed at its rank (its lane plus
+// binary searches in the other runs).  Position t of the sorted keys is the row of rank
 // t.  Top-K takes positions < K; factor decoding tests (t+2)(1 - c) < f at
 // every position and takes the largest admissible one (a max reduction, so
 // it equals "the largest n" for any input, monotone or not).  The test runs
@@ -37,7 +38,8 @@ __global__ __launch_bounds__(kRankNT) void k_rank_select(
     const float* __restrict__ conf, const uint8_t* __restrict__ eligible,
     const int32_t* __restrict__ seq_offsets, int k, float f, uint8_t* __restrict__ commit,
     int32_t* __restrict__ n_commit, uint8_t* __restrict__ certificate) {
-  __shared__ uint64_t keys[kRankMax];  // candidates' (desc conf, row), then ~0 padding
+  __shared__ uint64_t keys[kRankMax];  // candidates' (desc conf, row), then sorted runs
+  __shared__ uint64_t sorted[kRankMax];  // keys in order (more than 64 keys)
   __shared__ float cs[kRankMax];       // confidence by row
   __shared__ uint8_t take[kRankMax];   // selected, by row
   __shared__ int shi[kRankNT / DLM_WAVE];
@@ -68,16 +70,16 @@ __global__ __launch_bounds__(kRankNT) void k_rank_select(
   const int n_ok = cnt;
   int n2 = 1;
   while (n2 < n_ok) n2 <<= 1;
-  for (int s = n_ok + tid; s < n2; s += kRankNT) keys[s] = ~0ull;
-  __syncthreads();
+  const uint64_t* order = keys;  // position t holds the key of rank t
   if (n2 <= DLM_WAVE) {
     if (tid < DLM_WAVE) {  // one wave, in registers: lane l holds key l
-      const uint64_t v = dlm::wave_sort_asc(tid < n2 ? keys[tid] : ~0ull, n2);
-      if (tid < n2) keys[tid] = v;
+      const uint64_t v = dlm::wave_sort_asc(tid < n_ok ? keys[tid] : ~0ull, n2);
+      if (tid < n_ok) keys[tid] = v;
     }
     __syncthreads();
-  } else {
-    dlm::bitonic_sort<kRankNT>(keys, n2);
+  } else {  // runs of 64 sorted in registers, placed by rank
+    dlm::sort_runs<kRankNT>(keys, sorted, n_ok, n_ok);
+    order = sorted;
   }
   int n;
   if constexpr (MODE == kTopK) {
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(kRankNT) void k_rank_select(
   } else {
     int adm = 0;  // largest admissible position + 1 among this thread's positions
     for (int t = tid; t < n_ok; t += kRankNT) {
-      const float ct = cs[keys[t] & 0xffffffffu];
+      const float ct = cs[order[t] & 0xffffffffu];
       if (static_cast<double>(t + 2) * (1.0 - static_cast<double>(ct)) < static_cast<double>(f))
         adm = t + 1;
     }
@@ -95,14 +97,14 @@ __global__ __launch_bounds__(kRankNT) void k_rank_select(
       if (n == 0) {
         if (tid == 0) certificate[b] = 0;
       } else if ((n - 1) % kRankNT == tid) {
-        const float ct = cs[keys[n - 1] & 0xffffffffu];
+        const float ct = cs[order[n - 1] & 0xffffffffu];
         certificate[b] = static_cast<uint8_t>(static_cast<double>(n + 1) *
                                                   (1.0 - static_cast<double>(ct)) <=
                                               1.0);
       }
     }
   }
-  for (int t = tid; t < n; t += kRankNT) take[keys[t] & 0xffffffffu] = 1;
+  for (int t = tid; t < n; t += kRankNT) take[order[t] & 0xffffffffu] = 1;
   __syncthreads();
   for (int r = tid; r < M; r += kRankNT) commit[lo + r] = take[r];
   if (tid == 0) n_commit[b] = n;
