@@ -135,3 +135,36 @@ def test_fused_many_sequences_row_gather_and_f32():
              dapd=dict(attn=att32, masked_pos=pos32, m_max=48, tau=0.02))
     # ld 5003 f32 rows are not 16-byte aligned: the element-wise statistics path
     _check(c32, p32, so32, ri32, **d, tag="f32 padded ld", vocab=5000)
+
+
+@pytest.mark.parametrize("seed", [101, 202, 303, 404, 505, 606])
+def test_fused_random_shapes(seed):
+    # random batch, rows, vocabulary (often not a multiple of the 16-byte
+    # chunk), dtypes, row gathers and rule parameters: every rule bitwise
+    # equal to its entry point on the fused statistics, statistics against
+    # the oracle
+    g = np.random.default_rng(seed)
+    B, rows, V = int(g.integers(1, 5)), int(g.integers(1, 97)), int(g.integers(64, 6001))
+    dt = (torch.bfloat16, torch.float32)[int(g.integers(0, 2))]
+    has_prev = bool(g.integers(0, 2))
+    spec = synth.Spec(f"rand{seed}", seed, B, rows, V, dt, 2.0, float(g.uniform(0.2, 1.0)), 12.0,
+                      0.5 if has_prev else None, n_lh=int(g.integers(1, 9)),
+                      seq_len=rows + int(g.integers(0, 40)), attn_sigma=float(g.uniform(0.5, 3.0)),
+                      attn_dtype=(torch.bfloat16, torch.float32)[int(g.integers(0, 2))])
+    cur, prev, so, ri = synth.logits(spec, DEV)
+    if g.integers(0, 2):
+        ri = torch.from_numpy(g.permutation(B * rows)).to(DEV)
+    pos, offs = synth.gen_positions(spec, DEV)
+    attn = synth.attention(spec, DEV)
+    n = B * rows
+    el = torch.from_numpy((g.random(n) < 0.7).astype(np.uint8)).to(DEV) if g.integers(0, 2) else None
+    l_min = int(g.integers(1, 9))
+    parts = dict(
+        fast=dict(eligible=el, tau=float(g.uniform(0.3, 0.95))),
+        depcap=dict(lam=float(g.uniform(0.5, 2.0)), l_min=l_min,
+                    l_max=l_min + int(g.integers(0, 64))) if has_prev else None,
+        cap=dict(eligible=el, tau_low=float(g.uniform(0.2, 0.9)), tau_high=0.95, gamma=-16.0,
+                 k_max=int(g.integers(1, 129))),
+        dapd=dict(attn=attn, masked_pos=pos, m_max=rows + int(g.integers(0, 20)),
+                  tau=float((0.005, 0.02, 0.1)[int(g.integers(0, 3))])))
+    _check(cur, prev, offs, ri, **parts, tag=f"random seed {seed}: B {B} rows {rows} V {V} {dt}")
