@@ -424,3 +424,33 @@ def test_dapd_nan_keys_never_chosen():
     for tau in (0.01, 0.05):
         out = _dapd_case(attn, pos, offs, conf_g, conf_o, tau, 32, f"nan keys tau={tau}")
         assert host(out["commit"])[[3, 17, 31]].sum() == 0
+
+
+@pytest.mark.parametrize("seed", [11, 22, 33, 44])
+def test_rules_random_shapes(seed):
+    # every rule, decision-only and end to end, on a random shape: batch,
+    # rows, ragged vocabulary, dtype, eligibility, thresholds and caps
+    g = np.random.default_rng(seed)
+    B, rows, V = int(g.integers(1, 5)), int(g.integers(2, 97)), int(g.integers(64, 6001))
+    dt = (torch.bfloat16, torch.float32)[int(g.integers(0, 2))]
+    spec = synth.Spec(f"rrand{seed}", seed, B, rows, V, dt, 2.0, float(g.uniform(0.2, 1.0)), 12.0,
+                      0.5, n_lh=int(g.integers(1, 9)), seq_len=rows + int(g.integers(0, 40)),
+                      attn_sigma=float(g.uniform(0.5, 3.0)))
+    cur, prev, so, ri = synth.logits(spec, DEV)
+    gs = api.step_stats(cur, prev)
+    torch.cuda.synchronize()
+    o = oracle.step_stats(host(cur), host(prev))
+    n = B * rows
+    el = torch.from_numpy((g.random(n) < 0.7).astype(np.uint8)).to(DEV) if g.integers(0, 2) else None
+    tag = f"seed {seed}: B {B} rows {rows} V {V} {dt}"
+    _fastdllm_case(gs["conf"], o["conf"], so, float(g.uniform(0.3, 0.95)), el, tag)
+    l_min = int(g.integers(0, 9))
+    _depcap_case(gs, o, so, dict(lam=float(g.uniform(0.5, 2.0)), l_min=l_min,
+                                 l_max=max(1, l_min + int(g.integers(0, 64)))), tag)
+    R = dict(tau_low=float(g.uniform(0.2, 0.9)), tau_high=0.95, gamma=-16.0,
+             k_max=int(g.integers(1, 129)))
+    _cap_case(cur, ri, so, gs, o, R, el, tag)
+    pos, offs = synth.gen_positions(spec, DEV)
+    attn = synth.attention(spec, DEV)
+    _dapd_case(attn, pos, offs, gs["conf"], o["conf"], float((0.005, 0.02, 0.1)[int(g.integers(0, 3))]),
+               rows + int(g.integers(0, 20)), tag)
