@@ -14,9 +14,10 @@ vocabulary 126464, bf16 current and previous-step logits):
                        attention (prompt 512 + generation 256), tau 0.01
 
 By default (`--mode fused`) the step is the one call dlm_decide_step, which
-runs the same decisions in three launches (statistics rows and attention
-averaging in one streaming kernel, then the four rules, then the DAPD
-selection), issued back to back on one stream; the host stays ahead of the
+runs the same decisions in two launches (statistics rows and attention
+averaging in one streaming kernel, then the four rules, with the DAPD
+selection in the last of its scores workgroups), issued back to back on one
+stream; the host stays ahead of the
 GPU, so the launches queue without gaps (a graph per step measured slower:
 each graph launch adds a few microseconds).  Its decisions equal the five
 calls' (checked on every run and reported).
@@ -204,7 +205,7 @@ class LladaStep:
         return d
 
     def fused(self, r, ev=None):
-        """The same step as one dlm_decide_step call (three launches); with
+        """The same step as one dlm_decide_step call (two launches); with
         `ev` (a pair of raw HIP events), the library records them around its
         streaming launch."""
         import ctypes
@@ -429,7 +430,7 @@ def _per_call_body(dev, timed, stats_of, schedules, res):
     timed("dapd_select/llada", lambda r: api.dapd_select(attn[r], pos, offs, st["conf"], 0.01,
                                                          m_max=256, workspace=ws), 4, nb,
           "1 x [320, 768, 768] bf16 maps, 256 masked")
-    # the whole step as one call (three launches)
+    # the whole step as one call (two launches)
     prevs = [prev] + [prev.clone() for _ in range(3)]
     parts = dict(fast=dict(eligible=block, tau=R["tau"]),
                  depcap=dict(lam=R["lam"], l_min=R["l_min"], l_max=R["l_max"]),
@@ -484,8 +485,8 @@ def _per_call_body(dev, timed, stats_of, schedules, res):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -495,7 +496,7 @@ def main() -> int:
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     ap.add_argument("--mode", choices=("fused", "fused-graph", "graph", "eager"),
                     default="fused",
-                    help="fused: one dlm_decide_step call (three launches) per step; "
+                    help="fused: one dlm_decide_step call (two launches) per step; "
                          "fused-graph: that call captured once per input replica and "
                          "replayed; graph: the five individual calls captured and replayed; "
                          "eager: the five calls launched one by one")

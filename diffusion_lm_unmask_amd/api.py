@@ -320,7 +320,7 @@ def fixed_block_eligible(masked_pos, seq_offsets, block_len, gen_start=None):
 
 def decide_step(logits, prev=None, seq_offsets=None, row_index=None, vocab=None, fast=None,
                 depcap=None, cap=None, dapd=None):
-    """dlm_decide_step: statistics plus the enabled rules in three launches.
+    """dlm_decide_step: statistics plus the enabled rules in two launches.
 
     Each rule part is None (off) or a dict of its parameters, named as in the
     individual wrappers:

@@ -14,8 +14,10 @@ __global__ __launch_bounds__(kCapNT) void k_cap(
     const uint8_t* __restrict__ eligible, float tau_low, float tau_high, float gamma, int k_max,
     uint8_t* __restrict__ commit, int32_t* __restrict__ n_commit, int32_t* __restrict__ cand_out,
     float* __restrict__ dmat_out) {
+  __shared__ CapSmem sm;
   cap_seq<BF16>(blockIdx.x, logits, ld, vocab, row_index, seq_offsets, conf, argmax, lse,
-                eligible, tau_low, tau_high, gamma, k_max, commit, n_commit, cand_out, dmat_out);
+                eligible, tau_low, tau_high, gamma, k_max, commit, n_commit, cand_out, dmat_out,
+                sm);
 }
 
 }  // namespace

@@ -32,28 +32,52 @@ __device__ __forceinline__ float gather(const void* logits, int64_t idx) {
   return static_cast<const float*>(logits)[idx];
 }
 
+// The workgroup's LDS.  The caller declares it (__shared__), so that a kernel
+// running other roles in other workgroups can overlay their LDS on it.
+struct CapSmem {
+  uint64_t keys[kMaxRows];
+  uint64_t top[kKM];       // the first k_max keys in order (runs path)
+  float rc[kMaxRows];      // by local row (pool rows only): conf
+  int32_t ry[kMaxRows];    // argmax
+  float rlse[kMaxRows];    // lse
+  int64_t rri[kMaxRows];   // row_index
+  float G[kKM][kKM + 1];
+  uint64_t cw[kKM][2];
+  int64_t coff[kKM];
+  int crow[kKM], cy[kKM];
+  float cconf[kKM], clse[kKM];
+  uint32_t sel[kMaxRows / 32];
+  float shf[kCapNT / DLM_WAVE];
+  int shi[kCapNT / DLM_WAVE];
+  int npool, bad;
+};
+
 template <bool BF16>
 __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, int64_t ld,
     int64_t vocab, const int64_t* __restrict__ row_index, const int32_t* __restrict__ seq_offsets,
     const float* __restrict__ conf, const int32_t* __restrict__ argmax,
     const float* __restrict__ lse, const uint8_t* __restrict__ eligible, float tau_low,
     float tau_high, float gamma, int k_max, uint8_t* __restrict__ commit,
-    int32_t* __restrict__ n_commit, int32_t* __restrict__ cand_out, float* __restrict__ dmat_out) {
-  __shared__ uint64_t keys[kMaxRows];
-  __shared__ uint64_t top[kKM];       // the first k_max keys in order (runs path)
-  __shared__ float rc[kMaxRows];      // by local row (pool rows only): conf
-  __shared__ int32_t ry[kMaxRows];    // argmax
-  __shared__ float rlse[kMaxRows];    // lse
-  __shared__ int64_t rri[kMaxRows];   // row_index
-  __shared__ float G[kKM][kKM + 1];
-  __shared__ uint64_t cw[kKM][2];
-  __shared__ int64_t coff[kKM];
-  __shared__ int crow[kKM], cy[kKM];
-  __shared__ float cconf[kKM], clse[kKM];
-  __shared__ uint32_t sel[kMaxRows / 32];
-  __shared__ float shf[kCapNT / DLM_WAVE];
-  __shared__ int shi[kCapNT / DLM_WAVE];
-  __shared__ int npool, bad;
+    int32_t* __restrict__ n_commit, int32_t* __restrict__ cand_out, float* __restrict__ dmat_out,
+    CapSmem& sm) {
+  auto& keys = sm.keys;
+  auto& top = sm.top;
+  auto& rc = sm.rc;
+  auto& ry = sm.ry;
+  auto& rlse = sm.rlse;
+  auto& rri = sm.rri;
+  auto& G = sm.G;
+  auto& cw = sm.cw;
+  auto& coff = sm.coff;
+  auto& crow = sm.crow;
+  auto& cy = sm.cy;
+  auto& cconf = sm.cconf;
+  auto& clse = sm.clse;
+  auto& sel = sm.sel;
+  auto& shf = sm.shf;
+  auto& shi = sm.shi;
+  int& npool = sm.npool;
+  int& bad = sm.bad;
 
   const int tid = threadIdx.x;
   const int lo = seq_offsets[b], n = seq_offsets[b + 1] - lo;

@@ -20,7 +20,7 @@ __global__ __launch_bounds__(kSymNT) void k_dapd_sym(
     int m_max, const float* __restrict__ conf, float tau, const char* __restrict__ ws, Layout L,
     float* __restrict__ degree, float* __restrict__ sym, float* __restrict__ key_out, Policy P) {
   dapd_sym_rows(blockIdx.y, blockIdx.x, seq_offsets, masked_pos, S, m_max, conf, tau, ws, L,
-                degree, sym, key_out, P);
+                degree, sym, key_out, P, nullptr);
 }
 
 __global__ __launch_bounds__(kSelNT) void k_dapd_select(
@@ -28,8 +28,9 @@ __global__ __launch_bounds__(kSelNT) void k_dapd_select(
     int m_max, const char* __restrict__ ws, Layout L, const float* __restrict__ conf,
     uint8_t* __restrict__ commit, int32_t* __restrict__ n_commit, float* __restrict__ degree,
     float* __restrict__ sym, float* __restrict__ key_out, Policy P) {
-  dapd_select_seq(blockIdx.x, masked_pos, S, seq_offsets, m_max, ws, L, conf, commit, n_commit,
-                  degree, sym, key_out, P);
+  __shared__ SelSmem<kSelNT> sm;
+  dapd_select_seq<kSelNT>(blockIdx.x, masked_pos, S, seq_offsets, m_max, ws, L, conf, commit,
+                          n_commit, degree, sym, key_out, P, sm);
 }
 
 }  // namespace

@@ -20,7 +20,9 @@
 //                (the four teams of a wave share its cache lines), so no
 //                transposed copy is written; each step's 16 edge bits are one
 //                ballot slice; fp64 proxy degree and the ordering key.
-//  k_dapd_select one workgroup (1024 threads) per sequence:
+//  k_dapd_select one workgroup (1024 threads) per sequence (the fused step
+//                runs it at 256 threads, in the sequence's last scores
+//                workgroup; see dapd_scores_select):
 //                1. the adjacency bitset and keys into LDS;
 //                2. order by the 64-bit keys (key desc, position asc): each
 //                   wave sorts a run of 64 in registers, and a key's rank is
@@ -200,8 +202,9 @@ __device__ __forceinline__ void dapd_avg_tile(int b, int tile, const void* __res
 //   adj        u64 [n_seq][m_max][words]     adjacency bitsets, words = ceil(m_max/64)
 //   keys       u64 [n_seq][m_max]            (order key, position)
 //   has_edge   u8  [n_seq][m_max]            bit 0: an edge; bit 1: position out of range
+//   tally      u64 [n_seq]                   the fused step's per-sequence counters
 struct Layout {
-  size_t a, adj, keys, has_edge, total;
+  size_t a, adj, keys, has_edge, tally, total;
   int ld, words;
 };
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -214,7 +217,8 @@ __host__ __device__ inline Layout layout(int n_seq, int m_max) {
   L.adj = align256(nm * L.ld * sizeof(float));
   L.keys = L.adj + align256(nm * L.words * sizeof(uint64_t));
   L.has_edge = L.keys + align256(nm * sizeof(uint64_t));
-  L.total = L.has_edge + align256(nm);
+  L.tally = L.has_edge + align256(nm);
+  L.total = L.tally + align256(static_cast<size_t>(n_seq) * sizeof(uint64_t));
   return L;
 }
 
@@ -226,20 +230,31 @@ __host__ __device__ inline Layout layout(int n_seq, int m_max) {
 constexpr int kSymRows = DLM_DAPD_SYM_ROWS;  // rows per k_dapd_sym workgroup (16 lanes each)
 constexpr int kSymNT = kSymRows * 16;
 
+// A row's part of its sequence's tally (the fused step adds them up): bits
+// 16-31 count commits as an edgeless graph makes them, 32-47 rows with an
+// edge, 48-63 rows whose position is out of range (or a sequence longer than
+// m_max).  Bits 0-15 count blocks of kSymRows rows.  Each field stays below
+// 2^16 (at most 1024 rows, at most 256 blocks per sequence).
+constexpr uint64_t kTallyWG = 1ull, kTallyCommit = 1ull << 16, kTallyEdge = 1ull << 32,
+                   kTallyBad = 1ull << 48;
+
 // s = (a + aT)/2 for kSymRows rows per workgroup: adjacency bits (ballot slices),
 // fp64 proxy degree (fixed-pattern 16-lane reduction), ordering key.  Each
 // row's masked position is checked here too: has_edge carries bit 1 for a
-// position outside [0, S), which the selection reports.
-__device__ __forceinline__ void dapd_sym_rows(int b, int rb,
+// position outside [0, S), which the selection reports.  With `commit`, each
+// row also gets the commit an edgeless graph gives it (a key that is not NaN,
+// or pre-unmasked).  Returns the row's tally on its team's lane 0, else 0.
+__device__ __forceinline__ uint64_t dapd_sym_rows(int b, int rb,
     const int32_t* __restrict__ seq_offsets, const int32_t* __restrict__ masked_pos, int64_t S,
     int m_max, const float* __restrict__ conf, float tau,
     const char* __restrict__ ws, Layout L, float* __restrict__ degree, float* __restrict__ sym,
-    float* __restrict__ key_out, Policy P) {
+    float* __restrict__ key_out, Policy P, uint8_t* __restrict__ commit) {
   const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
-  const int team = threadIdx.x / 16, tl = threadIdx.x % 16;
+  const int team = (threadIdx.x % DLM_WAVE) / 16, tl = threadIdx.x % 16;  // this wave's teams
   const int i = rb * kSymRows + team;
   const int64_t sbase = static_cast<int64_t>(b) * m_max * m_max;
-  if (M > m_max || M < 0 || i >= m_max) return;  // over-long sequences: k_dapd_select reports
+  if (M > m_max || M < 0) return tl == 0 ? kTallyBad : 0ull;  // over-long: the selection reports
+  if (i >= m_max) return 0ull;
   if (i >= M || late_stage(P, b, M)) {  // pad rows, or no graph: NaN in the optional outputs
     if (i < M && tl == 0) {
       if (degree) degree[lo + i] = NAN;
@@ -247,7 +262,7 @@ __device__ __forceinline__ void dapd_sym_rows(int b, int rb,
     }
     if (sym)
       for (int j = tl; j < m_max; j += 16) sym[sbase + static_cast<int64_t>(i) * m_max + j] = NAN;
-    return;
+    return 0ull;
   }
   // read now, used at the end: their latency hides behind the row reads
   const int pos_i = masked_pos[lo + i];
@@ -315,38 +330,64 @@ __device__ __forceinline__ void dapd_sym_rows(int b, int rb,
     const uint32_t bad = pos_i < 0 || pos_i >= S;
     reinterpret_cast<uint8_t*>(const_cast<char*>(ws) + L.has_edge)[static_cast<int64_t>(b) * m_max + i] =
         static_cast<uint8_t>(anyb | (bad << 1));
+    const uint32_t c = (kk == kk) | (P.pre_unmask && conf_i == 1.0f);
+    if (commit) commit[lo + i] = static_cast<uint8_t>(c);
+    return c * kTallyCommit + anyb * kTallyEdge + bad * kTallyBad;
   }
+  return 0ull;
 }
 
-// Per sequence: load the graph into LDS, order the nodes, run the greedy.
+// The greedy's LDS for NT threads, declared by the caller (__shared__) so
+// that a kernel running other roles in other workgroups can overlay their LDS
+// on it.
+template <int NT>
+struct SelSmem {
+  uint64_t adj[kMaxM][kWords];   // 128 KiB; row i = neighbours of node i
+  uint64_t keys[kMaxM];          // by node, then sorted runs of 64
+  uint64_t chosen[kWords];
+  uint64_t bmk[kWords][kWords];  // block k (ranks 64k..64k+63): its nodes as a bitset
+  uint64_t lmask[kMaxM];         // by rank: lanes of the earlier neighbours in its block
+  uint64_t tally;                // the fused step: the sequence's totals
+  int16_t order[kMaxM];          // node of rank t (-1 - node: NaN key)
+  int16_t rank_of[kMaxM];        // rank of each node
+  uint8_t has_edge[kMaxM];
+  int shi[NT / DLM_WAVE];
+  float shf[NT / DLM_WAVE];
+  int last;                      // the fused step: this workgroup counted in last
+};
+
+// Per sequence: load the graph into LDS, order the nodes, run the greedy
+// (NT threads).  The result does not depend on NT.
+template <int NT>
 __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict__ masked_pos,
     int64_t S, const int32_t* __restrict__ seq_offsets, int m_max, const char* __restrict__ ws,
     Layout L, const float* __restrict__ conf, uint8_t* __restrict__ commit,
     int32_t* __restrict__ n_commit, float* __restrict__ degree, float* __restrict__ sym,
-    float* __restrict__ key_out, Policy P) {
-  __shared__ uint64_t adj[kMaxM][kWords];  // 128 KiB; row i = neighbours of node i
-  __shared__ uint64_t keys[kMaxM];         // by node, then sorted runs of 64
-  __shared__ int16_t order[kMaxM];         // node of rank t (-1 - node: NaN key)
-  __shared__ uint64_t chosen[kWords];
-  __shared__ int16_t rank_of[kMaxM];       // rank of each node
-  __shared__ uint64_t bmk[kWords][kWords]; // block k (ranks 64k..64k+63): its nodes as a bitset
-  __shared__ uint64_t lmask[kMaxM];        // by rank: lanes of the earlier neighbours in its block
-  __shared__ uint8_t has_edge[kMaxM];
-  __shared__ int shi[kSelNT / DLM_WAVE];
-  __shared__ float shf[kSelNT / DLM_WAVE];
+    float* __restrict__ key_out, Policy P, SelSmem<NT>& sm) {
+  constexpr int NW = NT / DLM_WAVE;
+  auto& adj = sm.adj;
+  auto& keys = sm.keys;
+  auto& order = sm.order;
+  auto& chosen = sm.chosen;
+  auto& rank_of = sm.rank_of;
+  auto& bmk = sm.bmk;
+  auto& lmask = sm.lmask;
+  auto& has_edge = sm.has_edge;
+  auto& shi = sm.shi;
+  auto& shf = sm.shf;
   const int tid = threadIdx.x;
   const int wv = tid / DLM_WAVE, ln = tid % DLM_WAVE;
   const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
   const int64_t sbase = static_cast<int64_t>(b) * m_max * m_max;
 
   auto report = [&]() {  // nothing committed, n_commit = -1
-    for (int r = tid; r < M; r += kSelNT) {
+    for (int r = tid; r < M; r += NT) {
       commit[lo + r] = 0;
       if (degree) degree[lo + r] = NAN;
       if (key_out) key_out[lo + r] = NAN;
     }
     if (sym)
-      for (int64_t e = tid; e < static_cast<int64_t>(m_max) * m_max; e += kSelNT)
+      for (int64_t e = tid; e < static_cast<int64_t>(m_max) * m_max; e += NT)
         sym[sbase + e] = NAN;
     if (tid == 0) {
       n_commit[b] = -1;
@@ -364,7 +405,7 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
   int bad_pos = 0, any_edge = 0;
   const int nw = (M + 63) / 64;  // adjacency words in use
   if (late) {
-    for (int r = tid; r < M; r += kSelNT) {
+    for (int r = tid; r < M; r += NT) {
       const int p = masked_pos[lo + r];
       bad_pos |= p < 0 || p >= S;
     }
@@ -375,11 +416,11 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
                             static_cast<int64_t>(b) * m_max;
     const uint8_t* gedge = reinterpret_cast<const uint8_t*>(ws + L.has_edge) +
                            static_cast<int64_t>(b) * m_max;
-    for (int e = tid; e < M * nw; e += kSelNT) {
+    for (int e = tid; e < M * nw; e += NT) {
       const int i = e / nw, w = e - i * nw;
       adj[i][w] = gadj[static_cast<int64_t>(i) * L.words + w];
     }
-    for (int e = tid; e < M; e += kSelNT) {
+    for (int e = tid; e < M; e += NT) {
       const uint8_t he = gedge[e];
       keys[e] = gkeys[e];
       has_edge[e] = he & 1u;
@@ -387,9 +428,9 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
       bad_pos |= he >> 1;
     }
     if (tid < kWords) chosen[tid] = 0ull;
-    for (int e = tid; e < kWords * kWords; e += kSelNT) bmk[e / kWords][e % kWords] = 0ull;
+    for (int e = tid; e < kWords * kWords; e += NT) bmk[e / kWords][e % kWords] = 0ull;
   }
-  const int flags = dlm::block_or_i<kSelNT>(bad_pos | (any_edge << 1), shi);  // ends with a barrier
+  const int flags = dlm::block_or_i<NT>(bad_pos | (any_edge << 1), shi);  // ends with a barrier
   if (flags & 1) {
     report();
     return;
@@ -398,7 +439,7 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
   if (late) {  // no graph: conf > late_tau, else the most confident row
     int above = 0, bi = INT32_MAX;
     float bv = -INFINITY;
-    for (int r = tid; r < M; r += kSelNT) {
+    for (int r = tid; r < M; r += NT) {
       const float cf = conf[lo + r];
       above += cf > P.late_tau;
       if (cf == cf && (bi == INT32_MAX || cf > bv)) {
@@ -406,16 +447,16 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
         bi = r;
       }
     }
-    above = dlm::block_sum<kSelNT>(above, shi);
-    const int fb = above == 0 ? dlm::block_argmax<kSelNT>(bv, bi, shf, shi) : INT32_MAX;
+    above = dlm::block_sum<NT>(above, shi);
+    const int fb = above == 0 ? dlm::block_argmax<NT>(bv, bi, shf, shi) : INT32_MAX;
     int cnt = 0;
-    for (int r = tid; r < M; r += kSelNT) {
+    for (int r = tid; r < M; r += NT) {
       const float cf = conf[lo + r];
       const int c = (cf > P.late_tau) || r == fb || (P.pre_unmask && cf == 1.0f);
       commit[lo + r] = static_cast<uint8_t>(c);
       cnt += c;
     }
-    cnt = dlm::block_sum<kSelNT>(cnt, shi);
+    cnt = dlm::block_sum<NT>(cnt, shi);
     if (tid == 0) n_commit[b] = cnt;
     return;
   }
@@ -424,36 +465,36 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
     // no edge anywhere: the independent set is every node whatever the
     // order, except a NaN key (never chosen)
     int cnt = 0;
-    for (int r = tid; r < M; r += kSelNT) {
+    for (int r = tid; r < M; r += NT) {
       const int c = static_cast<int>((keys[r] >> 32) != 0xffffffffull) |
                     (P.pre_unmask && conf[lo + r] == 1.0f);  // pre-unmask
       commit[lo + r] = static_cast<uint8_t>(c);
       cnt += c;
     }
-    cnt = dlm::block_sum<kSelNT>(cnt, shi);
+    cnt = dlm::block_sum<NT>(cnt, shi);
     if (tid == 0) n_commit[b] = cnt;
     return;
   }
 
   // ---- order the nodes (keys are unique: they carry the node).  Wave w
-  // sorts keys 64w .. 64w+63 in registers; a key's rank is its lane plus, for
-  // every other wave's sorted run, the number of keys below it (binary
-  // searches, four runs side by side).  Padding keys (~0) sort after every
-  // node and get no rank.
+  // sorts runs w, w + NW, ... (keys 64r .. 64r+63 of run r) in registers; a
+  // key's rank is its lane plus, for every other sorted run, the number of
+  // keys below it (binary searches, four runs side by side).  Padding keys
+  // (~0) sort after every node and get no rank.
   const int n_runs = (M + 63) / 64;
-  uint64_t v_sorted = ~0ull;
-  if (wv < n_runs) {  // whole waves: every lane of the wave takes part
-    const int i = wv * 64 + ln;
-    v_sorted = dlm::wave_sort_asc(i < M ? keys[i] : ~0ull, 64);
-    keys[i] = v_sorted;  // run wv, sorted (a wave rewrites only its own run)
+  for (int run = wv; run < n_runs; run += NW) {  // whole waves: every lane takes part
+    const int i = run * 64 + ln;
+    keys[i] = dlm::wave_sort_asc(i < M ? keys[i] : ~0ull, 64);  // a wave rewrites only its run
   }
   __syncthreads();
-  if (wv < n_runs && v_sorted != ~0ull) {
-    const int rank = ln + dlm::count_below_in_runs(keys, n_runs, wv, v_sorted);
+  for (int run = wv; run < n_runs; run += NW) {
+    const uint64_t v = keys[run * 64 + ln];
+    if (v == ~0ull) continue;
+    const int rank = ln + dlm::count_below_in_runs(keys, n_runs, run, v);
     // a NaN key (it sorts after every finite key) is stored as -1 - node:
     // such a node is never chosen
-    const int node = static_cast<int>(v_sorted & 0xffffffffu);
-    order[rank] = static_cast<int16_t>((v_sorted >> 32) == 0xffffffffull ? -1 - node : node);
+    const int node = static_cast<int>(v & 0xffffffffu);
+    order[rank] = static_cast<int16_t>((v >> 32) == 0xffffffffull ? -1 - node : node);
     rank_of[node] = static_cast<int16_t>(rank);
     atomicOr(reinterpret_cast<unsigned long long*>(&bmk[rank >> 6][node >> 6]), 1ull << (node & 63));
   }
@@ -462,7 +503,7 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
   // ---- each node's earlier neighbours inside its block of 64 ranks, as lane
   // bits.  They do not depend on what earlier blocks chose, so every node is
   // done at once here rather than inside the sequential greedy.
-  for (int v = tid; v < M; v += kSelNT) {
+  for (int v = tid; v < M; v += NT) {
     const int t = rank_of[v], k = t >> 6;
     uint64_t loc = 0ull;
     if (has_edge[v]) {
@@ -521,14 +562,69 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
   }
   __syncthreads();
   int cnt = 0;
-  for (int r = tid; r < M; r += kSelNT) {
+  for (int r = tid; r < M; r += NT) {
     const int c = static_cast<int>((chosen[r >> 6] >> (r & 63)) & 1ull) |
                   (P.pre_unmask && conf[lo + r] == 1.0f);  // pre-unmask
     commit[lo + r] = static_cast<uint8_t>(c);
     cnt += c;
   }
-  cnt = dlm::block_sum<kSelNT>(cnt, shi);
+  cnt = dlm::block_sum<NT>(cnt, shi);
   if (tid == 0) n_commit[b] = cnt;
+}
+
+// The fused step's DAPD part, on NT-thread workgroups: `waves` waves of the
+// workgroup each score one block of kSymRows rows of sequence b (blocks
+// waves*wg .. of the sequence's `blocks` blocks; dapd_sym_rows), writing each
+// row's commit as an edgeless graph has it, then add their tallies to the
+// sequence's counter, which the launch before zeroed.  The wave that counts
+// in the last block holds the totals, and its workgroup goes on.  Without an
+// edge, a bad position, an over-long sequence or the late stage, the commits
+// written are the greedy's (every node whose key is not NaN, and the
+// pre-unmasked rows), so it only writes n_commit.  Otherwise it runs the
+// greedy, which rewrites every commit.  The outputs are those of k_dapd_sym
+// then k_dapd_select.
+template <int NT>
+__device__ __forceinline__ void dapd_scores_select(int b, int wg, int waves, int blocks,
+    const int32_t* __restrict__ seq_offsets, const int32_t* __restrict__ masked_pos, int64_t S,
+    int m_max, const float* __restrict__ conf, float tau, const char* __restrict__ ws, Layout L,
+    uint8_t* __restrict__ commit, int32_t* __restrict__ n_commit, Policy P, SelSmem<NT>& sm) {
+  static_assert(kSymNT == DLM_WAVE && NT >= DLM_WAVE, "a block of rows is one wave's");
+  const int wv = threadIdx.x / DLM_WAVE, rb = wg * waves + wv;
+  if (threadIdx.x == 0) sm.last = 0;
+  __syncthreads();
+  if (wv < waves && rb < blocks) {
+    uint64_t t = dapd_sym_rows(b, rb, seq_offsets, masked_pos, S, m_max, conf, tau, ws, L, nullptr,
+                               nullptr, nullptr, P, commit);
+    t += __shfl_xor(static_cast<unsigned long long>(t), 16);  // the four teams' lane 0
+    t += __shfl_xor(static_cast<unsigned long long>(t), 32);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this wave's rows, before counting in
+    if (threadIdx.x % DLM_WAVE == 0) {
+      unsigned long long* ctr =
+          reinterpret_cast<unsigned long long*>(const_cast<char*>(ws) + L.tally) + b;
+      const uint64_t mine = t + kTallyWG;
+      const uint64_t tot = atomicAdd(ctr, static_cast<unsigned long long>(mine)) + mine;
+      if ((tot & 0xffffull) == static_cast<uint64_t>(blocks)) {  // one wave per sequence
+        sm.tally = tot;
+        sm.last = 1;
+      }
+    }
+  }
+  __syncthreads();
+  if (!sm.last) return;  // uniform over the workgroup
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other workgroups' rows
+  const uint64_t tot = sm.tally;
+  // no edge, bad position or over-long sequence, and not the late stage (no
+  // trip to memory for the stage test when there is no stage policy)
+  if (tot < kTallyEdge &&
+      (P.gen_len == nullptr || !late_stage(P, b, seq_offsets[b + 1] - seq_offsets[b]))) {
+    if (threadIdx.x == 0) {
+      n_commit[b] = static_cast<int32_t>((tot >> 16) & 0xffffull);
+      if (P.stage) P.stage[b] = 0;
+    }
+    return;
+  }
+  dapd_select_seq<NT>(b, masked_pos, S, seq_offsets, m_max, ws, L, conf, commit, n_commit,
+                      nullptr, nullptr, nullptr, P, sm);
 }
 
 }  // namespace

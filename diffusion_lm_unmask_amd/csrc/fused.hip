@@ -1,4 +1,4 @@
-// fused.hip — dlm_decide_step: the small-batch decision step in three
+// fused.hip — dlm_decide_step: the small-batch decision step in two
 // launches, built from the same device code as the individual entry points
 // (stats_impl.h, rules_impl.h, cap_impl.h, dapd_impl.h).  The statistics run
 // with four 16-byte chunks per lane and segment (the statistics call uses
@@ -11,13 +11,17 @@
 //            keeps the memory system busy through each other's ramp-up and
 //            tail instead of paying two.
 //  launch 2  k_step_rules: Fast-dLLM, DepCap and CAP one workgroup per
-//            sequence each, and the DAPD scores four rows per workgroup
-//            (its first wave), side by side.
-//  launch 3  k_step_select: the DAPD greedy, one workgroup per sequence.
+//            sequence each, and the DAPD scores four rows per wave (one to
+//            four waves per workgroup), side by side.  The workgroup that
+//            finishes a sequence's last block of scores (an atomic tally per
+//            sequence) runs that sequence's greedy (dapd_scores_select).
 //
-// No part waits for another inside a launch: the dependencies (statistics
-// before the rules, scores before the greedy) are the launch boundaries.
+// No workgroup waits for another: the statistics reach the rules through
+// the launch boundary, and the scores reach the greedy through the tally's
+// release/acquire, in the one workgroup that sees every other one done.
 #include <hip/hip_ext.h>
+
+#include <algorithm>
 
 #include "cap_impl.h"
 #include "checks.h"
@@ -55,6 +59,7 @@ struct StreamArgs {
   const int32_t* masked_pos;
   const int32_t* seq_offsets;
   float* ws_a;
+  uint64_t* tally;  // [n_seq], zeroed here for launch 2
   Policy P;
 };
 
@@ -66,6 +71,7 @@ __global__ __launch_bounds__(kStepNT) void k_step_stream(const StreamArgs a) {
     return;
   }
   const int64_t t = g - a.n_rows;
+  if (threadIdx.x == 0 && t % a.tiles_per_seq == 0) a.tally[t / a.tiles_per_seq] = 0ull;
   dapd_avg_tile<ABF16, DLM_STEP_TILE_UNR>(
       static_cast<int>(t / a.tiles_per_seq), static_cast<int>(t % a.tiles_per_seq), a.attn, a.n_lh,
       a.S, a.batch_stride, a.masked_pos, a.seq_offsets, a.m_max, a.n_tc, a.vec_ok, a.ws_a, a.P);
@@ -96,18 +102,28 @@ struct RulesArgs {
   int c_kmax;
   uint8_t* c_commit;
   int32_t* c_n;
-  // DAPD scores
+  // DAPD scores and greedy
   const int32_t* masked_pos;
   int64_t S;
-  int m_max, rb_per_seq;
+  int m_max, blocks, waves, wg_per_seq;  // row blocks per sequence, blocks per workgroup
   float tau;
   const char* ws;
   Layout L;
   Policy P;
+  uint8_t* p_commit;
+  int32_t* p_n;
+};
+
+// The roles' LDS share one allocation: a workgroup runs one role.
+union RulesSmem {
+  CapSmem cap;
+  DepSmem dep;
+  SelSmem<kRulesNT> sel;
 };
 
 template <bool BF16>
 __global__ __launch_bounds__(kRulesNT) void k_step_rules(const RulesArgs a) {
+  __shared__ RulesSmem sm;
   int g = blockIdx.x;
   if (g < a.nf) {
     fastdllm_seq(g, a.conf, a.f_el, a.seq_offsets, a.f_tau, a.f_commit, a.f_n);
@@ -116,38 +132,20 @@ __global__ __launch_bounds__(kRulesNT) void k_step_rules(const RulesArgs a) {
   g -= a.nf;
   if (g < a.nd) {
     depcap_seq(g, a.kl, a.ent, a.seq_offsets, a.d_has_prev, a.d_lambda, a.d_lmin, a.d_lmax,
-               a.d_radius, a.d_eps, a.d_block_len, a.d_score);
+               a.d_radius, a.d_eps, a.d_block_len, a.d_score, sm.dep);
     return;
   }
   g -= a.nd;
   if (g < a.nc) {
     cap_seq<BF16>(g, a.logits, a.ld, a.vocab, a.row_index, a.seq_offsets, a.conf, a.argmax,
                   a.lse, a.c_el, a.c_tau_low, a.c_tau_high, a.c_gamma, a.c_kmax, a.c_commit,
-                  a.c_n, nullptr, nullptr);
+                  a.c_n, nullptr, nullptr, sm.cap);
     return;
   }
   g -= a.nc;
-  if (threadIdx.x >= kSymNT) return;  // the scores use one wave: four 16-lane teams
-  dapd_sym_rows(g / a.rb_per_seq, g % a.rb_per_seq, a.seq_offsets, a.masked_pos, a.S, a.m_max,
-                a.conf, a.tau, a.ws, a.L, nullptr, nullptr, nullptr, a.P);
-}
-
-struct SelectArgs {
-  const int32_t* masked_pos;
-  int64_t S;
-  const int32_t* seq_offsets;
-  int m_max;
-  const char* ws;
-  Layout L;
-  const float* conf;
-  uint8_t* commit;
-  int32_t* n_commit;
-  Policy P;
-};
-
-__global__ __launch_bounds__(kSelNT) void k_step_select(const SelectArgs a) {
-  dapd_select_seq(blockIdx.x, a.masked_pos, a.S, a.seq_offsets, a.m_max, a.ws, a.L, a.conf,
-                  a.commit, a.n_commit, nullptr, nullptr, nullptr, a.P);
+  dapd_scores_select<kRulesNT>(g / a.wg_per_seq, g % a.wg_per_seq, a.waves, a.blocks,
+                               a.seq_offsets, a.masked_pos, a.S, a.m_max, a.conf, a.tau, a.ws,
+                               a.L, a.p_commit, a.p_n, a.P, sm.sel);
 }
 
 // With events, the launch itself sets them to the kernel's start and end
@@ -229,6 +227,7 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
     sa.masked_pos = d->masked_pos;
     sa.seq_offsets = d->seq_offsets;
     sa.ws_a = reinterpret_cast<float*>(ws + L.a);
+    sa.tally = reinterpret_cast<uint64_t*>(ws + L.tally);
     n_tiles = static_cast<int64_t>(sa.tiles_per_seq) * d->n_seq;
   }
   const int64_t g1 = d->n_rows + n_tiles;
@@ -246,7 +245,7 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
   }
   DLM_CHECK_LAUNCH();
 
-  // ---- launch 2: the per-sequence rules and the DAPD scores
+  // ---- launch 2: the per-sequence rules, the DAPD scores and greedy
   RulesArgs ra{};
   ra.seq_offsets = d->seq_offsets;
   ra.conf = d->conf;
@@ -257,8 +256,23 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
   ra.nf = fast ? d->n_seq : 0;
   ra.nd = dep ? d->n_seq : 0;
   ra.nc = cap ? d->n_seq : 0;
-  ra.rb_per_seq = dapd ? (d->m_max + kSymRows - 1) / kSymRows : 0;
-  ra.ns = dapd ? ra.rb_per_seq * d->n_seq : 0;
+  if (dapd) {
+    // one block of kSymRows rows per wave; with more blocks than free compute
+    // units (every launch-2 workgroup takes a whole compute unit's LDS), a
+    // workgroup scores up to four blocks, so that the scores finish in one
+    // round of workgroups
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return DLM_ERR_HIP;
+    ra.blocks = (d->m_max + kSymRows - 1) / kSymRows;
+    const int64_t total = static_cast<int64_t>(ra.blocks) * d->n_seq;
+    const int64_t free_cus = std::max<int64_t>(1, cus - (ra.nf + ra.nd + ra.nc));
+    ra.waves = static_cast<int>(
+        std::min<int64_t>(kRulesNT / DLM_WAVE, std::max<int64_t>(1, (total + free_cus - 1) / free_cus)));
+    ra.wg_per_seq = (ra.blocks + ra.waves - 1) / ra.waves;
+    ra.ns = ra.wg_per_seq * d->n_seq;
+  }
   ra.f_el = d->fast_eligible;
   ra.f_tau = d->fast_tau;
   ra.f_commit = d->fast_commit;
@@ -289,6 +303,8 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
   ra.ws = ws;
   ra.L = L;
   ra.P = P;
+  ra.p_commit = d->dapd_commit;
+  ra.p_n = d->dapd_n_commit;
   const int64_t g2 = static_cast<int64_t>(ra.nf) + ra.nd + ra.nc + ra.ns;
   if (g2 > 0) {
     if (bf16)
@@ -300,12 +316,5 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
     DLM_CHECK_LAUNCH();
   }
 
-  // ---- launch 3: the DAPD greedy
-  if (dapd) {
-    const SelectArgs sel{d->masked_pos, d->S, d->seq_offsets, d->m_max, ws, L, d->conf,
-                         d->dapd_commit, d->dapd_n_commit, P};
-    hipLaunchKernelGGL(k_step_select, dim3(d->n_seq), dim3(kSelNT), 0, s, sel);
-    DLM_CHECK_LAUNCH();
-  }
   return DLM_OK;
 }

@@ -21,8 +21,9 @@ __global__ __launch_bounds__(kRuleNT) void k_depcap(const float* __restrict__ kl
                                                 double lambda, int l_min, int l_max, int R,
                                                 double eps, int32_t* __restrict__ block_len,
                                                 float* __restrict__ score) {
+  __shared__ DepSmem sm;
   depcap_seq(blockIdx.x, kl, ent, seq_offsets, has_prev, lambda, l_min, l_max, R, eps, block_len,
-             score);
+             score, sm);
 }
 
 }  // namespace

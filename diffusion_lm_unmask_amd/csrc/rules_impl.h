@@ -50,6 +50,15 @@ __device__ __forceinline__ void fastdllm_seq(int b, const float* __restrict__ co
   }
 }
 
+// DepCap's LDS, declared by the caller (__shared__) so that a kernel running
+// other roles in other workgroups can overlay their LDS on it.
+struct DepSmem {
+  double sI[DLM_MAX_WINDOW];
+  double sH[DLM_MAX_WINDOW];
+  double shd[kRuleNT / DLM_WAVE];
+  int shi[kRuleNT / DLM_WAVE];
+};
+
 // DepGA-Block boundary.  Window W = min(l_max, rows); box smoothing of
 // radius R clipped to the window, division by the window mean (+eps),
 // S_k = I~_k - lambda*H~_k in fp64 rounded to f32; k* = first f32 S_k < 0.
@@ -59,11 +68,11 @@ __device__ __forceinline__ void depcap_seq(int b, const float* __restrict__ kl,
                                            const uint8_t* __restrict__ has_prev,
                                            double lambda, int l_min, int l_max, int R,
                                            double eps, int32_t* __restrict__ block_len,
-                                           float* __restrict__ score) {
-  __shared__ double sI[DLM_MAX_WINDOW];
-  __shared__ double sH[DLM_MAX_WINDOW];
-  __shared__ double shd[kRuleNT / DLM_WAVE];
-  __shared__ int shi[kRuleNT / DLM_WAVE];
+                                           float* __restrict__ score, DepSmem& sm) {
+  auto& sI = sm.sI;
+  auto& sH = sm.sH;
+  auto& shd = sm.shd;
+  auto& shi = sm.shi;
   const int lo = seq_offsets[b], n = seq_offsets[b + 1] - lo;
   const int W = max(0, min(l_max, n));
   const bool warm = has_prev ? has_prev[b] != 0 : true;

@@ -202,8 +202,8 @@ int dlm_cap_select(const void* logits, int dtype, int64_t vocab, int64_t ld,
 /*
  * dlm_dapd_workspace_bytes — device workspace that dlm_dapd_select needs for
  * n_seq sequences of at most m_max masked positions (per sequence: the fp32
- * m_max x m_max attention average, the adjacency bitsets and the ordering
- * keys).  Returns 0 for invalid sizes.
+ * m_max x m_max attention average, the adjacency bitsets, the ordering keys
+ * and one counter that dlm_decide_step uses).  Returns 0 for invalid sizes.
  */
 size_t dlm_dapd_workspace_bytes(int32_t n_seq, int32_t m_max);
 
@@ -305,14 +305,15 @@ int dlm_fixed_block_eligible(const int32_t* masked_pos, const int32_t* seq_offse
                              uint8_t* eligible, void* stream);
 
 /*
- * dlm_decide_step — the whole small-batch decision step in three launches
+ * dlm_decide_step — the whole small-batch decision step in two launches
  * (Fast-dLLM review, Limitations: the gains are small-batch; DepCap summary,
  * Applications: profile the decision for large batches).
  *   launch 1: the statistics of every row and, when DAPD is on, the
  *             attention average, side by side in one grid;
  *   launch 2: Fast-dLLM, the DepCap boundary, CAP and the DAPD scores, each
- *             part in its own workgroups;
- *   launch 3: the DAPD selection.
+ *             part in its own workgroups; the last scores workgroup of a
+ *             sequence to finish (a per-sequence counter in the DAPD
+ *             workspace, zeroed by launch 1) runs its DAPD selection.
  * Each part computes what its own entry point computes.  The statistics are
  * those of dlm_step_stats to its stated accuracy (argmax identical; the
  * streaming order differs, so the floats may differ in the last bits), and

@@ -12,7 +12,7 @@ import oracle
 from _parity import assert_close, host
 from diffusion_lm_unmask_amd import api, synth
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("poisoned_outputs")]
 DEV = "cuda"
 
 
@@ -168,3 +168,49 @@ def test_fused_random_shapes(seed):
         dapd=dict(attn=attn, masked_pos=pos, m_max=rows + int(g.integers(0, 20)),
                   tau=float((0.005, 0.02, 0.1)[int(g.integers(0, 3))])))
     _check(cur, prev, offs, ri, **parts, tag=f"random seed {seed}: B {B} rows {rows} V {V} {dt}")
+
+
+@pytest.mark.parametrize("rows,m_max,variant", [(700, 700, "peak"), (1024, 1024, "cov"),
+                                                (300, 1000, "peak")])
+def test_fused_dapd_long_edge_rich_sequences(rows, m_max, variant):
+    # more than 256 masked rows on a graph with many edges: the step runs the
+    # greedy in a 256-thread workgroup (each wave sorts several runs of 64
+    # keys), the selection call in a 1024-thread one; the commits must agree
+    # bit for bit, and the graph must really have edges that block nodes
+    spec = synth.Spec(f"long{rows}", 11 + rows, 2, rows, 512, torch.bfloat16, 2.0, 0.6, 12.0,
+                      None, n_lh=2, seq_len=rows + 16, attn_sigma=2.5)
+    cur, _, _, ri = synth.logits(spec, DEV)
+    pos, offs = synth.gen_positions(spec, DEV)
+    attn = synth.attention(spec, DEV, variant=variant, masked_pos=pos[:rows])
+    tau = 0.005
+    dapd = dict(attn=attn, masked_pos=pos, m_max=m_max, tau=tau)
+    f = _check(cur, None, offs, ri, dapd=dapd, tag=f"long {rows} m_max {m_max} {variant}")
+    g = api.dapd_select(attn, pos, offs, f["conf"], tau, m_max=m_max, want_sym=True)
+    sym = host(g["sym"])[:, :rows, :rows]
+    off_diag = ~torch.eye(rows, dtype=torch.bool)
+    edges = ((sym > tau) & off_diag).sum(dim=(1, 2))
+    n = host(f["dapd"][1])
+    assert bool((edges > 0).all()) and bool((n < rows).all()) and bool((n > 0).all()), (edges, n)
+
+
+def test_fused_dapd_bad_position_and_empty_sequence():
+    # sequence 0 holds a position outside [0, S) (n_commit -1, nothing
+    # committed), sequence 1 is empty, sequence 2 is ordinary: the step's
+    # tally must reach the same outputs as the selection call
+    spec = synth.Spec("bad", 17, 3, 40, 700, torch.bfloat16, 2.0, 0.6, 12.0, None, n_lh=3,
+                      seq_len=64, attn_sigma=2.0)
+    cur, _, _, _ = synth.logits(spec, DEV)
+    pos = torch.arange(24, 64, device=DEV, dtype=torch.int32)
+    pos_bad = pos.clone()
+    pos_bad[7] = 64  # == S
+    masked = torch.cat([pos_bad, pos])
+    offs = torch.tensor([0, 40, 40, 80], device=DEV, dtype=torch.int32)
+    ri = torch.cat([torch.arange(0, 40), torch.arange(80, 120)]).to(DEV)
+    attn = synth.attention(spec, DEV)
+    for tau in (0.005, 0.5):  # edge-rich, then edgeless
+        dapd = dict(attn=attn, masked_pos=masked, m_max=40, tau=tau)
+        f = _check(cur, None, offs, ri, fast=dict(eligible=None, tau=0.9), dapd=dapd,
+                   tag=f"bad position, empty sequence, tau {tau}")
+        n = host(f["dapd"][1]).tolist()
+        assert n[0] == -1 and n[1] == 0 and n[2] > 0, n
+        assert int(host(f["dapd"][0][:40]).sum()) == 0

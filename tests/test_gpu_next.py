@@ -17,7 +17,7 @@ import oracle
 from _parity import Flags, f64, host, near_any, near_tie
 from diffusion_lm_unmask_amd import api, synth
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("poisoned_outputs")]
 DEV = "cuda"
 
 

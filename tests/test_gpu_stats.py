@@ -13,7 +13,7 @@ import oracle
 from _parity import assert_close, host
 from diffusion_lm_unmask_amd import api, synth
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("poisoned_outputs")]
 DEV = "cuda"
 
 
