@@ -416,16 +416,51 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
                             static_cast<int64_t>(b) * m_max;
     const uint8_t* gedge = reinterpret_cast<const uint8_t*>(ws + L.has_edge) +
                            static_cast<int64_t>(b) * m_max;
-    for (int e = tid; e < M * nw; e += NT) {
-      const int i = e / nw, w = e - i * nw;
-      adj[i][w] = gadj[static_cast<int64_t>(i) * L.words + w];
+    // every load of a batch is issued before its LDS stores, so a thread
+    // with several words (fewer threads, longer sequences) waits for memory
+    // once per batch rather than once per word
+    constexpr int kAU = 8, kKU = 4;
+    const int n_adj = M * nw;
+    for (int e0 = tid; e0 < n_adj; e0 += kAU * NT) {
+      uint64_t v[kAU];
+#pragma unroll
+      for (int u = 0; u < kAU; ++u) {
+        const int e = e0 + u * NT;
+        if (e < n_adj) {
+          const int i = e / nw, w = e - i * nw;
+          v[u] = gadj[static_cast<int64_t>(i) * L.words + w];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kAU; ++u) {
+        const int e = e0 + u * NT;
+        if (e < n_adj) {
+          const int i = e / nw, w = e - i * nw;
+          adj[i][w] = v[u];
+        }
+      }
     }
-    for (int e = tid; e < M; e += NT) {
-      const uint8_t he = gedge[e];
-      keys[e] = gkeys[e];
-      has_edge[e] = he & 1u;
-      any_edge |= he & 1u;
-      bad_pos |= he >> 1;
+    for (int e0 = tid; e0 < M; e0 += kKU * NT) {
+      uint64_t kv[kKU];
+      uint8_t he[kKU];
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) {
+        const int e = e0 + u * NT;
+        if (e < M) {
+          kv[u] = gkeys[e];
+          he[u] = gedge[e];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) {
+        const int e = e0 + u * NT;
+        if (e < M) {
+          keys[e] = kv[u];
+          has_edge[e] = he[u] & 1u;
+          any_edge |= he[u] & 1u;
+          bad_pos |= he[u] >> 1;
+        }
+      }
     }
     if (tid < kWords) chosen[tid] = 0ull;
     for (int e = tid; e < kWords * kWords; e += NT) bmk[e / kWords][e % kWords] = 0ull;

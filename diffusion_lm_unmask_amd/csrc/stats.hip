@@ -8,7 +8,8 @@ namespace {
 
 template <int NT, bool BF16, bool PREV>
 __global__ __launch_bounds__(NT) void k_stats(const StatsArgs p) {
-  stats_block<NT, BF16, PREV>(p, blockIdx.x / p.splits, static_cast<int>(blockIdx.x % p.splits));
+  stats_block<NT, BF16, PREV, NT == 256 ? DLM_STATS_U_BF16_256 : DLM_STATS_U_BF16>(
+      p, blockIdx.x / p.splits, static_cast<int>(blockIdx.x % p.splits));
 }
 
 template <int NT, bool BF16>
@@ -57,8 +58,11 @@ int64_t workspace_rows(size_t bytes) {
 // CU.  Splitting more rows than that costs more than it gains: each split's
 // agent-scope release/acquire writes back / invalidates its XCD's L2 while
 // the other workgroups stream through it.
+#ifndef DLM_STATS_NT256_ROWS
+#define DLM_STATS_NT256_ROWS 4096
+#endif
 void launch_shape(int64_t n_rows, int64_t n_chunks, bool can_split, int* nt, int* splits) {
-  *nt = n_rows >= 4096 ? 256 : 512;
+  *nt = n_rows >= DLM_STATS_NT256_ROWS ? 256 : 512;
   int sp = 1;
   if (can_split && n_rows <= 64) {
     sp = static_cast<int>((256 + n_rows - 1) / n_rows);

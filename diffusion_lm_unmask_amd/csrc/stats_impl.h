@@ -40,10 +40,18 @@ constexpr float kLow = -1e30f;  // running-max sentinel: no finite data seen yet
 
 __device__ __forceinline__ float ex2(float t) { return __builtin_amdgcn_exp2f(t); }
 
-// Tuning: 16-byte chunks per lane per segment, and whether row loads carry the
-// non-temporal hint (streamed once, not worth caching).
+// Tuning: 16-byte chunks per lane per segment (512-thread workgroups, and the
+// 256-thread ones of very many rows), and whether row loads carry the
+// non-temporal hint (streamed once, not worth caching).  Same-process A/B of
+// back-to-back statistics calls: 2 chunks at 512 threads (256 rows: 25.0 us
+// against 25.5 with 3 and 26.6 with 4; 2048 rows: even); 3 at 256 threads
+// (4096 x 151936: 190.9 us against 196.0 with 2 and 192.1 with 4; 65536
+// rows: 4846 against 4868 us).
 #ifndef DLM_STATS_U_BF16
 #define DLM_STATS_U_BF16 2
+#endif
+#ifndef DLM_STATS_U_BF16_256
+#define DLM_STATS_U_BF16_256 3
 #endif
 #ifndef DLM_STATS_NT_LOADS
 #define DLM_STATS_NT_LOADS 1
