@@ -69,6 +69,7 @@ inline int check_dapd(const void* attn, int dtype, int32_t n_lh, int64_t S, int6
   if (late_frac != late_frac || late_tau != late_tau) return DLM_ERR_ARG;
   if (dtype != DLM_BF16 && dtype != DLM_F32) return DLM_ERR_UNSUPPORTED;
   if (m_max > DLM_MAX_SEQ_ROWS || S > 2147483647LL) return DLM_ERR_UNSUPPORTED;
+  if (S > INT64_MAX / S / n_lh) return DLM_ERR_UNSUPPORTED;  // n_lh * S * S elements overflow
   const int64_t maps = static_cast<int64_t>(n_lh) * S * S;
   if (n_seq > 1 && batch_stride < maps) return DLM_ERR_ARG;
   const int es = dtype == DLM_BF16 ? 2 : 4;

@@ -113,7 +113,9 @@ extern "C" {
  *   aligned and ld*element_size is a multiple of 16; otherwise a slower
  *   element-wise path is used.
  * vocab: 1 <= vocab < 2^31; ld >= vocab.
- * row_index (device int64 [n_rows]); n_rows >= 1.
+ * row_index (device int64 [n_rows]); n_rows >= 1.  Each entry must name a row
+ *   of logits (and of prev_logits): 0 <= row_index[r] and the row's vocab
+ *   elements inside the caller's allocation, which the library cannot see.
  * conf, entropy, kl, lse (device f32 [n_rows]); argmax (device int32 [n_rows]).
  * workspace (device, optional): NULL, or at least
  *   dlm_step_stats_workspace_bytes(n_rows) bytes, 16-byte aligned and
@@ -223,8 +225,8 @@ size_t dlm_dapd_workspace_bytes(int32_t n_seq, int32_t m_max);
  * n_commit = -1.  conf (device f32 [rows]) in the same row order.
  * 1 <= m_max <= 1024 bounds the masked positions per sequence (a longer
  * sequence gets n_commit = -1).
- * workspace (device, >= dlm_dapd_workspace_bytes(n_seq, m_max) bytes, 256-byte
- * aligned): scratch, overwritten.
+ * workspace (device, >= dlm_dapd_workspace_bytes(n_seq, m_max) bytes, 16-byte
+ * aligned, else DLM_ERR_ARG): scratch, overwritten.
  * commit (device u8 [rows]); n_commit (device int32 [n_seq]); degree, key
  * (device f32 [rows] or NULL); sym (device f32 [n_seq*m_max*m_max] or NULL):
  * s_ij, NaN pad.

@@ -103,7 +103,9 @@ def test_dapd_validation(L):
     for i, v, code in ((17, need - 1, _lib.ERR_ARG), (8, 1025, _lib.ERR_UNSUPPORTED),
                        (10, math.nan, _lib.ERR_ARG), (4, 10, _lib.ERR_ARG),
                        (16, None, _lib.ERR_ARG), (16, FAKE + 4, _lib.ERR_ARG),
-                       (1, 9, _lib.ERR_UNSUPPORTED), (2, 0, _lib.ERR_ARG)):
+                       (1, 9, _lib.ERR_UNSUPPORTED), (2, 0, _lib.ERR_ARG),
+                       (3, 2**31, _lib.ERR_UNSUPPORTED),
+                       (3, 2**31 - 1, _lib.ERR_UNSUPPORTED)):  # 4 maps of S*S overflow int64
         bad = list(ok)
         bad[i] = v
         assert f(*bad) == code, (i, v)
