@@ -51,6 +51,20 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _len(t, n, name):
+    """Per-row (or per-sequence) tensors must match the count they go with:
+    the kernels index them by row, and the library cannot see their sizes."""
+    if t is not None and t.numel() != n:
+        raise DLMError(f"{name} has {t.numel()} entries, expected {n}")
+
+
+def _vocab(vocab, logits):
+    vocab = logits.shape[1] if vocab is None else int(vocab)
+    if not 1 <= vocab <= logits.shape[1]:
+        raise DLMError(f"vocab must be in [1, {logits.shape[1]}] (the logits' row length)")
+    return vocab
+
+
 def _dtype_code(t):
     if t.dtype == torch.bfloat16:
         return _lib.BF16
@@ -92,7 +106,7 @@ def step_stats(logits: torch.Tensor, prev: torch.Tensor | None = None,
     runs one workgroup per row (no workspace)."""
     ld = _rows2d(logits, "logits")
     dev = logits.device
-    vocab = logits.shape[1] if vocab is None else int(vocab)
+    vocab = _vocab(vocab, logits)
     if prev is not None:
         _rows2d(prev, "prev")
         if prev.dtype != logits.dtype or prev.stride(0) != ld or prev.shape != logits.shape:
@@ -119,6 +133,7 @@ def fastdllm_select(conf, seq_offsets, tau=DEFAULTS["fastdllm_tau"], eligible=No
     dev = _vec(conf, "conf", torch.float32, conf.device).device
     _vec(seq_offsets, "seq_offsets", torch.int32, dev)
     _opt(eligible, "eligible", torch.uint8, dev)
+    _len(eligible, conf.numel(), "eligible")
     n_seq = seq_offsets.numel() - 1
     commit = torch.empty(conf.numel(), device=dev, dtype=torch.uint8)
     n_commit = torch.empty(max(n_seq, 0), device=dev, dtype=torch.int32)
@@ -141,6 +156,7 @@ def depcap_boundary(kl, entropy, seq_offsets, has_prev=None, lam=DEFAULTS["depca
     if entropy.numel() != kl.numel():
         raise DLMError("kl and entropy must have the same length")
     n_seq = seq_offsets.numel() - 1
+    _len(has_prev, n_seq, "has_prev")
     block_len = torch.empty(max(n_seq, 0), device=dev, dtype=torch.int32)
     score = torch.empty(kl.numel(), device=dev, dtype=torch.float32) if want_score else None
     st = _lib.lib().dlm_depcap_boundary(kl.data_ptr(), entropy.data_ptr(), seq_offsets.data_ptr(),
@@ -158,13 +174,16 @@ def cap_select(logits, row_index, seq_offsets, conf, argmax, lse, eligible=None,
     """dlm_cap_select -> dict(commit, n_commit, cand or None, dmat or None)."""
     ld = _rows2d(logits, "logits")
     dev = logits.device
-    vocab = logits.shape[1] if vocab is None else int(vocab)
+    vocab = _vocab(vocab, logits)
     _vec(row_index, "row_index", torch.int64, dev)
     _vec(seq_offsets, "seq_offsets", torch.int32, dev)
     _vec(conf, "conf", torch.float32, dev)
     _vec(argmax, "argmax", torch.int32, dev)
     _vec(lse, "lse", torch.float32, dev)
     _opt(eligible, "eligible", torch.uint8, dev)
+    for t, name in ((row_index, "row_index"), (argmax, "argmax"), (lse, "lse"),
+                    (eligible, "eligible")):
+        _len(t, conf.numel(), name)
     n_seq = seq_offsets.numel() - 1
     k_max = int(k_max)
     commit = torch.empty(conf.numel(), device=dev, dtype=torch.uint8)
@@ -199,6 +218,7 @@ def dapd_select(attn, masked_pos, seq_offsets, conf, tau, m_max=None, workspace=
     _vec(masked_pos, "masked_pos", torch.int32, dev)
     _vec(seq_offsets, "seq_offsets", torch.int32, dev)
     _vec(conf, "conf", torch.float32, dev)
+    _len(masked_pos, conf.numel(), "masked_pos")
     n_seq = seq_offsets.numel() - 1
     if n_seq > B:
         raise DLMError("more sequences than attention batches")
@@ -240,7 +260,9 @@ def dapd_step(attn, masked_pos, seq_offsets, conf, tau, gen_len=None,
     _vec(seq_offsets, "seq_offsets", torch.int32, dev)
     _vec(conf, "conf", torch.float32, dev)
     _opt(gen_len, "gen_len", torch.int32, dev)
+    _len(masked_pos, conf.numel(), "masked_pos")
     n_seq = seq_offsets.numel() - 1
+    _len(gen_len, n_seq, "gen_len")
     if n_seq > B:
         raise DLMError("more sequences than attention batches")
     if m_max is None:
@@ -275,6 +297,7 @@ def _select_common(conf, seq_offsets, eligible):
     _vec(conf, "conf", torch.float32, dev)
     _vec(seq_offsets, "seq_offsets", torch.int32, dev)
     _opt(eligible, "eligible", torch.uint8, dev)
+    _len(eligible, conf.numel(), "eligible")
     n_seq = seq_offsets.numel() - 1
     commit = torch.empty(conf.numel(), device=dev, dtype=torch.uint8)
     n_commit = torch.empty(max(n_seq, 0), device=dev, dtype=torch.int32)
@@ -310,6 +333,7 @@ def fixed_block_eligible(masked_pos, seq_offsets, block_len, gen_start=None):
     _vec(seq_offsets, "seq_offsets", torch.int32, dev)
     _opt(gen_start, "gen_start", torch.int32, dev)
     n_seq = seq_offsets.numel() - 1
+    _len(gen_start, n_seq, "gen_start")
     el = torch.empty(masked_pos.numel(), device=dev, dtype=torch.uint8)
     st = _lib.lib().dlm_fixed_block_eligible(masked_pos.data_ptr(), seq_offsets.data_ptr(), n_seq,
                                              _ptr(gen_start), int(block_len), el.data_ptr(),
@@ -332,7 +356,7 @@ def decide_step(logits, prev=None, seq_offsets=None, row_index=None, vocab=None,
     enabled part, its outputs (fast / depcap / cap / dapd)."""
     ld = _rows2d(logits, "logits")
     dev = logits.device
-    vocab = logits.shape[1] if vocab is None else int(vocab)
+    vocab = _vocab(vocab, logits)
     if prev is not None:
         _rows2d(prev, "prev")
         if prev.dtype != logits.dtype or prev.stride(0) != ld or prev.shape != logits.shape:
@@ -361,12 +385,14 @@ def decide_step(logits, prev=None, seq_offsets=None, row_index=None, vocab=None,
     keep = [row_index, seq_offsets]
     if fast is not None:
         el = _opt(fast.get("eligible"), "eligible", torch.uint8, dev)
+        _len(el, n, "eligible")
         out["fast"] = (torch.empty(n, **u8), torch.empty(max(n_seq, 0), **i32))
         d.fast_eligible, d.fast_tau = _ptr(el), float(fast.get("tau", DEFAULTS["fastdllm_tau"]))
         d.fast_commit, d.fast_n_commit = out["fast"][0].data_ptr(), out["fast"][1].data_ptr()
         keep.append(el)
     if depcap is not None:
         hp = _opt(depcap.get("has_prev"), "has_prev", torch.uint8, dev)
+        _len(hp, n_seq, "has_prev")
         out["depcap"] = (torch.empty(max(n_seq, 0), **i32), torch.empty(n, **f))
         d.depcap_has_prev = _ptr(hp)
         d.depcap_lambda = float(depcap.get("lam", DEFAULTS["depcap_lambda"]))
@@ -379,6 +405,7 @@ def decide_step(logits, prev=None, seq_offsets=None, row_index=None, vocab=None,
         keep.append(hp)
     if cap is not None:
         el = _opt(cap.get("eligible"), "eligible", torch.uint8, dev)
+        _len(el, n, "eligible")
         out["cap"] = (torch.empty(n, **u8), torch.empty(max(n_seq, 0), **i32))
         d.cap_eligible = _ptr(el)
         d.cap_tau_low = float(cap.get("tau_low", DEFAULTS["cap_tau_low"]))
@@ -395,6 +422,7 @@ def decide_step(logits, prev=None, seq_offsets=None, row_index=None, vocab=None,
         if n_seq > attn.shape[0]:
             raise DLMError("more sequences than attention batches")
         pos = _vec(dapd["masked_pos"], "masked_pos", torch.int32, dev)
+        _len(pos, n, "masked_pos")
         m_max = int(dapd["m_max"])
         ws = dapd.get("workspace")
         if ws is None:

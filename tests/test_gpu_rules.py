@@ -454,3 +454,42 @@ def test_rules_random_shapes(seed):
     attn = synth.attention(spec, DEV)
     _dapd_case(attn, pos, offs, gs["conf"], o["conf"], float((0.005, 0.02, 0.1)[int(g.integers(0, 3))]),
                rows + int(g.integers(0, 20)), tag)
+
+
+def test_binding_rejects_mismatched_lengths():
+    # per-row and per-sequence tensors whose lengths do not match: the binding
+    # refuses before any launch (the library cannot see tensor sizes)
+    from diffusion_lm_unmask_amd._lib import DLMError
+    n = 10
+    conf = torch.rand(n, device=DEV)
+    so = torch.tensor([0, 4, n], device=DEV, dtype=torch.int32)
+    el9 = torch.ones(n - 1, device=DEV, dtype=torch.uint8)
+    i32 = dict(device=DEV, dtype=torch.int32)
+    logits = torch.randn(n, 50, device=DEV)
+    ri = torch.arange(n, device=DEV)
+    arg = torch.zeros(n, **i32)
+    lse = torch.zeros(n, device=DEV)
+    attn = torch.rand(2, 1, 16, 16, device=DEV)
+    pos = torch.arange(6, 16, **i32)
+    cases = [
+        lambda: api.fastdllm_select(conf, so, eligible=el9),
+        lambda: api.topk_select(conf, so, 2, eligible=el9),
+        lambda: api.factor_select(conf, so, eligible=el9),
+        lambda: api.depcap_boundary(conf, conf, so, has_prev=torch.ones(3, device=DEV,
+                                                                        dtype=torch.uint8)),
+        lambda: api.cap_select(logits, ri[:-1], so, conf, arg, lse),
+        lambda: api.cap_select(logits, ri, so, conf, arg[:-1], lse),
+        lambda: api.cap_select(logits, ri, so, conf, arg, lse, eligible=el9),
+        lambda: api.cap_select(logits, ri, so, conf, arg, lse, vocab=51),
+        lambda: api.step_stats(logits, vocab=0),
+        lambda: api.dapd_select(attn, pos[:-1], so, conf, 0.01, m_max=8),
+        lambda: api.dapd_step(attn, pos, so, conf, 0.01, gen_len=torch.ones(3, **i32), m_max=8),
+        lambda: api.fixed_block_eligible(pos, so, 4, gen_start=torch.zeros(1, **i32)),
+        lambda: api.decide_step(logits, None, so, row_index=ri, fast=dict(eligible=el9)),
+        lambda: api.decide_step(logits, None, so, row_index=ri,
+                                dapd=dict(attn=attn, masked_pos=pos[:-1], m_max=8)),
+    ]
+    for k, call in enumerate(cases):
+        with pytest.raises(DLMError):
+            call()
+            pytest.fail(f"case {k} was accepted")
