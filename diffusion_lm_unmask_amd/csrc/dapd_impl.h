@@ -281,43 +281,49 @@ __device__ __forceinline__ uint64_t dapd_sym_rows(int b, int rb,
     // on this lane; lane e keeps step e's 16 edge bits.  a[j][i] (the
     // transposed half) is read straight from a: the four teams of a wave read
     // neighbouring columns of the same rows, so a wave load touches 16 lines.
+    // Columns past M read column M - 1 instead (i < M, so M >= 1) and are
+    // masked below: the loads carry no branch and issue back to back.
     float va[16], vt[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int j = c0 + 16 * e + tl;
-      va[e] = vt[e] = 0.f;
-      if (j < M) {
-        va[e] = ar[j];
-        vt[e] = A[static_cast<int64_t>(j) * L.ld + i];
-      }
+      const int jc = min(c0 + 16 * e + tl, M - 1);
+      va[e] = ar[jc];
+      vt[e] = A[static_cast<int64_t>(jc) * L.ld + i];
     }
+    float sv[16];
     uint32_t mine = 0u;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int j = c0 + 16 * e + tl;
-      float sv = NAN;
-      bool edge = false;
-      if (j < M) {
-        sv = 0.5f * (va[e] + vt[e]);
-        if (j != i) {
-          dsum += static_cast<double>(sv);
-          edge = sv > tau;
-        }
-      }
-      if (so && j < m_max) so[j] = sv;
+      sv[e] = j < M ? 0.5f * (va[e] + vt[e]) : NAN;
+      const bool off = j < M && j != i;
+      if (off) dsum += static_cast<double>(sv[e]);
+      const bool edge = off && sv[e] > tau;
       const uint32_t slice = static_cast<uint32_t>(__ballot(edge) >> shift) & 0xffffu;
-      if (e == tl) mine = slice;
+      mine = e == tl ? slice : mine;
+    }
+    if (so) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = c0 + 16 * e + tl;
+        if (j < m_max) so[j] = sv[e];
+      }
     }
     if (c0 + 16 * tl < 64 * nw) adj16[c0 / 16 + tl] = static_cast<uint16_t>(mine);  // zero past M
     any = any || mine != 0u;
   }
   if (so)
     for (int j = 64 * nw + tl; j < m_max; j += 16) so[j] = NAN;
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) dsum += __shfl_xor(dsum, o, 16);  // fixed pattern
+  // over the team's 16 lanes (a DPP row), in a fixed pattern
+  dsum += dlm::xor_val<8>(dsum);
+  dsum += dlm::xor_val<4>(dsum);
+  dsum += dlm::xor_val<2>(dsum);
+  dsum += dlm::xor_val<1>(dsum);
   uint32_t anyb = any ? 1u : 0u;
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) anyb |= __shfl_xor(anyb, o, 16);
+  anyb |= dlm::xor_val<8>(anyb);
+  anyb |= dlm::xor_val<4>(anyb);
+  anyb |= dlm::xor_val<2>(anyb);
+  anyb |= dlm::xor_val<1>(anyb);
   if (tl == 0) {
     const float df = static_cast<float>(dsum);
     const float kk = df * conf_i;
@@ -630,8 +636,8 @@ __device__ __forceinline__ void dapd_scores_select(int b, int wg, int waves, int
   if (wv < waves && rb < blocks) {
     uint64_t t = dapd_sym_rows(b, rb, seq_offsets, masked_pos, S, m_max, conf, tau, ws, L, nullptr,
                                nullptr, nullptr, P, commit);
-    t += __shfl_xor(static_cast<unsigned long long>(t), 16);  // the four teams' lane 0
-    t += __shfl_xor(static_cast<unsigned long long>(t), 32);
+    t += dlm::xor_lane64<16>(t);  // the four teams' lane 0
+    t += dlm::xor_lane64<32>(t);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this wave's rows, before counting in
     if (threadIdx.x % DLM_WAVE == 0) {
       unsigned long long* ctr =

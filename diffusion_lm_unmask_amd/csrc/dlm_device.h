@@ -19,13 +19,6 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, DLM_WAVE);
-  return v;
-}
-
 // Wave reductions on the DPP crossbar (no LDS traffic).  Inside each row of
 // 16 lanes, four steps pair every lane with one lane of the other half of its
 // current group: quad swaps (xor 1, xor 2), then the half-row mirror (i with
@@ -97,24 +90,58 @@ __device__ __forceinline__ uint32_t desc_bits(float f) {
   return ~asc;
 }
 
-// The value of lane (l xor J) for every lane l.  Inside a row of 16 lanes
-// this is DPP on the VALU (no LDS crossbar): xor 1 and xor 2 are quad
+// The value of lane (l xor J) for every lane l, on the VALU (no LDS
+// crossbar).  Inside a row of 16 lanes it is DPP: xor 1 and xor 2 are quad
 // permutations; xor 4 is the half-row mirror (xor 7) followed by the quad
 // reversal (xor 3); xor 8 is the row mirror (xor 15) followed by the half-row
-// mirror (xor 7).  Across rows it is a shuffle.
+// mirror (xor 7).  Across rows it is gfx950's lane swaps, given the value
+// twice: v_permlane16_swap exchanges rows 1 and 3 of its first operand with
+// rows 0 and 2 of its second, so the second result holds each even row's
+// partner and the first each odd row's; v_permlane32_swap does the same for
+// the two halves of the wave.
 template <int J>
 __device__ __forceinline__ int xor_lane(int v) {
+  static_assert(J == 1 || J == 2 || J == 4 || J == 8 || J == 16 || J == 32, "a lane of the wave");
   if constexpr (J == 1) return dpp<0xB1>(v);                  // quad_perm [1,0,3,2]
   else if constexpr (J == 2) return dpp<0x4E>(v);             // quad_perm [2,3,0,1]
   else if constexpr (J == 4) return dpp<0x1B>(dpp<0x141>(v));  // quad_perm [3,2,1,0]
   else if constexpr (J == 8) return dpp<0x141>(dpp<0x140>(v));
-  else return __shfl_xor(v, J, DLM_WAVE);
+  else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return static_cast<int>((__lane_id() & 16) ? r[0] : r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return static_cast<int>((__lane_id() & 32) ? r[0] : r[1]);
+  }
 }
 template <int J>
 __device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
   const uint32_t lo = static_cast<uint32_t>(xor_lane<J>(static_cast<int>(v)));
   const uint32_t hi = static_cast<uint32_t>(xor_lane<J>(static_cast<int>(v >> 32)));
   return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+// xor_lane for any 4- or 8-byte value (the bits move unchanged).
+template <int J, typename T>
+__device__ __forceinline__ T xor_val(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "a 32- or 64-bit value");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, xor_lane<J>(__builtin_bit_cast(int, v)));
+  } else {
+    return __builtin_bit_cast(T, xor_lane64<J>(__builtin_bit_cast(uint64_t, v)));
+  }
+}
+
+// Butterfly sum over the wave (xor 32, 16, ..., 1): every lane ends with the
+// total, in one fixed order of additions.
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+  v += xor_val<32>(v);
+  v += xor_val<16>(v);
+  v += xor_val<8>(v);
+  v += xor_val<4>(v);
+  v += xor_val<2>(v);
+  v += xor_val<1>(v);
+  return v;
 }
 
 // One compare-exchange step of the bitonic network (pair distance J, merge
