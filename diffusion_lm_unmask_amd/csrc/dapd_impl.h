@@ -222,24 +222,33 @@ __host__ __device__ inline Layout layout(int n_seq, int m_max) {
   return L;
 }
 
-// Tuning (build flag): rows per scores workgroup, 16 lanes each (four rows
-// make one wave; sixteen rows measured 6.4 against 5.1 us on the step).
-#ifndef DLM_DAPD_SYM_ROWS
-#define DLM_DAPD_SYM_ROWS 4
+// Tuning (build flag): lanes per scored row, 16 or 32.  A wave scores
+// 64 / DLM_DAPD_TEAM rows (a block), in 256 / DLM_DAPD_TEAM steps per 256
+// columns; a k_dapd_sym workgroup is one wave.  Same-process A/B: 32 lanes
+// (half the steps per wave, twice the waves and the column reads' cache
+// lines) made the fused LLaDA step 0.6 us slower and the fused 8-sequence
+// DAPD part 9 us slower, for 0.8 us off the 8-sequence selection call.
+// (Sixteen rows per workgroup, four waves of 16-lane teams, measured 6.4
+// against 5.1 us on the step.)
+#ifndef DLM_DAPD_TEAM
+#define DLM_DAPD_TEAM 16
 #endif
-constexpr int kSymRows = DLM_DAPD_SYM_ROWS;  // rows per k_dapd_sym workgroup (16 lanes each)
-constexpr int kSymNT = kSymRows * 16;
+constexpr int kTeam = DLM_DAPD_TEAM;
+static_assert(kTeam == 16 || kTeam == 32, "a team is a DPP row or a half wave");
+constexpr int kSymRows = DLM_WAVE / kTeam;  // rows per k_dapd_sym workgroup (one wave)
+constexpr int kSymNT = DLM_WAVE;
+constexpr int kSteps = 256 / kTeam;  // steps per 256 columns
 
 // A row's part of its sequence's tally (the fused step adds them up): bits
 // 16-31 count commits as an edgeless graph makes them, 32-47 rows with an
 // edge, 48-63 rows whose position is out of range (or a sequence longer than
 // m_max).  Bits 0-15 count blocks of kSymRows rows.  Each field stays below
-// 2^16 (at most 1024 rows, at most 256 blocks per sequence).
+// 2^16 (at most 1024 rows, at most 512 blocks per sequence).
 constexpr uint64_t kTallyWG = 1ull, kTallyCommit = 1ull << 16, kTallyEdge = 1ull << 32,
                    kTallyBad = 1ull << 48;
 
 // s = (a + aT)/2 for kSymRows rows per workgroup: adjacency bits (ballot slices),
-// fp64 proxy degree (fixed-pattern 16-lane reduction), ordering key.  Each
+// fp64 proxy degree (fixed-pattern reduction over the team), ordering key.  Each
 // row's masked position is checked here too: has_edge carries bit 1 for a
 // position outside [0, S), which the selection reports.  With `commit`, each
 // row also gets the commit an edgeless graph gives it (a key that is not NaN,
@@ -250,7 +259,7 @@ __device__ __forceinline__ uint64_t dapd_sym_rows(int b, int rb,
     const char* __restrict__ ws, Layout L, float* __restrict__ degree, float* __restrict__ sym,
     float* __restrict__ key_out, Policy P, uint8_t* __restrict__ commit) {
   const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
-  const int team = (threadIdx.x % DLM_WAVE) / 16, tl = threadIdx.x % 16;  // this wave's teams
+  const int team = (threadIdx.x % DLM_WAVE) / kTeam, tl = threadIdx.x % kTeam;  // this wave's teams
   const int i = rb * kSymRows + team;
   const int64_t sbase = static_cast<int64_t>(b) * m_max * m_max;
   if (M > m_max || M < 0) return tl == 0 ? kTallyBad : 0ull;  // over-long: the selection reports
@@ -261,7 +270,7 @@ __device__ __forceinline__ uint64_t dapd_sym_rows(int b, int rb,
       if (key_out) key_out[lo + i] = NAN;
     }
     if (sym)
-      for (int j = tl; j < m_max; j += 16) sym[sbase + static_cast<int64_t>(i) * m_max + j] = NAN;
+      for (int j = tl; j < m_max; j += kTeam) sym[sbase + static_cast<int64_t>(i) * m_max + j] = NAN;
     return 0ull;
   }
   // read now, used at the end: their latency hides behind the row reads
@@ -269,57 +278,66 @@ __device__ __forceinline__ uint64_t dapd_sym_rows(int b, int rb,
   const float conf_i = conf[lo + i];
   const float* A = reinterpret_cast<const float*>(ws + L.a) + static_cast<int64_t>(b) * m_max * L.ld;
   const float* ar = A + static_cast<int64_t>(i) * L.ld;
-  uint16_t* adj16 = reinterpret_cast<uint16_t*>(
+  // the row's adjacency words, written as one kTeam-bit piece per step
+  using Piece = typename dlm::UIntOf<kTeam>::type;
+  Piece* adjp = reinterpret_cast<Piece*>(
       const_cast<char*>(ws) + L.adj + (static_cast<int64_t>(b) * m_max + i) * L.words * 8);
   const int nw = (M + 63) / 64;
   float* so = sym ? sym + sbase + static_cast<int64_t>(i) * m_max : nullptr;
-  const int shift = 16 * (team % (DLM_WAVE / 16));  // this team's lanes in a ballot
   double dsum = 0.0;
   bool any = false;
   for (int c0 = 0; c0 < 64 * nw; c0 += 256) {
-    // step e covers columns c0 + 16e .. c0 + 16e + 15, column c0 + 16e + tl
-    // on this lane; lane e keeps step e's 16 edge bits.  a[j][i] (the
-    // transposed half) is read straight from a: the four teams of a wave read
-    // neighbouring columns of the same rows, so a wave load touches 16 lines.
-    // Columns past M read column M - 1 instead (i < M, so M >= 1) and are
-    // masked below: the loads carry no branch and issue back to back.
-    float va[16], vt[16];
+    // step e covers columns c0 + kTeam*e .. + kTeam - 1, column c0 + kTeam*e
+    // + tl on this lane; lane e keeps step e's kTeam edge bits.  a[j][i] (the
+    // transposed half) is read straight from a: the teams of a wave read
+    // neighbouring columns of the same rows, so a wave load touches kTeam
+    // lines.  Columns past M read column M - 1 instead (i < M, so M >= 1)
+    // and are masked below: the loads carry no branch and issue back to back.
+    float va[kSteps], vt[kSteps];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int jc = min(c0 + 16 * e + tl, M - 1);
+    for (int e = 0; e < kSteps; ++e) {
+      const int jc = min(c0 + kTeam * e + tl, M - 1);
       va[e] = ar[jc];
       vt[e] = A[static_cast<int64_t>(jc) * L.ld + i];
     }
-    float sv[16];
+    float sv[kSteps];
     uint32_t mine = 0u;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = c0 + 16 * e + tl;
+    for (int e = 0; e < kSteps; ++e) {
+      const int j = c0 + kTeam * e + tl;
       sv[e] = j < M ? 0.5f * (va[e] + vt[e]) : NAN;
       const bool off = j < M && j != i;
       if (off) dsum += static_cast<double>(sv[e]);
       const bool edge = off && sv[e] > tau;
-      const uint32_t slice = static_cast<uint32_t>(__ballot(edge) >> shift) & 0xffffu;
+      const uint64_t bal = __ballot(edge);
+      uint32_t slice;  // this team's lanes of the ballot
+      if constexpr (kTeam == 32)
+        slice = team ? static_cast<uint32_t>(bal >> 32) : static_cast<uint32_t>(bal);
+      else
+        slice = static_cast<uint32_t>(bal >> (16 * team)) & 0xffffu;
       mine = e == tl ? slice : mine;
     }
     if (so) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = c0 + 16 * e + tl;
+      for (int e = 0; e < kSteps; ++e) {
+        const int j = c0 + kTeam * e + tl;
         if (j < m_max) so[j] = sv[e];
       }
     }
-    if (c0 + 16 * tl < 64 * nw) adj16[c0 / 16 + tl] = static_cast<uint16_t>(mine);  // zero past M
+    if (tl < kSteps && c0 + kTeam * tl < 64 * nw)
+      adjp[c0 / kTeam + tl] = static_cast<Piece>(mine);  // zero past M
     any = any || mine != 0u;
   }
   if (so)
-    for (int j = 64 * nw + tl; j < m_max; j += 16) so[j] = NAN;
-  // over the team's 16 lanes (a DPP row), in a fixed pattern
+    for (int j = 64 * nw + tl; j < m_max; j += kTeam) so[j] = NAN;
+  // over the team's lanes, in a fixed pattern
+  if constexpr (kTeam == 32) dsum += dlm::xor_val<16>(dsum);
   dsum += dlm::xor_val<8>(dsum);
   dsum += dlm::xor_val<4>(dsum);
   dsum += dlm::xor_val<2>(dsum);
   dsum += dlm::xor_val<1>(dsum);
   uint32_t anyb = any ? 1u : 0u;
+  if constexpr (kTeam == 32) anyb |= dlm::xor_val<16>(anyb);
   anyb |= dlm::xor_val<8>(anyb);
   anyb |= dlm::xor_val<4>(anyb);
   anyb |= dlm::xor_val<2>(anyb);
