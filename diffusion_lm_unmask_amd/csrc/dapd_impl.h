@@ -372,6 +372,7 @@ struct SelSmem {
   uint64_t bmk[kWords][kWords];  // block k (ranks 64k..64k+63): its nodes as a bitset
   uint64_t lmask[kMaxM];         // by rank: lanes of the earlier neighbours in its block
   uint64_t tally;                // the fused step: the sequence's totals
+  uint64_t part[NT / DLM_WAVE];  // the fused step: each wave's tally
   int16_t order[kMaxM];          // node of rank t (-1 - node: NaN key)
   int16_t rank_of[kMaxM];        // rank of each node
   uint8_t has_edge[kMaxM];
@@ -634,9 +635,10 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
 // The fused step's DAPD part, on NT-thread workgroups: `waves` waves of the
 // workgroup each score one block of kSymRows rows of sequence b (blocks
 // waves*wg .. of the sequence's `blocks` blocks; dapd_sym_rows), writing each
-// row's commit as an edgeless graph has it, then add their tallies to the
-// sequence's counter, which the launch before zeroed.  The wave that counts
-// in the last block holds the totals, and its workgroup goes on.  Without an
+// row's commit as an edgeless graph has it; the workgroup then adds its
+// tally to the sequence's counter, which the launch before zeroed.  The
+// workgroup whose count completes the sequence holds the totals and goes on.
+// Without an
 // edge, a bad position, an over-long sequence or the late stage, the commits
 // written are the greedy's (every node whose key is not NaN, and the
 // pre-unmasked rows), so it only writes n_commit.  Otherwise it runs the
@@ -651,18 +653,36 @@ __device__ __forceinline__ void dapd_scores_select(int b, int wg, int waves, int
   const int wv = threadIdx.x / DLM_WAVE, rb = wg * waves + wv;
   if (threadIdx.x == 0) sm.last = 0;
   __syncthreads();
-  if (wv < waves && rb < blocks) {
-    uint64_t t = dapd_sym_rows(b, rb, seq_offsets, masked_pos, S, m_max, conf, tau, ws, L, nullptr,
-                               nullptr, nullptr, P, commit);
-    t += dlm::xor_lane64<16>(t);  // the four teams' lane 0
+  const bool scores = wv < waves && rb < blocks;
+  uint64_t t = 0;
+  if (scores) {
+    t = dapd_sym_rows(b, rb, seq_offsets, masked_pos, S, m_max, conf, tau, ws, L, nullptr,
+                      nullptr, nullptr, P, commit);
+    t += dlm::xor_lane64<16>(t);  // the teams' lane 0
     t += dlm::xor_lane64<32>(t);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this wave's rows, before counting in
-    if (threadIdx.x % DLM_WAVE == 0) {
-      unsigned long long* ctr =
-          reinterpret_cast<unsigned long long*>(const_cast<char*>(ws) + L.tally) + b;
-      const uint64_t mine = t + kTallyWG;
-      const uint64_t tot = atomicAdd(ctr, static_cast<unsigned long long>(mine)) + mine;
-      if ((tot & 0xffffull) == static_cast<uint64_t>(blocks)) {  // one wave per sequence
+    t += kTallyWG;
+  }
+  // count in: the workgroup's tally in one atomic, after one agent-scope
+  // release.  With several scoring waves, each first waits until its stores
+  // are complete, and the workgroup barrier orders them before wave 0's
+  // release (one release and one atomic per workgroup, not per wave: on the
+  // 8-sequence shape the per-wave releases cost 4.6 us).
+  unsigned long long* ctr = reinterpret_cast<unsigned long long*>(const_cast<char*>(ws) + L.tally) + b;
+  if (waves > 1) {
+    __builtin_amdgcn_s_waitcnt(0);
+    if (threadIdx.x % DLM_WAVE == 0) sm.part[wv] = t;
+    __syncthreads();
+    if (wv == 0) {
+      t = 0;
+#pragma unroll
+      for (int w = 0; w < NT / DLM_WAVE; ++w) t += w < waves ? sm.part[w] : 0ull;
+    }
+  }
+  if (wv == 0 && t != 0ull) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // the rows, before counting in
+    if (threadIdx.x == 0) {
+      const uint64_t tot = atomicAdd(ctr, static_cast<unsigned long long>(t)) + t;
+      if ((tot & 0xffffull) == static_cast<uint64_t>(blocks)) {  // one workgroup per sequence
         sm.tally = tot;
         sm.last = 1;
       }
