@@ -26,9 +26,12 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p, int64_t i) {
 // total, bitwise equal across the row because + , max and min are
 // commutative.  The four row totals (lanes 0, 16, 32, 48) are combined in a
 // fixed order and returned to every lane.  Call with all 64 lanes active.
+// Every control used here (quad permutations, row and half-row mirrors)
+// reads a lane of the same row for every lane, so all lanes are written and
+// no old value is needed (v_mov_dpp without an initialising move).
 template <int CTRL>
 __device__ __forceinline__ int dpp(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -154,9 +157,10 @@ __device__ __forceinline__ T wave_sum(T v) {
 template <int J>
 __device__ __forceinline__ uint64_t bitonic_step(uint64_t v, int k, int l) {
   const uint64_t o = xor_lane64<J>(v);
-  // the lower lane of a pair keeps the min in an ascending run
+  // the lower lane of a pair keeps the min in an ascending run: one compare
+  // picks it (equal keys are interchangeable)
   const bool keep_min = ((l & J) == 0) == ((l & k) == 0);
-  return keep_min ? (v < o ? v : o) : (v < o ? o : v);
+  return (v < o) == keep_min ? v : o;
 }
 
 // Ascending bitonic sort of the first n (a power of two <= 64) lanes' keys
