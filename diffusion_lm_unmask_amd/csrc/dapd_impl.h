@@ -15,11 +15,13 @@
 //                flight (more only queues up behind the memory system).  Map
 //                groups are summed in LDS in a fixed order.
 //  k_dapd_sym    grid-wide: s = (a + aT)/2 for 4 rows per workgroup (one
-//                wave), one 16-lane team per row, lane l taking columns l,
-//                l+16, ...; the transposed half a[j][i] is read from a itself
-//                (the four teams of a wave share its cache lines), so no
-//                transposed copy is written; each step's 16 edge bits are one
-//                ballot slice; fp64 proxy degree and the ordering key.
+//                wave), one 16-lane team per row, lane l taking the 16
+//                consecutive columns 16l .. 16l+15 of each 256 (four 16-byte
+//                row loads), whose edge bits are its own 16-bit adjacency
+//                piece; the transposed half a[j][i] is read from a itself
+//                (the four teams of a wave read neighbouring columns of the
+//                same rows), so no transposed copy is written; fp64 proxy
+//                degree and the ordering key.
 //  k_dapd_select one workgroup (1024 threads) per sequence (the fused step
 //                runs it at 256 threads, in the sequence's last scores
 //                workgroup; see dapd_scores_select):
@@ -222,22 +224,13 @@ __host__ __device__ inline Layout layout(int n_seq, int m_max) {
   return L;
 }
 
-// Tuning (build flag): lanes per scored row, 16 or 32.  A wave scores
-// 64 / DLM_DAPD_TEAM rows (a block), in 256 / DLM_DAPD_TEAM steps per 256
-// columns; a k_dapd_sym workgroup is one wave.  Same-process A/B: 32 lanes
-// (half the steps per wave, twice the waves and the column reads' cache
-// lines) made the fused LLaDA step 0.6 us slower and the fused 8-sequence
-// DAPD part 9 us slower, for 0.8 us off the 8-sequence selection call.
-// (Sixteen rows per workgroup, four waves of 16-lane teams, measured 6.4
-// against 5.1 us on the step.)
-#ifndef DLM_DAPD_TEAM
-#define DLM_DAPD_TEAM 16
-#endif
-constexpr int kTeam = DLM_DAPD_TEAM;
-static_assert(kTeam == 16 || kTeam == 32, "a team is a DPP row or a half wave");
-constexpr int kSymRows = DLM_WAVE / kTeam;  // rows per k_dapd_sym workgroup (one wave)
+// Rows per k_dapd_sym workgroup: one wave of four 16-lane teams, one row
+// each.  (Sixteen rows per workgroup, four waves, measured 6.4 against 5.1
+// us on the step; 32-lane teams, half the steps per wave but twice the waves
+// and cache lines, made the fused LLaDA step 0.6 us slower.)
+constexpr int kTeam = 16;
+constexpr int kSymRows = DLM_WAVE / kTeam;
 constexpr int kSymNT = DLM_WAVE;
-constexpr int kSteps = 256 / kTeam;  // steps per 256 columns
 
 // A row's part of its sequence's tally (the fused step adds them up): bits
 // 16-31 count commits as an edgeless graph makes them, 32-47 rows with an
@@ -247,8 +240,9 @@ constexpr int kSteps = 256 / kTeam;  // steps per 256 columns
 constexpr uint64_t kTallyWG = 1ull, kTallyCommit = 1ull << 16, kTallyEdge = 1ull << 32,
                    kTallyBad = 1ull << 48;
 
-// s = (a + aT)/2 for kSymRows rows per workgroup: adjacency bits (ballot slices),
-// fp64 proxy degree (fixed-pattern reduction over the team), ordering key.  Each
+// s = (a + aT)/2 for kSymRows rows per workgroup: adjacency bits (each lane's
+// own 16-column piece), fp64 proxy degree (fixed-pattern reduction over the
+// team), ordering key.  Each
 // row's masked position is checked here too: has_edge carries bit 1 for a
 // position outside [0, S), which the selection reports.  With `commit`, each
 // row also gets the commit an edgeless graph gives it (a key that is not NaN,
@@ -270,7 +264,7 @@ __device__ __forceinline__ uint64_t dapd_sym_rows(int b, int rb,
       if (key_out) key_out[lo + i] = NAN;
     }
     if (sym)
-      for (int j = tl; j < m_max; j += kTeam) sym[sbase + static_cast<int64_t>(i) * m_max + j] = NAN;
+      for (int j = tl; j < m_max; j += 16) sym[sbase + static_cast<int64_t>(i) * m_max + j] = NAN;
     return 0ull;
   }
   // read now, used at the end: their latency hides behind the row reads
@@ -278,66 +272,65 @@ __device__ __forceinline__ uint64_t dapd_sym_rows(int b, int rb,
   const float conf_i = conf[lo + i];
   const float* A = reinterpret_cast<const float*>(ws + L.a) + static_cast<int64_t>(b) * m_max * L.ld;
   const float* ar = A + static_cast<int64_t>(i) * L.ld;
-  // the row's adjacency words, written as one kTeam-bit piece per step
-  using Piece = typename dlm::UIntOf<kTeam>::type;
-  Piece* adjp = reinterpret_cast<Piece*>(
+  // the row's adjacency words, as 16-bit pieces: piece q = columns 16q .. 16q+15
+  uint16_t* adjp = reinterpret_cast<uint16_t*>(
       const_cast<char*>(ws) + L.adj + (static_cast<int64_t>(b) * m_max + i) * L.words * 8);
   const int nw = (M + 63) / 64;
   float* so = sym ? sym + sbase + static_cast<int64_t>(i) * m_max : nullptr;
   double dsum = 0.0;
   bool any = false;
   for (int c0 = 0; c0 < 64 * nw; c0 += 256) {
-    // step e covers columns c0 + kTeam*e .. + kTeam - 1, column c0 + kTeam*e
-    // + tl on this lane; lane e keeps step e's kTeam edge bits.  a[j][i] (the
-    // transposed half) is read straight from a: the teams of a wave read
-    // neighbouring columns of the same rows, so a wave load touches kTeam
-    // lines.  Columns past M read column M - 1 instead (i < M, so M >= 1)
-    // and are masked below: the loads carry no branch and issue back to back.
-    float va[kSteps], vt[kSteps];
+    // lane tl takes the 16 consecutive columns j0 .. j0 + 15 of its piece
+    // c0/16 + tl, so its edge bits are its own piece (no ballots).  Its row
+    // part is four 16-byte loads: from column j0, or, past the row's stride
+    // (columns that are all >= M, read and masked), from its last 16
+    // columns.  a[j][i] (the transposed half) is read straight from a, with
+    // columns past M reading column M - 1 (i < M, so M >= 1); every load is
+    // in range and none is branched.
+    const int j0 = c0 + 16 * tl;
+    float va[16], vt[16];
+    const float4* rp = reinterpret_cast<const float4*>(ar + min(j0, L.ld - 16));
 #pragma unroll
-    for (int e = 0; e < kSteps; ++e) {
-      const int jc = min(c0 + kTeam * e + tl, M - 1);
-      va[e] = ar[jc];
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = rp[q];
+      va[4 * q] = f.x;
+      va[4 * q + 1] = f.y;
+      va[4 * q + 2] = f.z;
+      va[4 * q + 3] = f.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int jc = min(j0 + e, M - 1);
       vt[e] = A[static_cast<int64_t>(jc) * L.ld + i];
     }
-    float sv[kSteps];
+    float sv[16];
     uint32_t mine = 0u;
 #pragma unroll
-    for (int e = 0; e < kSteps; ++e) {
-      const int j = c0 + kTeam * e + tl;
+    for (int e = 0; e < 16; ++e) {
+      const int j = j0 + e;
       sv[e] = j < M ? 0.5f * (va[e] + vt[e]) : NAN;
       const bool off = j < M && j != i;
       if (off) dsum += static_cast<double>(sv[e]);
-      const bool edge = off && sv[e] > tau;
-      const uint64_t bal = __ballot(edge);
-      uint32_t slice;  // this team's lanes of the ballot
-      if constexpr (kTeam == 32)
-        slice = team ? static_cast<uint32_t>(bal >> 32) : static_cast<uint32_t>(bal);
-      else
-        slice = static_cast<uint32_t>(bal >> (16 * team)) & 0xffffu;
-      mine = e == tl ? slice : mine;
+      if (off && sv[e] > tau) mine |= 1u << e;
     }
     if (so) {
 #pragma unroll
-      for (int e = 0; e < kSteps; ++e) {
-        const int j = c0 + kTeam * e + tl;
+      for (int e = 0; e < 16; ++e) {
+        const int j = j0 + e;
         if (j < m_max) so[j] = sv[e];
       }
     }
-    if (tl < kSteps && c0 + kTeam * tl < 64 * nw)
-      adjp[c0 / kTeam + tl] = static_cast<Piece>(mine);  // zero past M
+    if (j0 < 64 * nw) adjp[c0 / 16 + tl] = static_cast<uint16_t>(mine);  // zero past M
     any = any || mine != 0u;
   }
   if (so)
-    for (int j = 64 * nw + tl; j < m_max; j += kTeam) so[j] = NAN;
-  // over the team's lanes, in a fixed pattern
-  if constexpr (kTeam == 32) dsum += dlm::xor_val<16>(dsum);
+    for (int j = 64 * nw + tl; j < m_max; j += 16) so[j] = NAN;
+  // over the team's 16 lanes (a DPP row), in a fixed pattern
   dsum += dlm::xor_val<8>(dsum);
   dsum += dlm::xor_val<4>(dsum);
   dsum += dlm::xor_val<2>(dsum);
   dsum += dlm::xor_val<1>(dsum);
   uint32_t anyb = any ? 1u : 0u;
-  if constexpr (kTeam == 32) anyb |= dlm::xor_val<16>(anyb);
   anyb |= dlm::xor_val<8>(anyb);
   anyb |= dlm::xor_val<4>(anyb);
   anyb |= dlm::xor_val<2>(anyb);

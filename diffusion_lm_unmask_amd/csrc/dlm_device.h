@@ -123,11 +123,6 @@ __device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
   const uint32_t hi = static_cast<uint32_t>(xor_lane<J>(static_cast<int>(v >> 32)));
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
-// The unsigned integer of B bits.
-template <int B> struct UIntOf;
-template <> struct UIntOf<16> { using type = uint16_t; };
-template <> struct UIntOf<32> { using type = uint32_t; };
-
 // xor_lane for any 4- or 8-byte value (the bits move unchanged).
 template <int J, typename T>
 __device__ __forceinline__ T xor_val(T v) {
