@@ -507,7 +507,8 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the decision path shards by sequence with no "
-              "exchange, and this build runs on a single MI355X (use --gpus 1).", file=sys.stderr)
+              "exchange between GPUs, so one GPU's figure is the per-GPU rate (use --gpus 1).",
+              file=sys.stderr)
         return 2
 
     import torch
