@@ -137,7 +137,7 @@ def test_fused_many_sequences_row_gather_and_f32():
     _check(c32, p32, so32, ri32, **d, tag="f32 padded ld", vocab=5000)
 
 
-@pytest.mark.parametrize("seed", [101, 202, 303, 404, 505, 606])
+@pytest.mark.parametrize("seed", [101, 202, 303, 404, 505, 606, 1001, 1017, 1018, 1033, 1047, 1066])
 def test_fused_random_shapes(seed):
     # random batch, rows, vocabulary (often not a multiple of the 16-byte
     # chunk), dtypes, row gathers and rule parameters: every rule bitwise
