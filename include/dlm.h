@@ -226,7 +226,8 @@ size_t dlm_dapd_workspace_bytes(int32_t n_seq, int32_t m_max);
  * 1 <= m_max <= 1024 bounds the masked positions per sequence (a longer
  * sequence gets n_commit = -1).
  * workspace (device, >= dlm_dapd_workspace_bytes(n_seq, m_max) bytes, 16-byte
- * aligned, else DLM_ERR_ARG): scratch, overwritten.
+ * aligned, else DLM_ERR_ARG): scratch, overwritten; calls that overlap in
+ * time (including dlm_decide_step's DAPD part) must not share one.
  * commit (device u8 [rows]); n_commit (device int32 [n_seq]); degree, key
  * (device f32 [rows] or NULL); sym (device f32 [n_seq*m_max*m_max] or NULL):
  * s_ij, NaN pad.
@@ -370,7 +371,8 @@ typedef struct dlm_step_desc {
   float dapd_tau;
   uint8_t* dapd_commit;
   int32_t* dapd_n_commit;
-  void* dapd_workspace;
+  void* dapd_workspace;        /* as dlm_dapd_select's; its per-sequence counters are
+                                  zeroed by launch 1 and counted up in launch 2 */
   size_t dapd_workspace_bytes;
   /* optional hipEvent_t handles (created, timing enabled) that launch 1 sets
    * to its own start and end (hipExtLaunchKernel's start and stop events), to
