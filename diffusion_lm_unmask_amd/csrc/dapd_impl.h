@@ -303,21 +303,26 @@ __device__ __forceinline__ uint64_t dapd_sym_rows(int b, int rb,
       const int jc = min(j0 + e, M - 1);
       vt[e] = A[static_cast<int64_t>(jc) * L.ld + i];
     }
+    // off-diagonal columns below M as a 16-bit lane mask; a masked column
+    // adds +0.0 to the degree (the same sum as skipping it: the terms are
+    // never negative) and sets no edge
+    const int lim = M - j0, di = i - j0;
+    uint32_t valid = lim >= 16 ? 0xffffu : (lim <= 0 ? 0u : (1u << lim) - 1u);
+    if (di >= 0 && di < 16) valid &= ~(1u << di);
     float sv[16];
-    uint32_t mine = 0u;
+    uint32_t gt = 0u;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int j = j0 + e;
-      sv[e] = j < M ? 0.5f * (va[e] + vt[e]) : NAN;
-      const bool off = j < M && j != i;
-      if (off) dsum += static_cast<double>(sv[e]);
-      if (off && sv[e] > tau) mine |= 1u << e;
+      sv[e] = 0.5f * (va[e] + vt[e]);
+      gt |= static_cast<uint32_t>(sv[e] > tau) << e;
+      dsum += static_cast<double>(((valid >> e) & 1u) ? sv[e] : 0.0f);
     }
+    const uint32_t mine = gt & valid;
     if (so) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int j = j0 + e;
-        if (j < m_max) so[j] = sv[e];
+        if (j < m_max) so[j] = j < M ? sv[e] : NAN;
       }
     }
     if (j0 < 64 * nw) adjp[c0 / 16 + tl] = static_cast<uint16_t>(mine);  // zero past M
