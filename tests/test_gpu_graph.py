@@ -71,7 +71,8 @@ def test_fused_step_repeats_bitwise_and_graph_replays_match_eager():
             step.fused(r)
         torch.cuda.synchronize()
         want = step.outputs()
-        for t in (step.conf, step.commit_d, step.commit_c, step.blen):   # clobber the outputs
+        for t in (step.conf, step.commit_d, step.nd, step.commit_c, step.nc, step.commit_f,
+                  step.nf, step.blen):                                    # clobber the outputs
             t.fill_(7)
         scratch.mul_(1.0001).add_(0.5)                                    # unrelated eager work
         torch.cuda.synchronize()
