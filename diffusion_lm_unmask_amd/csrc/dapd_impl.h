@@ -636,10 +636,9 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
 // row's commit as an edgeless graph has it; the workgroup then adds its
 // tally to the sequence's counter, which the launch before zeroed.  The
 // workgroup whose count completes the sequence holds the totals and goes on.
-// Without an
-// edge, a bad position, an over-long sequence or the late stage, the commits
-// written are the greedy's (every node whose key is not NaN, and the
-// pre-unmasked rows), so it only writes n_commit.  Otherwise it runs the
+// Without an edge, a bad position, an over-long sequence or the late stage,
+// the commits written are the greedy's (every node whose key is not NaN, and
+// the pre-unmasked rows), so it only writes n_commit.  Otherwise it runs the
 // greedy, which rewrites every commit.  The outputs are those of k_dapd_sym
 // then k_dapd_select.
 template <int NT>
