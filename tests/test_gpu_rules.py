@@ -426,7 +426,7 @@ def test_dapd_nan_keys_never_chosen():
         assert host(out["commit"])[[3, 17, 31]].sum() == 0
 
 
-@pytest.mark.parametrize("seed", [11, 22, 33, 44])
+@pytest.mark.parametrize("seed", [11, 22, 33, 44, 2007, 2017])
 def test_rules_random_shapes(seed):
     # every rule, decision-only and end to end, on a random shape: batch,
     # rows, ragged vocabulary, dtype, eligibility, thresholds and caps
