@@ -129,7 +129,7 @@ class TimingEvents:
 
 def torch_int_view(t):
     import torch
-    return {torch.float32: torch.int32}.get(t.dtype, t.dtype)
+    return {torch.float32: torch.int32, torch.float64: torch.int64}.get(t.dtype, t.dtype)
 
 
 class LladaStep:
@@ -163,7 +163,7 @@ class LladaStep:
         i32 = dict(device=dev, dtype=torch.int32)
         self.commit_f, self.commit_c, self.commit_d = (torch.empty(n, **u8) for _ in range(3))
         self.nf, self.nc, self.nd, self.blen = (torch.empty(1, **i32) for _ in range(4))
-        self.score = torch.empty(n, **f32)
+        self.score = torch.empty(n, device=dev, dtype=torch.float64)
         self.sws_bytes = int(self.L.dlm_step_stats_workspace_bytes(n))
         self.sws = torch.zeros(self.sws_bytes, **u8)     # zero-filled once; kept zero by the library
         self.ws_bytes = int(self.L.dlm_dapd_workspace_bytes(1, n))

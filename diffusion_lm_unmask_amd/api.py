@@ -148,7 +148,7 @@ def depcap_boundary(kl, entropy, seq_offsets, has_prev=None, lam=DEFAULTS["depca
                     l_min=DEFAULTS["depcap_l_min"], l_max=DEFAULTS["depcap_l_max"],
                     radius=DEFAULTS["depcap_radius"], eps=DEFAULTS["depcap_eps"],
                     want_score=True):
-    """dlm_depcap_boundary -> (block_len int32 [n_seq], score f32 [rows] or None)."""
+    """dlm_depcap_boundary -> (block_len int32 [n_seq], score f64 [rows] or None)."""
     dev = _vec(kl, "kl", torch.float32, kl.device).device
     _vec(entropy, "entropy", torch.float32, dev)
     _vec(seq_offsets, "seq_offsets", torch.int32, dev)
@@ -158,7 +158,7 @@ def depcap_boundary(kl, entropy, seq_offsets, has_prev=None, lam=DEFAULTS["depca
     n_seq = seq_offsets.numel() - 1
     _len(has_prev, n_seq, "has_prev")
     block_len = torch.empty(max(n_seq, 0), device=dev, dtype=torch.int32)
-    score = torch.empty(kl.numel(), device=dev, dtype=torch.float32) if want_score else None
+    score = torch.empty(kl.numel(), device=dev, dtype=torch.float64) if want_score else None
     st = _lib.lib().dlm_depcap_boundary(kl.data_ptr(), entropy.data_ptr(), seq_offsets.data_ptr(),
                                         n_seq, _ptr(has_prev), float(lam), int(l_min), int(l_max),
                                         int(radius), float(eps), block_len.data_ptr(),
@@ -393,7 +393,8 @@ def decide_step(logits, prev=None, seq_offsets=None, row_index=None, vocab=None,
     if depcap is not None:
         hp = _opt(depcap.get("has_prev"), "has_prev", torch.uint8, dev)
         _len(hp, n_seq, "has_prev")
-        out["depcap"] = (torch.empty(max(n_seq, 0), **i32), torch.empty(n, **f))
+        out["depcap"] = (torch.empty(max(n_seq, 0), **i32),
+                         torch.empty(n, device=dev, dtype=torch.float64))
         d.depcap_has_prev = _ptr(hp)
         d.depcap_lambda = float(depcap.get("lam", DEFAULTS["depcap_lambda"]))
         d.depcap_l_min = int(depcap.get("l_min", DEFAULTS["depcap_l_min"]))

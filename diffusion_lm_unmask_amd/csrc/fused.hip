@@ -92,7 +92,7 @@ struct RulesArgs {
   double d_lambda, d_eps;
   int d_lmin, d_lmax, d_radius;
   int32_t* d_block_len;
-  float* d_score;
+  double* d_score;
   // CAP
   const void* logits;
   int64_t ld, vocab;

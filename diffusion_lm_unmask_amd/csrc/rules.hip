@@ -20,7 +20,7 @@ __global__ __launch_bounds__(kRuleNT) void k_depcap(const float* __restrict__ kl
                                                 const uint8_t* __restrict__ has_prev,
                                                 double lambda, int l_min, int l_max, int R,
                                                 double eps, int32_t* __restrict__ block_len,
-                                                float* __restrict__ score) {
+                                                double* __restrict__ score) {
   __shared__ DepSmem sm;
   depcap_seq(blockIdx.x, kl, ent, seq_offsets, has_prev, lambda, l_min, l_max, R, eps, block_len,
              score, sm);
@@ -43,7 +43,7 @@ extern "C" int dlm_depcap_boundary(const float* kl, const float* entropy,
                                    const int32_t* seq_offsets, int32_t n_seq,
                                    const uint8_t* has_prev, double lambda, int32_t l_min,
                                    int32_t l_max, int32_t smooth_radius, double eps,
-                                   int32_t* block_len, float* score, void* stream) {
+                                   int32_t* block_len, double* score, void* stream) {
   const int rc = dlmh::check_depcap(kl, entropy, seq_offsets, n_seq, lambda, l_min, l_max,
                                     smooth_radius, eps, block_len);
   if (rc != DLM_OK) return rc;

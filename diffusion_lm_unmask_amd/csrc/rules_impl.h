@@ -61,14 +61,14 @@ struct DepSmem {
 
 // DepGA-Block boundary.  Window W = min(l_max, rows); box smoothing of
 // radius R clipped to the window, division by the window mean (+eps),
-// S_k = I~_k - lambda*H~_k in fp64 rounded to f32; k* = first f32 S_k < 0.
+// S_k = I~_k - lambda*H~_k in fp64, stored in fp64; k* = first S_k < 0.
 __device__ __forceinline__ void depcap_seq(int b, const float* __restrict__ kl,
                                            const float* __restrict__ ent,
                                            const int32_t* __restrict__ seq_offsets,
                                            const uint8_t* __restrict__ has_prev,
                                            double lambda, int l_min, int l_max, int R,
                                            double eps, int32_t* __restrict__ block_len,
-                                           float* __restrict__ score, DepSmem& sm) {
+                                           double* __restrict__ score, DepSmem& sm) {
   auto& sI = sm.sI;
   auto& sH = sm.sH;
   auto& shd = sm.shd;
@@ -117,9 +117,9 @@ __device__ __forceinline__ void depcap_seq(int b, const float* __restrict__ kl,
   for (int j = 0; j < KPT; ++j) {
     const int k = threadIdx.x + j * kRuleNT;
     if (k < W) {
-      const float s = static_cast<float>(ib[j] / (mi + eps) - lambda * (hb[j] / (mh + eps)));
+      const double s = ib[j] / (mi + eps) - lambda * (hb[j] / (mh + eps));
       if (score) score[lo + k] = s;
-      if (s < 0.f) first = min(first, k);
+      if (s < 0.0) first = min(first, k);
     }
   }
   const int ks = dlm::block_min_i<kRuleNT>(first, shi);

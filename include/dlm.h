@@ -159,18 +159,18 @@ int dlm_fastdllm_select(const float* conf, const uint8_t* eligible, const int32_
  * l_min (clipped to W_b) on cold start (has_prev[b] == 0).
  * Readings (the pages give no formula): I-bar_k = mean of I_j over
  * j in [k-r, k+r] clipped to the window; I~_k = I-bar_k / (mean_k I-bar + eps);
- * the same for H.  S_k is computed in fp64, rounded to f32, and the
- * decision is taken on the f32 value (NaN is not negative).
+ * the same for H.  S_k is computed, returned and compared with 0 in fp64
+ * (NaN is not negative), so the returned score is the value decided on.
  * kl, entropy (device f32 [rows]); seq_offsets (device int32 [n_seq+1]);
  * has_prev (device u8 [n_seq] or NULL = all warm); 0 <= l_min <= l_max <= 1024;
  * smooth_radius >= 0; eps >= 0; lambda, eps not NaN.
- * block_len (device int32 [n_seq]); score (device f32 [rows] or NULL):
+ * block_len (device int32 [n_seq]); score (device f64 [rows] or NULL):
  * S_k for the first W_b rows of a warm sequence, NaN elsewhere.
  */
 int dlm_depcap_boundary(const float* kl, const float* entropy, const int32_t* seq_offsets,
                         int32_t n_seq, const uint8_t* has_prev, double lambda, int32_t l_min,
                         int32_t l_max, int32_t smooth_radius, double eps, int32_t* block_len,
-                        float* score, void* stream);
+                        double* score, void* stream);
 
 /*
  * dlm_cap_select — [DepCap, Methodology bullets 4-6; Technical Contribution;
@@ -355,7 +355,7 @@ typedef struct dlm_step_desc {
   int32_t depcap_l_min, depcap_l_max, depcap_radius;
   double depcap_eps;
   int32_t* depcap_block_len;
-  float* depcap_score;
+  double* depcap_score;
   /* CAP (dlm_cap_select); skipped when cap_commit is NULL */
   const uint8_t* cap_eligible;
   float cap_tau_low, cap_tau_high, cap_gamma;

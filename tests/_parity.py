@@ -3,8 +3,9 @@
 Tolerances: statistics (conf, entropy, KL, lse, S_k, D_ij, s_ij, degree) within
 1e-5 absolute of the fp64 oracle; argmax bit-exact.  Decisions are compared two
 ways:
-  decision-only  the oracle's rule applied to the GPU's exported fp32 scores must
-                 reproduce the GPU's masks and boundaries bit for bit, always;
+  decision-only  the oracle's rule applied to the GPU's exported scores (fp32;
+                 S_k in fp64) must reproduce the GPU's masks and boundaries bit
+                 for bit, always;
   end-to-end     GPU decisions from GPU statistics vs oracle decisions from oracle
                  statistics.  A differing sequence is accepted (and counted as
                  flagged) only if decision-only parity holds for it and the oracle

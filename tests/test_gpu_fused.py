@@ -41,8 +41,9 @@ def _same(a, b, name):
     if a is None or b is None:
         assert a is None and b is None, name
         return
-    av = a.view(torch.int32) if a.dtype == torch.float32 else a
-    bv = b.view(torch.int32) if b.dtype == torch.float32 else b
+    bits = {torch.float32: torch.int32, torch.float64: torch.int64}   # NaN equals NaN
+    assert a.dtype == b.dtype, name
+    av, bv = a.view(bits.get(a.dtype, a.dtype)), b.view(bits.get(b.dtype, b.dtype))
     assert torch.equal(av, bv), f"{name}: fused differs from the individual call"
 
 

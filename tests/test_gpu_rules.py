@@ -1,6 +1,6 @@
 """GPU parity of the four selection rules (marked gpu).
 
-Each rule is checked decision-only (oracle rule on the GPU's exported fp32
+Each rule is checked decision-only (oracle rule on the GPU's exported
 scores must equal the GPU decision bit for bit) and end-to-end (GPU decisions
 from GPU statistics vs oracle decisions from oracle statistics, differences
 allowed only at near-threshold quantities, counted as flagged).  Exported
@@ -92,7 +92,7 @@ def _depcap_case(g, o, so, R, tag, has_prev=None):
     # scores from the GPU's own KL/H, in fp64: within 1e-5
     S_from_g = oracle.depcap_scores(f64(kl_g), f64(h_g), so_h, R["l_max"], R["lam"], 1, 1e-12, hp)
     assert_close(S_g, S_from_g, f"{tag} S (gpu stats)")
-    # decision-only: oracle's boundary rule on the GPU's f32 scores
+    # decision-only: oracle's boundary rule on the GPU's fp64 scores
     dec = oracle.depcap_decide(f64(S_g), so_h, R["l_max"], R["l_min"], hp)
     assert np.array_equal(host(L_g).numpy(), dec), f"{tag}: decision-only"
     # end-to-end
@@ -131,6 +131,36 @@ def test_depcap_edges():
     ref, Sref = oracle.depcap_boundary(f64(kl), f64(h), host(so).numpy(), 128, 4, 1.2)
     assert host(L).tolist() == list(ref)
     assert_close(S, Sref, "edge S")
+
+
+@pytest.mark.parametrize("l_min", [0, 8, 1000, 1024])
+def test_depcap_max_window(l_min):
+    # the largest window (l_max = 1024, four scores per lane) on sequences
+    # longer than, equal to and shorter than it, one empty and one single row;
+    # KL and entropy drawn directly: a head of high-KL, zero-entropy rows, then
+    # a quiet stretch (the first negative score), then noise, so the
+    # boundaries fall inside the window, at its last row and past it
+    lens = [1100, 1024, 1023, 600, 0, 1, 1500, 1030]
+    heads = [517, 1023, 90, 333, 0, 0, 1200, 1022]
+    so_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    g = np.random.default_rng(4242 + l_min)
+    n = int(so_h[-1])
+    kl = g.exponential(0.3, n).astype(np.float32)
+    h = g.uniform(0.0, 4.0, n).astype(np.float32)
+    for lo, q in zip(so_h[:-1], heads):
+        kl[lo:lo + q] = 1.0 + g.exponential(0.3, q)
+        h[lo:lo + q] = 0.0
+        kl[lo + q:lo + q + 40] *= 0.01
+        h[lo + q:lo + q + 40] += 3.0
+    so = torch.from_numpy(so_h).to(DEV)
+    gs = dict(kl=torch.from_numpy(kl).to(DEV), entropy=torch.from_numpy(h).to(DEV))
+    os_ = dict(kl=kl.astype(np.float64), entropy=h.astype(np.float64))
+    R = dict(lam=1.2, l_min=l_min, l_max=1024)
+    L = _depcap_case(gs, os_, so, R, f"max window l_min={l_min}")
+    hp = torch.tensor([b % 3 != 2 for b in range(len(lens))], device=DEV, dtype=torch.uint8)
+    _depcap_case(gs, os_, so, R, f"max window l_min={l_min} mixed-cold", has_prev=hp)
+    Lh = host(L).numpy()
+    assert Lh[4] == 0 and np.all(Lh <= np.minimum(lens, 1024))
 
 
 # -------------------------------------------------------------- CAP-Decoding
