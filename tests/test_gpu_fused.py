@@ -194,6 +194,26 @@ def test_fused_dapd_long_edge_rich_sequences(rows, m_max, variant):
     assert bool((edges > 0).all()) and bool((n < rows).all()) and bool((n > 0).all()), (edges, n)
 
 
+@pytest.mark.parametrize("rows", [1024, 700])
+def test_fused_every_rule_at_the_per_sequence_limits(rows):
+    # all four rules on sequences of up to 1024 rows with the previous step:
+    # DepCap at its largest window (l_max 1024), CAP at its largest K_max
+    # (128, the pool filled by a low tau_low) and DAPD at m_max 1024; every
+    # fused output must equal its entry point's bit for bit
+    spec = synth.Spec(f"limits{rows}", 29 + rows, 2, rows, 384, torch.bfloat16, 2.0, 0.6, 12.0,
+                      0.5, n_lh=2, seq_len=rows + 8, attn_sigma=2.5)
+    cur, prev, so, ri = synth.logits(spec, DEV)
+    pos, offs = synth.gen_positions(spec, DEV)
+    attn = synth.attention(spec, DEV)
+    parts = dict(fast=dict(eligible=None, tau=0.9),
+                 depcap=dict(lam=1.2, l_min=8, l_max=1024),
+                 cap=dict(eligible=None, tau_low=0.05, tau_high=0.95, gamma=-16.0, k_max=128),
+                 dapd=dict(attn=attn, masked_pos=pos, m_max=1024, tau=0.005))
+    f = _check(cur, prev, offs, ri, **parts, tag=f"limits {rows}")
+    assert bool((host(f["cap"][1]) > 0).all()) and bool((host(f["dapd"][1]) > 0).all())
+    assert bool((host(f["depcap"][0]) >= 8).all())
+
+
 def test_fused_dapd_bad_position_and_empty_sequence():
     # sequence 0 holds a position outside [0, S) (n_commit -1, nothing
     # committed), sequence 1 is empty, sequence 2 is ordinary: the step's
