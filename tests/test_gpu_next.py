@@ -230,3 +230,76 @@ def test_dapd_step_late_fallback_and_scattered():
     for pre in (True, False):
         _dapd_step_case(attn, pos[:77].contiguous(), so, conf, gen_len, 0.02, 45,
                         f"scattered pre={pre}", pre_unmask=pre)
+
+
+# ------------------------------------------------------------ random shapes
+
+@pytest.mark.parametrize("seed", [71, 72, 73, 74, 75, 76])
+def test_schedules_random_shapes(seed):
+    # top-K, factor decoding and fixed-block eligibility on random sequence
+    # lengths (empty, single rows, the 1024-row limit and past it), random
+    # K, f, block length and eligibility: bit for bit against the oracle
+    g = np.random.default_rng(seed)
+    lens = [int(x) for x in g.choice([0, 1, 2, 31, 64, 65, 255, 511, 1023, 1024, 1025, 1300],
+                                     int(g.integers(1, 9)))]
+    so = _csr(lens)
+    n = int(so[-1])
+    conf = _conf_mix(n, seed)
+    el = (g.random(n) < g.uniform(0.1, 1.0)).astype(np.uint8) if g.integers(0, 2) else None
+    so_d, conf_d = torch.from_numpy(so).to(DEV), torch.from_numpy(conf).to(DEV)
+    el_d = None if el is None else torch.from_numpy(el).to(DEV)
+    over = [b for b, m in enumerate(lens) if m > 1024]
+    ok = [b for b, m in enumerate(lens) if m <= 1024]
+    k = int(g.integers(1, 1100))
+    c_g, n_g = (host(x).numpy() for x in api.topk_select(conf_d, so_d, k, eligible=el_d))
+    c_o, n_o = oracle.topk_select(conf.astype(np.float64), so, k, eligible=el)
+    f = float(np.float32(g.choice([1e-3, 0.1, 0.5, 1.0, 2.0, 10.0, 100.0]) * g.uniform(0.5, 1.5)))
+    fc_g, fn_g, ce_g = (host(x).numpy() for x in api.factor_select(conf_d, so_d, f,
+                                                                   eligible=el_d))
+    fc_o, fn_o, ce_o = oracle.factor_select(conf.astype(np.float64), so, f, eligible=el)
+    tag = f"seed {seed}: lens {lens} k {k} f {f:.4g} eligible {el is not None}"
+    for b in ok:
+        lo, hi = so[b], so[b + 1]
+        assert np.array_equal(c_g[lo:hi], c_o[lo:hi]) and n_g[b] == n_o[b], f"{tag} top-K seq {b}"
+        assert np.array_equal(fc_g[lo:hi], fc_o[lo:hi]) and fn_g[b] == fn_o[b] and \
+            ce_g[b] == ce_o[b], f"{tag} factor seq {b}"
+    for b in over:
+        lo, hi = so[b], so[b + 1]
+        assert n_g[b] == -1 and c_g[lo:hi].sum() == 0, f"{tag} top-K over-long seq {b}"
+        assert fn_g[b] == -1 and fc_g[lo:hi].sum() == 0 and ce_g[b] == 0, f"{tag} factor seq {b}"
+    # fixed-block eligibility over sorted positions starting near gen_start
+    gs = g.integers(0, 2000, len(lens)).astype(np.int32)
+    pos = np.concatenate([np.sort(g.choice(np.arange(max(0, s - 30), s + 3 * m + 40), m,
+                                           replace=False)) if m else np.zeros(0, np.int64)
+                          for m, s in zip(lens, gs)]).astype(np.int32)
+    L = int(g.choice([1, 16, 32, 64, 100]))
+    for start in (gs, None):
+        el_g = api.fixed_block_eligible(torch.from_numpy(pos).to(DEV), so_d, L,
+                                        gen_start=None if start is None
+                                        else torch.from_numpy(start).to(DEV))
+        el_o = oracle.fixed_block_eligible(pos, so, L, gen_start=start)
+        assert np.array_equal(host(el_g).numpy(), el_o), f"{tag} fixed block L {L}"
+    print(f"[schedules] {tag}: top-K {n_g.tolist()} factor {fn_g.tolist()}")
+
+
+@pytest.mark.parametrize("seed", [81, 82, 83, 84])
+def test_dapd_step_random_shapes(seed):
+    # the full DAPD step on random shapes: batch, rows, maps, S, attention
+    # dtype, tau, generation lengths on both sides of the late-stage switch,
+    # pre-unmask on and off, exact-1.0 confidences planted
+    g = np.random.default_rng(seed)
+    B, rows = int(g.integers(1, 5)), int(g.integers(2, 129))
+    spec = synth.Spec(f"dsrand{seed}", seed, B, rows, 64, torch.bfloat16, 2.0, 0.5, 12.0, None,
+                      n_lh=int(g.integers(1, 9)), seq_len=rows + int(g.integers(0, 40)),
+                      attn_sigma=float(g.uniform(0.5, 3.0)),
+                      attn_dtype=(torch.bfloat16, torch.float32)[int(g.integers(0, 2))])
+    attn = synth.attention(spec, DEV)
+    pos, offs = synth.gen_positions(spec, DEV)
+    conf = torch.from_numpy(g.random(B * rows).astype(np.float32)).to(DEV)
+    conf[torch.from_numpy(g.random(B * rows) < 0.05).to(DEV)] = 1.0
+    gen_len = torch.from_numpy(g.integers(rows, 3 * rows + 2, B).astype(np.int32)).to(DEV)
+    tau = float((0.005, 0.02, 0.1)[int(g.integers(0, 3))])
+    m_max = rows + int(g.integers(0, 20))
+    for pre in (True, False):
+        _dapd_step_case(attn, pos, offs, conf, gen_len, tau, m_max,
+                        f"random seed {seed} B {B} rows {rows} pre={pre}", pre_unmask=pre)
