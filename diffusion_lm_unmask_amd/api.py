@@ -51,6 +51,25 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+_PLACEHOLDER: dict = {}
+
+
+def _rows(t):
+    """Pointer to a per-row tensor.  A tensor with no rows has no storage
+    (data_ptr 0), which the library refuses as a missing argument.  With no
+    rows the kernels never dereference it, so the address of a small
+    per-device placeholder stands in, and the launch still writes every
+    sequence's outputs (an empty sequence commits nothing)."""
+    if t is None:
+        return None
+    if t.numel():
+        return t.data_ptr()
+    ph = _PLACEHOLDER.get(t.device)
+    if ph is None:
+        ph = _PLACEHOLDER[t.device] = torch.zeros(64, device=t.device, dtype=torch.int64)
+    return ph.data_ptr()
+
+
 def _len(t, n, name):
     """Per-row (or per-sequence) tensors must match the count they go with:
     the kernels index them by row, and the library cannot see their sizes."""
@@ -137,8 +156,8 @@ def fastdllm_select(conf, seq_offsets, tau=DEFAULTS["fastdllm_tau"], eligible=No
     n_seq = seq_offsets.numel() - 1
     commit = torch.empty(conf.numel(), device=dev, dtype=torch.uint8)
     n_commit = torch.empty(max(n_seq, 0), device=dev, dtype=torch.int32)
-    st = _lib.lib().dlm_fastdllm_select(conf.data_ptr(), _ptr(eligible), seq_offsets.data_ptr(),
-                                        n_seq, float(tau), commit.data_ptr(), n_commit.data_ptr(),
+    st = _lib.lib().dlm_fastdllm_select(_rows(conf), _ptr(eligible), seq_offsets.data_ptr(),
+                                        n_seq, float(tau), _rows(commit), n_commit.data_ptr(),
                                         _stream(conf))
     _lib.check(st, "dlm_fastdllm_select")
     return commit, n_commit
@@ -159,7 +178,7 @@ def depcap_boundary(kl, entropy, seq_offsets, has_prev=None, lam=DEFAULTS["depca
     _len(has_prev, n_seq, "has_prev")
     block_len = torch.empty(max(n_seq, 0), device=dev, dtype=torch.int32)
     score = torch.empty(kl.numel(), device=dev, dtype=torch.float64) if want_score else None
-    st = _lib.lib().dlm_depcap_boundary(kl.data_ptr(), entropy.data_ptr(), seq_offsets.data_ptr(),
+    st = _lib.lib().dlm_depcap_boundary(_rows(kl), _rows(entropy), seq_offsets.data_ptr(),
                                         n_seq, _ptr(has_prev), float(lam), int(l_min), int(l_max),
                                         int(radius), float(eps), block_len.data_ptr(),
                                         _ptr(score), _stream(kl))
@@ -191,11 +210,11 @@ def cap_select(logits, row_index, seq_offsets, conf, argmax, lse, eligible=None,
     cand = torch.empty(max(n_seq, 0), k_max, device=dev, dtype=torch.int32) if want_cand else None
     dmat = (torch.empty(max(n_seq, 0), k_max, k_max, device=dev, dtype=torch.float32)
             if want_dmat else None)
-    st = _lib.lib().dlm_cap_select(logits.data_ptr(), _dtype_code(logits), vocab, ld,
-                                   row_index.data_ptr(), seq_offsets.data_ptr(), n_seq,
-                                   conf.data_ptr(), argmax.data_ptr(), lse.data_ptr(),
+    st = _lib.lib().dlm_cap_select(_rows(logits), _dtype_code(logits), vocab, ld,
+                                   _rows(row_index), seq_offsets.data_ptr(), n_seq,
+                                   _rows(conf), _rows(argmax), _rows(lse),
                                    _ptr(eligible), float(tau_low), float(tau_high), float(gamma),
-                                   k_max, commit.data_ptr(), n_commit.data_ptr(), _ptr(cand),
+                                   k_max, _rows(commit), n_commit.data_ptr(), _ptr(cand),
                                    _ptr(dmat), _stream(logits))
     _lib.check(st, "dlm_cap_select")
     return {"commit": commit, "n_commit": n_commit, "cand": cand, "dmat": dmat}
@@ -236,8 +255,8 @@ def dapd_select(attn, masked_pos, seq_offsets, conf, tau, m_max=None, workspace=
     key = torch.empty(n, **f) if want_key else None
     sym = torch.empty(max(n_seq, 0), m_max, m_max, **f) if want_sym else None
     st = _lib.lib().dlm_dapd_select(attn.data_ptr(), _dtype_code(attn), n_lh, S, n_lh * S * S,
-                                    masked_pos.data_ptr(), seq_offsets.data_ptr(), n_seq,
-                                    int(m_max), conf.data_ptr(), float(tau), commit.data_ptr(),
+                                    _rows(masked_pos), seq_offsets.data_ptr(), n_seq,
+                                    int(m_max), _rows(conf), float(tau), _rows(commit),
                                     n_commit.data_ptr(), _ptr(degree), _ptr(sym), _ptr(key),
                                     workspace.data_ptr(), workspace.numel(), _stream(attn))
     _lib.check(st, "dlm_dapd_select")
@@ -280,10 +299,10 @@ def dapd_step(attn, masked_pos, seq_offsets, conf, tau, gen_len=None,
     key = torch.empty(n, **f) if want_key else None
     sym = torch.empty(max(n_seq, 0), m_max, m_max, **f) if want_sym else None
     st = _lib.lib().dlm_dapd_step(attn.data_ptr(), _dtype_code(attn), n_lh, S, n_lh * S * S,
-                                  masked_pos.data_ptr(), seq_offsets.data_ptr(), n_seq,
-                                  int(m_max), conf.data_ptr(), float(tau), _ptr(gen_len),
+                                  _rows(masked_pos), seq_offsets.data_ptr(), n_seq,
+                                  int(m_max), _rows(conf), float(tau), _ptr(gen_len),
                                   float(late_frac), float(late_tau), int(bool(pre_unmask)),
-                                  commit.data_ptr(), n_commit.data_ptr(), stage.data_ptr(),
+                                  _rows(commit), n_commit.data_ptr(), stage.data_ptr(),
                                   _ptr(degree), _ptr(sym), _ptr(key), workspace.data_ptr(),
                                   workspace.numel(), _stream(attn))
     _lib.check(st, "dlm_dapd_step")
@@ -308,8 +327,8 @@ def factor_select(conf, seq_offsets, f=DEFAULTS["factor_f"], eligible=None):
     """dlm_factor_select: returns commit, n_commit and the Theorem-1 certificate."""
     dev, n_seq, commit, n_commit = _select_common(conf, seq_offsets, eligible)
     cert = torch.empty(max(n_seq, 0), device=dev, dtype=torch.uint8)
-    st = _lib.lib().dlm_factor_select(conf.data_ptr(), _ptr(eligible), seq_offsets.data_ptr(),
-                                      n_seq, float(f), commit.data_ptr(), n_commit.data_ptr(),
+    st = _lib.lib().dlm_factor_select(_rows(conf), _ptr(eligible), seq_offsets.data_ptr(),
+                                      n_seq, float(f), _rows(commit), n_commit.data_ptr(),
                                       cert.data_ptr(), _stream(conf))
     _lib.check(st, "dlm_factor_select")
     return commit, n_commit, cert
@@ -318,8 +337,8 @@ def factor_select(conf, seq_offsets, f=DEFAULTS["factor_f"], eligible=None):
 def topk_select(conf, seq_offsets, k, eligible=None):
     """dlm_topk_select: the k most confident eligible rows per sequence."""
     dev, n_seq, commit, n_commit = _select_common(conf, seq_offsets, eligible)
-    st = _lib.lib().dlm_topk_select(conf.data_ptr(), _ptr(eligible), seq_offsets.data_ptr(),
-                                    n_seq, int(k), commit.data_ptr(), n_commit.data_ptr(),
+    st = _lib.lib().dlm_topk_select(_rows(conf), _ptr(eligible), seq_offsets.data_ptr(),
+                                    n_seq, int(k), _rows(commit), n_commit.data_ptr(),
                                     _stream(conf))
     _lib.check(st, "dlm_topk_select")
     return commit, n_commit
@@ -335,8 +354,8 @@ def fixed_block_eligible(masked_pos, seq_offsets, block_len, gen_start=None):
     n_seq = seq_offsets.numel() - 1
     _len(gen_start, n_seq, "gen_start")
     el = torch.empty(masked_pos.numel(), device=dev, dtype=torch.uint8)
-    st = _lib.lib().dlm_fixed_block_eligible(masked_pos.data_ptr(), seq_offsets.data_ptr(), n_seq,
-                                             _ptr(gen_start), int(block_len), el.data_ptr(),
+    st = _lib.lib().dlm_fixed_block_eligible(_rows(masked_pos), seq_offsets.data_ptr(), n_seq,
+                                             _ptr(gen_start), int(block_len), _rows(el),
                                              _stream(masked_pos))
     _lib.check(st, "dlm_fixed_block_eligible")
     return el

@@ -303,3 +303,38 @@ def test_dapd_step_random_shapes(seed):
     for pre in (True, False):
         _dapd_step_case(attn, pos, offs, conf, gen_len, tau, m_max,
                         f"random seed {seed} B {B} rows {rows} pre={pre}", pre_unmask=pre)
+
+
+def test_every_rule_with_all_sequences_empty():
+    # a batch whose sequences are all empty (nothing left to decode): the
+    # per-row tensors have no storage, and every rule call still runs and
+    # reports each sequence (nothing committed), as the oracle does
+    so = torch.zeros(4, device=DEV, dtype=torch.int32)          # three empty sequences
+    so_h = host(so).numpy()
+    e32 = torch.empty(0, device=DEV, dtype=torch.float32)
+    ei32 = torch.empty(0, device=DEV, dtype=torch.int32)
+    c, n = api.fastdllm_select(e32, so, 0.9)
+    assert c.numel() == 0 and host(n).tolist() == [0, 0, 0]
+    c, n = api.topk_select(e32, so, 4)
+    assert host(n).tolist() == list(oracle.topk_select(np.zeros(0), so_h, 4)[1]) == [0, 0, 0]
+    c, n, ce = api.factor_select(e32, so, 1.0)
+    _, n_o, ce_o = oracle.factor_select(np.zeros(0), so_h, 1.0)
+    assert host(n).tolist() == list(n_o) and host(ce).tolist() == list(ce_o)
+    L, S = api.depcap_boundary(e32, e32, so, l_min=8, l_max=128)
+    assert host(L).tolist() == list(oracle.depcap_boundary(np.zeros(0), np.zeros(0), so_h, 128,
+                                                           8, 1.2)[0]) == [0, 0, 0]
+    logits = torch.randn(5, 64, device=DEV)
+    r = api.cap_select(logits, torch.empty(0, device=DEV, dtype=torch.int64), so, e32, ei32, e32,
+                       k_max=8)
+    assert host(r["n_commit"]).tolist() == [0, 0, 0]
+    el = api.fixed_block_eligible(ei32, so, 32)
+    assert el.numel() == 0
+    attn = torch.rand(3, 2, 16, 16, device=DEV)
+    r = api.dapd_select(attn, ei32, so, e32, 0.01, m_max=16)
+    assert host(r["n_commit"]).tolist() == [0, 0, 0]
+    gen_len = torch.tensor([0, 4, 16], device=DEV, dtype=torch.int32)
+    r = api.dapd_step(attn, ei32, so, e32, 0.01, gen_len=gen_len, m_max=16)
+    ref = oracle.dapd_step(host(attn), np.zeros(0, np.int32), so_h, np.zeros(0), 0.01,
+                           gen_len=host(gen_len).numpy())
+    assert host(r["n_commit"]).tolist() == [0, 0, 0]
+    assert np.array_equal(host(r["stage"]).numpy(), ref["stage"])
