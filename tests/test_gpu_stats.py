@@ -159,3 +159,26 @@ def test_one_workspace_serves_any_row_count():
         spec = synth.Spec("mix", 14 + rows, 1, rows, 126464, torch.bfloat16, 2.0, 0.6, 12.0, 0.5)
         cur, prev, so, ri = synth.logits(spec, DEV)
         outs.append(_compare(cur, prev, tag=f"shared workspace {rows} rows "))
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("gap", [30.0, 120.0])
+def test_stats_large_kl(dt, gap):
+    # current and previous rows peaked on different tokens, the peak `gap`
+    # above N(0, 1) noise: KL is about the gap (up to ~123 nats), where the
+    # fp32 output spacing is largest; still within 1e-5 of the oracle
+    g = np.random.default_rng(int(gap))
+    n, V = 8, 126464
+    cur = torch.from_numpy(g.normal(0, 1, (n, V)).astype(np.float32))
+    prev = torch.from_numpy(g.normal(0, 1, (n, V)).astype(np.float32))
+    for r in range(n):
+        a, b = g.integers(0, V, 2)
+        cur[r, a] += gap
+        prev[r, b] += gap
+    cur, prev = cur.to(dt), prev.to(dt)
+    gs = api.step_stats(cur.to(DEV), prev.to(DEV))
+    torch.cuda.synchronize()
+    o = oracle.step_stats(cur, prev)
+    assert float(np.min(o["kl"])) > gap - 15.0
+    for k in ("conf", "entropy", "kl", "lse"):
+        assert_close(gs[k], o[k], f"large KL gap {gap} {dt} {k}")
