@@ -22,6 +22,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "cap_impl.h"
 #include "checks.h"
@@ -46,6 +47,29 @@
 namespace {
 
 constexpr int kStepNT = 512;
+
+// Compute units of the current device, queried once per device and cached
+// (the step asks before its first launch, so an error returns before anything
+// is enqueued, and repeated steps make no device query).
+int cu_count(int* cus) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DLM_ERR_HIP;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return DLM_OK;
+    }
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      c <= 0)
+    return DLM_ERR_HIP;
+  if (dev >= 0 && dev < 64) cache[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return DLM_OK;
+}
 static_assert(kAvgNT == kStepNT, "an attention tile must use the statistics workgroup size");
 static_assert(kRuleNT == 256 && kCapNT == 256 && kSymNT <= 256, "rules run with 256 threads");
 constexpr int kRulesNT = 256;
@@ -195,6 +219,9 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
                                      d->dapd_workspace, d->dapd_workspace_bytes)) != DLM_OK)
     return rc;
 
+  int cus = 0;
+  if (dapd && (rc = cu_count(&cus)) != DLM_OK) return rc;
+
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = d->dtype == DLM_BF16, prev = d->prev_logits != nullptr;
   const int es = bf16 ? 2 : 4;
@@ -261,10 +288,6 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
     // units (every launch-2 workgroup takes a whole compute unit's LDS), a
     // workgroup scores up to four blocks, so that the scores finish in one
     // round of workgroups
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return DLM_ERR_HIP;
     ra.blocks = (d->m_max + kSymRows - 1) / kSymRows;
     const int64_t total = static_cast<int64_t>(ra.blocks) * d->n_seq;
     const int64_t free_cus = std::max<int64_t>(1, cus - (ra.nf + ra.nd + ra.nc));

@@ -76,6 +76,7 @@ __device__ __forceinline__ void depcap_seq(int b, const float* __restrict__ kl,
   const int lo = seq_offsets[b], n = seq_offsets[b + 1] - lo;
   const int W = max(0, min(l_max, n));
   const bool warm = has_prev ? has_prev[b] != 0 : true;
+  R = min(R, W);  // a wider box covers the whole window anyway (and k + R stays in range)
   if (score)
     for (int k = W + threadIdx.x; k < n; k += kRuleNT) score[lo + k] = NAN;
   if (!warm || W == 0) {
