@@ -35,6 +35,8 @@ SIGNATURES = {
     "dlm_dapd_workspace_bytes": (_SZ, [_I32, _I32]),
     "dlm_dapd_select": (_INT, [_P, _INT, _I32, _I64, _I64, _P, _P, _I32, _I32, _P, _F, _P, _P, _P,
                                _P, _P, _P, _SZ, _P]),
+    "dlm_dapd_select_static": (_INT, [_P, _INT, _I32, _I64, _I64, _P, _P, _I32, _I32, _P, _F, _P,
+                                      _P, _P, _P, _P, _P]),
     "dlm_dapd_step": (_INT, [_P, _INT, _I32, _I64, _I64, _P, _P, _I32, _I32, _P, _F, _P, _F, _F,
                              _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "dlm_factor_select": (_INT, [_P, _P, _P, _I32, _F, _P, _P, _P, _P]),

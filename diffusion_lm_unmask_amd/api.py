@@ -224,11 +224,8 @@ def dapd_workspace_bytes(n_seq: int, m_max: int) -> int:
     return int(_lib.lib().dlm_dapd_workspace_bytes(int(n_seq), int(m_max)))
 
 
-def dapd_select(attn, masked_pos, seq_offsets, conf, tau, m_max=None, workspace=None,
-                want_degree=False, want_key=False, want_sym=False):
-    """dlm_dapd_select.  attn: [B, n_lh, S, S] contiguous (bf16 or f32), the
-    maps to average; masked_pos int32 CSR by seq_offsets; conf f32 per row.
-    Returns dict(commit, n_commit, degree, key, sym)."""
+def _dapd_args(attn, masked_pos, seq_offsets, conf, m_max):
+    """Checks shared by the DAPD selection bindings; returns (dev, n_lh, S, n_seq)."""
     _dev(attn, "attn")
     if attn.dim() != 4 or not attn.is_contiguous() or attn.shape[2] != attn.shape[3]:
         raise DLMError("attn must be a contiguous [B, n_lh, S, S] tensor")
@@ -243,23 +240,56 @@ def dapd_select(attn, masked_pos, seq_offsets, conf, tau, m_max=None, workspace=
         raise DLMError("more sequences than attention batches")
     if m_max is None:
         raise DLMError("m_max (an upper bound on masked positions per sequence) is required")
+    return dev, n_lh, S, n_seq
+
+
+def _dapd_outputs(dev, n, n_seq, m_max, want_degree, want_key, want_sym):
+    f = dict(device=dev, dtype=torch.float32)
+    return (torch.empty(n, device=dev, dtype=torch.uint8),
+            torch.empty(max(n_seq, 0), device=dev, dtype=torch.int32),
+            torch.empty(n, **f) if want_degree else None,
+            torch.empty(n, **f) if want_key else None,
+            torch.empty(max(n_seq, 0), m_max, m_max, **f) if want_sym else None)
+
+
+def dapd_select(attn, masked_pos, seq_offsets, conf, tau, m_max=None, workspace=None,
+                want_degree=False, want_key=False, want_sym=False):
+    """dlm_dapd_select.  attn: [B, n_lh, S, S] contiguous (bf16 or f32), the
+    maps to average; masked_pos int32 CSR by seq_offsets; conf f32 per row.
+    Returns dict(commit, n_commit, degree, key, sym)."""
+    dev, n_lh, S, n_seq = _dapd_args(attn, masked_pos, seq_offsets, conf, m_max)
     need = dapd_workspace_bytes(n_seq, m_max)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
     _vec(workspace, "workspace", torch.uint8, dev)
-    n = conf.numel()
-    f = dict(device=dev, dtype=torch.float32)
-    commit = torch.empty(n, device=dev, dtype=torch.uint8)
-    n_commit = torch.empty(max(n_seq, 0), device=dev, dtype=torch.int32)
-    degree = torch.empty(n, **f) if want_degree else None
-    key = torch.empty(n, **f) if want_key else None
-    sym = torch.empty(max(n_seq, 0), m_max, m_max, **f) if want_sym else None
+    commit, n_commit, degree, key, sym = _dapd_outputs(dev, conf.numel(), n_seq, m_max,
+                                                       want_degree, want_key, want_sym)
     st = _lib.lib().dlm_dapd_select(attn.data_ptr(), _dtype_code(attn), n_lh, S, n_lh * S * S,
                                     _rows(masked_pos), seq_offsets.data_ptr(), n_seq,
                                     int(m_max), _rows(conf), float(tau), _rows(commit),
                                     n_commit.data_ptr(), _ptr(degree), _ptr(sym), _ptr(key),
                                     workspace.data_ptr(), workspace.numel(), _stream(attn))
     _lib.check(st, "dlm_dapd_select")
+    return {"commit": commit, "n_commit": n_commit, "degree": degree, "key": key, "sym": sym}
+
+
+def dapd_select_static(attn, masked_pos, seq_offsets, conf, tau, m_max=None,
+                       want_degree=False, want_key=False, want_sym=False):
+    """dlm_dapd_select_static: dlm_dapd_select with the library's static
+    per-GPU workspace (no workspace argument; the library allocates nothing).
+    Calls that overlap in time on one GPU race.  The outputs are allocated
+    here, as for every binding; a caller that cannot allocate calls the C
+    entry point with its own output buffers."""
+    dev, n_lh, S, n_seq = _dapd_args(attn, masked_pos, seq_offsets, conf, m_max)
+    commit, n_commit, degree, key, sym = _dapd_outputs(dev, conf.numel(), n_seq, m_max,
+                                                       want_degree, want_key, want_sym)
+    st = _lib.lib().dlm_dapd_select_static(attn.data_ptr(), _dtype_code(attn), n_lh, S,
+                                           n_lh * S * S, _rows(masked_pos),
+                                           seq_offsets.data_ptr(), n_seq, int(m_max),
+                                           _rows(conf), float(tau), _rows(commit),
+                                           n_commit.data_ptr(), _ptr(degree), _ptr(sym),
+                                           _ptr(key), _stream(attn))
+    _lib.check(st, "dlm_dapd_select_static")
     return {"commit": commit, "n_commit": n_commit, "degree": degree, "key": key, "sym": sym}
 
 

@@ -1,6 +1,9 @@
 // dapd.hip — dlm_dapd_select and dlm_dapd_step: the three kernels (device
 // code and design notes in dapd_impl.h), the workspace size and the host
 // entry points.
+#include <atomic>
+#include <mutex>
+
 #include "checks.h"
 #include "dapd_impl.h"
 
@@ -99,4 +102,62 @@ extern "C" int dlm_dapd_step(const void* attn, int dtype, int32_t n_lh, int64_t 
   const Policy P{gen_len, late_frac, late_tau, pre_unmask != 0 ? 1 : 0, stage};
   return dapd_run(attn, dtype, n_lh, S, batch_stride, masked_pos, seq_offsets, n_seq, m_max, conf,
                   tau, P, commit, n_commit, degree, sym, key, workspace, workspace_bytes, stream);
+}
+
+// ---- dlm_dapd_select_static: the same selection with its workspace in a
+// file-scope device array instead of caller memory, for callers that cannot
+// allocate.  Each device holds its own copy of the array from the library's
+// load until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is handed to kernels.
+static __device__ __align__(256) char scratch[DLM_DAPD_STATIC_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array, or nullptr on a HIP
+// error (or a device ordinal beyond the table).
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr)
+      return nullptr;
+    g_scratch[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" int dlm_dapd_select_static(const void* attn, int dtype, int32_t n_lh, int64_t S,
+                                      int64_t batch_stride, const int32_t* masked_pos,
+                                      const int32_t* seq_offsets, int32_t n_seq, int32_t m_max,
+                                      const float* conf, float tau, uint8_t* commit,
+                                      int32_t* n_commit, float* degree, float* sym, float* key,
+                                      void* stream) {
+  // validate everything else first (with a stand-in workspace of the right
+  // size), so that a bad call returns the same code as dlm_dapd_select's
+  const size_t need = dlm_dapd_workspace_bytes(n_seq, m_max);
+  int rc = dlmh::check_dapd(attn, dtype, n_lh, S, batch_stride, masked_pos, seq_offsets, n_seq,
+                            m_max, conf, tau, 0.f, 0.f, commit, n_commit,
+                            reinterpret_cast<void*>(uintptr_t{256}), need);
+  if (rc != DLM_OK) return rc;
+  if (need > static_cast<size_t>(DLM_DAPD_STATIC_BYTES)) return DLM_ERR_UNSUPPORTED;
+  void* ws = scratch_ptr();
+  if (!ws) return DLM_ERR_HIP;
+  const Policy P{nullptr, 0.f, 0.f, 0, nullptr};
+  return dapd_run(attn, dtype, n_lh, S, batch_stride, masked_pos, seq_offsets, n_seq, m_max, conf,
+                  tau, P, commit, n_commit, degree, sym, key, ws,
+                  static_cast<size_t>(DLM_DAPD_STATIC_BYTES), stream);
 }

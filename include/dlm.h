@@ -239,6 +239,28 @@ int dlm_dapd_select(const void* attn, int dtype, int32_t n_lh, int64_t S, int64_
                     size_t workspace_bytes, void* stream);
 
 /*
+ * dlm_dapd_select_static — dlm_dapd_select without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The workspace is a
+ * static device array of DLM_DAPD_STATIC_BYTES in the library, one per GPU,
+ * held from the library's load until the process ends; the call allocates
+ * nothing.  Every argument, output and error is that of dlm_dapd_select,
+ * plus DLM_ERR_UNSUPPORTED when dlm_dapd_workspace_bytes(n_seq, m_max)
+ * exceeds DLM_DAPD_STATIC_BYTES (16 MiB: up to 32 sequences of 256 masked
+ * positions, or 3 of 1024, fit; 64 of 1024 do not), and DLM_ERR_HIP when the array's device address
+ * cannot be obtained.  All calls on one GPU share that GPU's array: calls
+ * that overlap in time on one GPU (any streams, any threads) race and must
+ * be serialised by the caller.  Nothing in the array needs to start zeroed;
+ * each call overwrites what it reads.
+ */
+#define DLM_DAPD_STATIC_BYTES (16 << 20)
+int dlm_dapd_select_static(const void* attn, int dtype, int32_t n_lh, int64_t S,
+                           int64_t batch_stride, const int32_t* masked_pos,
+                           const int32_t* seq_offsets, int32_t n_seq, int32_t m_max,
+                           const float* conf, float tau, uint8_t* commit, int32_t* n_commit,
+                           float* degree, float* sym, float* key, void* stream);
+
+/*
  * dlm_dapd_step — [DAPD, overall framework; key design 3]: dlm_dapd_select
  * with the full step policy.  For sequence b with M_b masked rows:
  *   - late stage iff gen_len != NULL and M_b < late_frac * gen_len[b]

@@ -109,6 +109,21 @@ def test_dapd_validation(L):
         bad = list(ok)
         bad[i] = v
         assert f(*bad) == code, (i, v)
+    # the static-workspace variant: the same checks (no workspace argument),
+    # and sizes beyond its static array are refused before any HIP call
+    g = L.dlm_dapd_select_static
+    ok_s = ok[:16] + ok[18:]
+    assert len(ok_s) == 17
+    for i, v, code in ((8, 1025, _lib.ERR_UNSUPPORTED), (10, math.nan, _lib.ERR_ARG),
+                       (4, 10, _lib.ERR_ARG), (1, 9, _lib.ERR_UNSUPPORTED), (2, 0, _lib.ERR_ARG),
+                       (0, None, _lib.ERR_ARG), (11, None, _lib.ERR_ARG)):
+        bad = list(ok_s)
+        bad[i] = v
+        assert g(*bad) == code, (i, v)
+    big = list(ok_s)
+    big[7], big[8] = 64, 1024                           # 277 MB of workspace: over the array
+    assert L.dlm_dapd_workspace_bytes(64, 1024) > 16 << 20
+    assert g(*big) == _lib.ERR_UNSUPPORTED
 
 
 def test_schedule_validation(L):
