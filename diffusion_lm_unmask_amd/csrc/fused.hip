@@ -9,7 +9,9 @@
 //            statistics; the rest average one DAPD attention tile.  Both are
 //            HBM streams with the same 512-thread workgroup, so one grid
 //            keeps the memory system busy through each other's ramp-up and
-//            tail instead of paying two.
+//            tail instead of paying two.  Without DAPD, launch 1 is
+//            k_step_rows: the statistics call's own kernel and launch shape
+//            (bitwise its results).
 //  launch 2  k_step_rules: Fast-dLLM, DepCap and CAP one workgroup per
 //            sequence each, and the DAPD scores four rows per wave (one to
 //            four waves per workgroup), side by side.  The workgroup that
@@ -86,6 +88,15 @@ struct StreamArgs {
   uint64_t* tally;  // [n_seq], zeroed here for launch 2
   Policy P;
 };
+
+// Launch 1 without attention tiles: exactly the statistics call's kernel and
+// launch shape (one workgroup per row, stats_threads(n_rows) threads), so
+// these statistics are bitwise those of dlm_step_stats without a workspace.
+template <int NT, bool BF16, bool PREV>
+__global__ __launch_bounds__(NT) void k_step_rows(const StatsArgs p) {
+  stats_block<NT, BF16, PREV, NT == 256 ? DLM_STATS_U_BF16_256 : DLM_STATS_U_BF16>(p, blockIdx.x,
+                                                                                 0);
+}
 
 template <bool BF16, bool PREV, bool ABF16>
 __global__ __launch_bounds__(kStepNT) void k_step_stream(const StreamArgs a) {
@@ -182,6 +193,21 @@ void launch_stream_k(dim3 grid, hipStream_t s, const StreamArgs& a, hipEvent_t e
   else
     hipLaunchKernelGGL((k_step_stream<BF16, PREV, ABF16>), grid, dim3(kStepNT), 0, s, a);
 }
+template <int NT, bool BF16, bool PREV>
+void launch_rows_k(int64_t n_rows, hipStream_t s, const StatsArgs& a, hipEvent_t e0,
+                   hipEvent_t e1) {
+  const dim3 grid(static_cast<unsigned>(n_rows));
+  if (e0 || e1)
+    hipExtLaunchKernelGGL((k_step_rows<NT, BF16, PREV>), grid, dim3(NT), 0, s, e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL((k_step_rows<NT, BF16, PREV>), grid, dim3(NT), 0, s, a);
+}
+template <bool BF16, bool PREV>
+void launch_rows(int64_t n_rows, hipStream_t s, const StatsArgs& a, hipEvent_t e0,
+                 hipEvent_t e1) {
+  if (stats_threads(n_rows) == 256) launch_rows_k<256, BF16, PREV>(n_rows, s, a, e0, e1);
+  else launch_rows_k<512, BF16, PREV>(n_rows, s, a, e0, e1);
+}
 template <bool BF16, bool PREV>
 void launch_stream(bool abf16, dim3 grid, hipStream_t s, const StreamArgs& a, hipEvent_t e0,
                    hipEvent_t e1) {
@@ -263,7 +289,15 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
   const bool abf16 = !dapd || d->attn_dtype == DLM_BF16;
   const hipEvent_t e0 = static_cast<hipEvent_t>(d->launch1_begin_event);
   const hipEvent_t e1 = static_cast<hipEvent_t>(d->launch1_end_event);
-  if (bf16) {
+  if (!dapd) {  // statistics only: the statistics call's own kernel and shape
+    if (bf16) {
+      if (prev) launch_rows<true, true>(d->n_rows, s, sa.st, e0, e1);
+      else launch_rows<true, false>(d->n_rows, s, sa.st, e0, e1);
+    } else {
+      if (prev) launch_rows<false, true>(d->n_rows, s, sa.st, e0, e1);
+      else launch_rows<false, false>(d->n_rows, s, sa.st, e0, e1);
+    }
+  } else if (bf16) {
     if (prev) launch_stream<true, true>(abf16, grid1, s, sa, e0, e1);
     else launch_stream<true, false>(abf16, grid1, s, sa, e0, e1);
   } else {

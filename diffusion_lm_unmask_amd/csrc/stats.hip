@@ -51,18 +51,13 @@ int64_t workspace_rows(size_t bytes) {
   return c;
 }
 
-// Threads per row and splits per row.  Many rows: one workgroup per row (256
-// threads from 4096 rows up, else 512; 1024 threads on 256 rows measured
-// 27.2 against 25.8 us).  Very few rows (<= 64) with a
-// workspace: split each row so that the launch has about one workgroup per
-// CU.  Splitting more rows than that costs more than it gains: each split's
-// agent-scope release/acquire writes back / invalidates its XCD's L2 while
-// the other workgroups stream through it.
-#ifndef DLM_STATS_NT256_ROWS
-#define DLM_STATS_NT256_ROWS 4096
-#endif
+// Threads per row (stats_threads) and splits per row.  Very few rows (<= 64)
+// with a workspace: split each row so that the launch has about one
+// workgroup per CU.  Splitting more rows than that costs more than it gains:
+// each split's agent-scope release/acquire writes back / invalidates its
+// XCD's L2 while the other workgroups stream through it.
 void launch_shape(int64_t n_rows, int64_t n_chunks, bool can_split, int* nt, int* splits) {
-  *nt = n_rows >= DLM_STATS_NT256_ROWS ? 256 : 512;
+  *nt = stats_threads(n_rows);
   int sp = 1;
   if (can_split && n_rows <= 64) {
     sp = static_cast<int>((256 + n_rows - 1) / n_rows);

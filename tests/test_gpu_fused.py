@@ -235,3 +235,20 @@ def test_fused_dapd_bad_position_and_empty_sequence():
         n = host(f["dapd"][1]).tolist()
         assert n[0] == -1 and n[1] == 0 and n[2] > 0, n
         assert int(host(f["dapd"][0][:40]).sum()) == 0
+
+
+@pytest.mark.parametrize("name", ["llada", "tiny"])
+def test_fused_without_dapd_statistics_equal_the_call_bitwise(name):
+    # without DAPD, launch 1 is the statistics call's own kernel and launch
+    # shape, so the statistics are bitwise those of dlm_step_stats (no
+    # workspace); the LLaDA workload as configured (statistics, Fast-dLLM,
+    # DepCap) runs on this path
+    cur, prev, so, ri = synth.logits(name, DEV)
+    R = synth.RULES[name]
+    fast, depcap, cap = _llada_parts(cur, R)
+    f = api.decide_step(cur, prev, so, row_index=ri, fast=fast, depcap=depcap)
+    g = api.step_stats(cur, prev, row_index=ri, split=False)
+    torch.cuda.synchronize()
+    for k in ("conf", "entropy", "kl", "lse", "argmax"):
+        assert torch.equal(f[k].view(torch.int32), g[k].view(torch.int32)), f"{name}: {k}"
+    _check(cur, prev, so, ri, fast=fast, depcap=depcap, tag=f"{name} as configured")

@@ -182,3 +182,86 @@ def test_stats_large_kl(dt, gap):
     assert float(np.min(o["kl"])) > gap - 15.0
     for k in ("conf", "entropy", "kl", "lse"):
         assert_close(gs[k], o[k], f"large KL gap {gap} {dt} {k}")
+
+
+# ------------------------------------------------------------ closed forms
+# Rows whose statistics have closed forms (DepCap, Methodology: H and KL of
+# each position's distribution; Fast-dLLM review, Method: max-softmax
+# confidence), on every path that computes statistics: the streaming path
+# (512-thread workgroups; split rows with a workspace; 256-thread workgroups
+# from 4096 rows up), the element-wise path (rows holding -inf), and the
+# fused step's streaming launch.
+#   uniform row (all logits c)       conf = 1/V, H = log V, lse = c + log V, argmax 0
+#   one-hot row (1000 at j, 0 else)  conf = 1, H = 0, lse = 1000, argmax j
+#   -inf except n equal entries      conf = 1/n, H = log n (element-wise path)
+#   -inf except one entry            conf = 1, H = 0 exactly (element-wise path)
+#   prev == cur                      KL = 0 exactly, on every row
+
+def _closed_form_rows(n_rows, V, dtype):
+    x = torch.zeros(n_rows, V, dtype=torch.float32)
+    kind, want = [], []
+    for r in range(n_rows):
+        k = r % 5
+        if k == 0:                                           # uniform at c
+            c = (0.0, 3.5, -7.25)[(r // 5) % 3]
+            x[r] = c
+            want.append((1.0 / V, np.log(V), c + np.log(V), 0))
+        elif k == 1:                                         # one-hot 1000
+            j = (r * 7919) % V
+            x[r, j] = 1000.0
+            want.append((1.0, 0.0, 1000.0, j))
+        elif k == 2:                                         # one-hot 1000 with negative rest
+            j = (r * 104729) % V
+            x[r] = -3.0
+            x[r, j] = 1000.0
+            want.append((1.0, 0.0, 1000.0, j))
+        elif k == 3:                                         # n equal entries, -inf elsewhere
+            n = 1 + (r * 31) % min(V, 97)
+            x[r] = float("-inf")
+            idx = torch.arange(n) * (V // n)
+            x[r, idx] = 2.0
+            want.append((1.0 / n, np.log(n), 2.0 + np.log(n), 0))
+        else:                                                # a single finite entry
+            j = (r * 13) % V
+            x[r] = float("-inf")
+            x[r, j] = -5.0
+            want.append((1.0, 0.0, -5.0, j))
+        kind.append(k)
+    return x.to(dtype).to(DEV), np.array(kind), want
+
+
+def _check_closed_forms(out, kind, want, tag):
+    conf, ent, lse = (host(out[k]).double().numpy() for k in ("conf", "entropy", "lse"))
+    kl, arg = host(out["kl"]).double().numpy(), host(out["argmax"]).numpy()
+    for r, (c, h, l, j) in enumerate(want):
+        assert arg[r] == j, f"{tag} row {r} (kind {kind[r]}): argmax {arg[r]} != {j}"
+        assert kl[r] == 0.0, f"{tag} row {r} (kind {kind[r]}): KL {kl[r]!r} with prev == cur"
+        assert abs(ent[r] - h) <= 1e-5, f"{tag} row {r}: entropy {ent[r]} vs {h}"
+        assert abs(lse[r] - l) <= 1e-5 + 6.2e-5 * (abs(l) >= 512), f"{tag} row {r}: lse {lse[r]} vs {l}"
+        if kind[r] in (0, 3):
+            assert abs(conf[r] * (1.0 / c) - 1.0) <= 1e-5, f"{tag} row {r}: conf {conf[r]} vs {c}"
+        else:
+            assert abs(conf[r] - 1.0) <= 1e-6, f"{tag} row {r}: conf {conf[r]}"
+            assert abs(ent[r]) <= 1e-6, f"{tag} row {r}: entropy {ent[r]}"
+        if kind[r] == 4:                                     # element-wise path: exact
+            assert conf[r] == 1.0 and ent[r] == 0.0, f"{tag} row {r}: {conf[r]!r} {ent[r]!r}"
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 126464), (torch.float32, 4099)])
+@pytest.mark.parametrize("n_rows,split", [(40, True), (40, False), (300, False)])
+def test_closed_forms(dtype, V, n_rows, split):
+    cur, kind, want = _closed_form_rows(n_rows, V, dtype)
+    out = api.step_stats(cur, cur, split=split)
+    torch.cuda.synchronize()
+    _check_closed_forms(out, kind, want, f"{dtype} V={V} rows={n_rows} split={split}")
+    fused = api.decide_step(cur, cur)                        # the fused step's launch 1
+    torch.cuda.synchronize()
+    _check_closed_forms(fused, kind, want, f"fused {dtype} V={V} rows={n_rows}")
+
+
+def test_closed_forms_256_thread_rows():
+    # 4096 rows take the 256-thread workgroups
+    cur, kind, want = _closed_form_rows(4096, 1000, torch.bfloat16)
+    out = api.step_stats(cur, cur)
+    torch.cuda.synchronize()
+    _check_closed_forms(out, kind, want, "4096 x 1000 bf16")
