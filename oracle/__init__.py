@@ -21,21 +21,31 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dlm_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# DLM_ORACLE_SANITIZED=1 selects the AddressSanitizer + UndefinedBehaviorSanitizer
+# build (tests only; the process must preload the sanitizer runtimes)
+_SANITIZED = os.environ.get("DLM_ORACLE_SANITIZED") == "1"
+_LIB_PATH = os.path.join(_HERE, "liboracle_san.so" if _SANITIZED else "liboracle.so")
 
 BF16 = 0
 F32 = 1
 
+_FLAGS = ["-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-pthread"]
+SANITIZE_FLAGS = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer"]
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (fp64, no fast-math, no FP contraction)."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
-               "-shared", "-pthread", _SRC, "-o", tmp, "-lm"]
+
+def build(force: bool = True, sanitized: bool | None = None) -> str:
+    """Compile the oracle with gcc (fp64, no fast-math, no FP contraction);
+    `sanitized` builds the ASan + UBSan variant instead."""
+    san = _SANITIZED if sanitized is None else sanitized
+    path = os.path.join(_HERE, "liboracle_san.so" if san else "liboracle.so")
+    if force or not os.path.exists(path):
+        tmp = path + ".tmp%d" % os.getpid()
+        opt = SANITIZE_FLAGS if san else ["-O2"]
+        cmd = ["gcc", *opt, *_FLAGS, _SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+        os.replace(tmp, path)
+    return path
 
 
 _lib = None

@@ -265,8 +265,10 @@ int dlmo_depcap_scores(const double* kl, const double* entropy, const int32_t* s
     double* ib = (double*)malloc(sizeof(double) * (size_t)W);
     double* hb = (double*)malloc(sizeof(double) * (size_t)W);
     for (int32_t k = 0; k < W; ++k) {
-      int32_t j0 = k - radius < 0 ? 0 : k - radius;
-      int32_t j1 = k + radius > W - 1 ? W - 1 : k + radius;
+      /* the window's ends in 64-bit: k + radius must not overflow */
+      int64_t lo64 = (int64_t)k - radius, hi64 = (int64_t)k + radius;
+      int32_t j0 = lo64 < 0 ? 0 : (int32_t)lo64;
+      int32_t j1 = hi64 > W - 1 ? W - 1 : (int32_t)hi64;
       double si = 0.0, sh = 0.0;
       for (int32_t j = j0; j <= j1; ++j) {
         si += kl[lo + j];
