@@ -1,37 +1,46 @@
 #!/usr/bin/env python3
-"""Benchmark of one per-denoising-step unmask decision on one MI355X.
+"""Benchmark of the per-denoising-step unmask decision on one MI355X.
 
 A step is one pass of the whole decision path over one batch of synthetic
-input, the LLaDA-shaped step (one sequence, 256 masked generation rows,
-vocabulary 126464, bf16 current and previous-step logits):
+input.  The headline step is the LLaDA-shaped workload as configured: one
+sequence of 256 masked generation rows, vocabulary 126464, bf16 current and
+previous-step logits, with
 
-  dlm_step_stats       confidence / argmax / entropy / KL / lse for 256 rows
-  dlm_fastdllm_select  threshold 0.9 on the active 32-token block (rows 0-31)
-  dlm_depcap_boundary  DepGA-Block scan over the 128-row window (lambda 1.2,
-                       L_min 8, L_max 128)
-  dlm_cap_select       CAP-Decoding on the same 32-token block (0.8 / 0.95 / -16)
-  dlm_dapd_select      DAPD graph over the 256 rows from [1, 320, 768, 768] bf16
-                       attention (prompt 512 + generation 256), tau 0.01
+  statistics   confidence / argmax / entropy / KL / lse of all 256 rows
+  Fast-dLLM    threshold 0.9 on the active 32-token block (rows 0-31)
+  DepCap       DepGA-Block boundary over the 128-row window (lambda 1.2,
+               L_min 8, L_max 128)
 
-By default (`--mode fused`) the step is the one call dlm_decide_step, which
-runs the same decisions in two launches (statistics rows and attention
-averaging in one streaming kernel, then the four rules, with the DAPD
-selection in the last of its scores workgroups), issued back to back on one
-stream; the host stays ahead of the
-GPU, so the launches queue without gaps (a graph per step measured slower:
-each graph launch adds a few microseconds).  Its decisions equal the five
-calls' (checked on every run and reported).
+issued as one dlm_decide_step call (two launches: the statistics kernel, then
+the two rules), back to back on one stream.  `value` is rows decided per
+second; `roofline` is that of the statistics kernel (launch 1), timed by HIP
+events that the launch itself sets to the kernel's start and end.
 
-Inputs are resident in HBM before timing starts; `--replicas` independent
-copies are rotated so that consecutive steps do not hit the 256 MB Infinity
-Cache.  Prints one JSON line (rank 0, N = 1): decisions/s, ms/step, the
-dominant kernel's achieved HBM bandwidth against the 8 TB/s peak (HIP events
-on its launch stream, averaged over the timed steps), and the CPU oracle's
-rate on the same step.
+The other workloads run in the same process under the same clock, each as
+one dlm_decide_step per step (sub-results under "workloads"):
+  llada_all_rules  the LLaDA step plus CAP on block 0 and a DAPD graph over
+                   the 256 rows from [1, 320, 768, 768] attention
+  dapd             8 x 256 rows (no prev) + DAPD over [8, 320, 768, 768]
+                   attention (literal: no edge at tau 0.01), and the same step
+                   on the partner-covariance attention (edge-rich greedy)
+  stress           64 x 1024 rows, cur + prev (33.15 GB) + DepCap + CAP (K 128)
+  dream            16 x 256 rows, V 151936 (no prev) + CAP (0.7, K 64)
+  tiny             1 x 32 rows, fp32, every rule (latency)
+For the three V = 126464 workloads the statistics kernel's achieved HBM
+bandwidth is reported against the 8 TB/s peak ("stats_kernel").
+
+Inputs are resident in HBM before timing starts; LLaDA-sized inputs rotate
+over `--replicas` copies so that consecutive steps miss the 256 MB Infinity
+Cache (the larger workloads exceed it by themselves).  The CPU oracle is timed
+on the LLaDA step on the host's cores (and on one core, on an 8-sequence
+sample of the stress step and on the DAPD step), and its decisions are
+compared with the GPU's on the same inputs ("oracle_parity").
+Prints one JSON line (N = 1).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -43,12 +52,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llada_step_traffic.json")
+METRIC = "masked-row decisions/sec and achieved HBM GB/s (% of peak), V=126464 bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # the device sources each timed kernel is built from: a counter reading is
 # only reported while they are unchanged since it was taken
 KERNEL_SOURCES = {
+    "k_step_rows": ("fused.hip", "stats_impl.h", "dlm_device.h"),
     "k_step_stream": ("fused.hip", "stats_impl.h", "dapd_impl.h", "dlm_device.h"),
-    "k_stats": ("stats.hip", "stats_impl.h", "dlm_device.h"),
 }
 
 
@@ -60,12 +70,13 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    runs (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None."""
+def measured_traffic(key: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, copy-calibrated), or None when absent or taken
+    on different kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f).get(kernel, {})
+            t = json.load(f).get(key, {})
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_sha256") != kernel_source_hash(kernel):
@@ -75,17 +86,14 @@ def measured_traffic(kernel: str):
 
 class TimingEvents:
     """Pairs of HIP timing events created without the system-scope fence
-    (hipEventDisableSystemFence), so that recording one adds no cache
-    write-back to the interval it brackets.  The fused step hands them to its
-    streaming launch, which sets them to the kernel's start and end; the
-    five-call step records them on the launch stream around the statistics
-    call.  They come from the HIP runtime already loaded into the process
-    (torch's), so they are valid on torch's streams."""
+    (hipEventDisableSystemFence), handed to dlm_decide_step, whose launch 1
+    sets them to its kernel's start and end.  They come from the HIP runtime
+    already loaded into the process (torch's), so they are valid on torch's
+    streams."""
 
     NO_SYSTEM_FENCE = 0x20000000
 
     def __init__(self, n: int):
-        import ctypes
         path = None
         with open("/proc/self/maps") as f:
             for line in f:
@@ -94,7 +102,6 @@ class TimingEvents:
                     break
         if path is None:
             raise RuntimeError("the HIP runtime is not loaded")
-        self.ct = ctypes
         self.hip = ctypes.CDLL(path)
         self.pairs = []
         for _ in range(n):
@@ -106,16 +113,12 @@ class TimingEvents:
                 pair.append(e.value)
             self.pairs.append(tuple(pair))
 
-    def record(self, ev, stream):
-        if self.hip.hipEventRecord(self.ct.c_void_p(ev), self.ct.c_void_p(stream)):
-            raise RuntimeError("hipEventRecord failed")
-
     def mean_us(self):
         """Average interval in microseconds (call after the device is synchronized)."""
-        ms, acc = self.ct.c_float(), 0.0
+        ms, acc = ctypes.c_float(), 0.0
         for a, b in self.pairs:
-            if self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ct.c_void_p(a),
-                                            self.ct.c_void_p(b)):
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                            ctypes.c_void_p(b)):
                 raise RuntimeError("hipEventElapsedTime failed")
             acc += ms.value
         return acc / len(self.pairs) * 1000.0
@@ -123,220 +126,453 @@ class TimingEvents:
     def close(self):
         for pair in self.pairs:
             for e in pair:
-                self.hip.hipEventDestroy(self.ct.c_void_p(e))
+                self.hip.hipEventDestroy(ctypes.c_void_p(e))
         self.pairs = []
 
 
-def torch_int_view(t):
-    import torch
-    return {torch.float32: torch.int32, torch.float64: torch.int64}.get(t.dtype, t.dtype)
+def gbs(nbytes, us):
+    return nbytes / (us * 1e-6) / 1e9
 
 
-class LladaStep:
-    """Preallocated buffers and ctypes argument lists for the LLaDA-shaped step."""
+class Step:
+    """One decision step as prebuilt dlm_decide_step descriptors, one per
+    input replica (api.step_descriptor marshals them once; the timed loop only
+    calls the C entry point)."""
 
-    def __init__(self, replicas: int, dev: str):
-        import torch
-        from diffusion_lm_unmask_amd import _lib, synth
-
-        self.torch = torch
+    def __init__(self, name, rows, replicas, stream, launch1_bytes, **parts):
+        """replicas: one dict of step_descriptor arguments per input replica;
+        `parts` are added to each (a replica's own entries take precedence)."""
+        from diffusion_lm_unmask_amd import _lib, api
+        self.name, self.rows, self.launch1_bytes = name, rows, launch1_bytes
+        self.stream = stream
         self.L = _lib.lib()
         self.check = _lib.check
-        spec = synth.SPECS["llada"]
-        self.R = synth.RULES["llada"]
-        self.rows, self.V = spec.rows, spec.vocab
-        cur, prev, so, ri = synth.logits("llada", dev)
-        attn = synth.attention("llada", dev, batch=1)
-        pos, offs = synth.gen_positions("llada", dev, batch=1)
-        self.cur = [cur] + [cur.clone() for _ in range(replicas - 1)]
-        self.prev = [prev] + [prev.clone() for _ in range(replicas - 1)]
-        self.attn = [attn] + [attn.clone() for _ in range(replicas - 1)]
-        self.so, self.ri, self.pos, self.offs = so, ri, pos, offs
-        n = self.rows
-        f32 = dict(device=dev, dtype=torch.float32)
-        self.conf, self.ent, self.kl, self.lse = (torch.empty(n, **f32) for _ in range(4))
-        self.arg = torch.empty(n, device=dev, dtype=torch.int32)
-        self.block = torch.zeros(n, device=dev, dtype=torch.uint8)
-        b0, b1 = self.R["fast_block"]
-        self.block[b0:b1] = 1
-        u8 = dict(device=dev, dtype=torch.uint8)
-        i32 = dict(device=dev, dtype=torch.int32)
-        self.commit_f, self.commit_c, self.commit_d = (torch.empty(n, **u8) for _ in range(3))
-        self.nf, self.nc, self.nd, self.blen = (torch.empty(1, **i32) for _ in range(4))
-        self.score = torch.empty(n, device=dev, dtype=torch.float64)
-        self.sws_bytes = int(self.L.dlm_step_stats_workspace_bytes(n))
-        self.sws = torch.zeros(self.sws_bytes, **u8)     # zero-filled once; kept zero by the library
-        self.ws_bytes = int(self.L.dlm_dapd_workspace_bytes(1, n))
-        self.ws = torch.empty(self.ws_bytes, **u8)
-        # every call goes to this stream (default priority), eager or captured
-        self.torch_stream = torch.cuda.Stream(device=dev)
-        self.stream = self.torch_stream.cuda_stream
-        self.n_lh, self.S = attn.shape[1], attn.shape[2]
-        self.bytes_stats = n * self.V * 2 * 2          # cur + prev rows, bf16
-        # the DAPD average reads the masked rows x masked columns of every
-        # attention map (bf16) and writes the fp32 average a
-        self.bytes_avg = self.n_lh * n * n * 2 + n * n * 4
-        self.desc = [self._desc(r) for r in range(replicas)]
+        self.built = [api.step_descriptor(**dict(parts, **r)) for r in replicas]
+        self.descs = [b[0] for b in self.built]
+        self.refs = [ctypes.byref(d) for d in self.descs]
 
-    def _desc(self, r):
-        """dlm_decide_step descriptor of the same step on input replica r."""
-        from diffusion_lm_unmask_amd import _lib
-        R, d = self.R, _lib.StepDesc()
-        d.logits, d.prev_logits, d.dtype = self.cur[r].data_ptr(), self.prev[r].data_ptr(), 0
-        d.vocab, d.ld, d.row_index, d.n_rows = self.V, self.V, self.ri.data_ptr(), self.rows
-        d.conf, d.argmax, d.entropy = self.conf.data_ptr(), self.arg.data_ptr(), self.ent.data_ptr()
-        d.kl, d.lse, d.seq_offsets, d.n_seq = self.kl.data_ptr(), self.lse.data_ptr(), \
-            self.so.data_ptr(), 1
-        d.fast_eligible, d.fast_tau = self.block.data_ptr(), R["tau"]
-        d.fast_commit, d.fast_n_commit = self.commit_f.data_ptr(), self.nf.data_ptr()
-        d.depcap_lambda, d.depcap_l_min, d.depcap_l_max = R["lam"], R["l_min"], R["l_max"]
-        d.depcap_radius, d.depcap_eps = 1, 1e-12
-        d.depcap_block_len, d.depcap_score = self.blen.data_ptr(), self.score.data_ptr()
-        d.cap_eligible, d.cap_tau_low, d.cap_tau_high = self.block.data_ptr(), R["tau_low"], \
-            R["tau_high"]
-        d.cap_gamma, d.cap_k_max = R["gamma"], R["k_max"]
-        d.cap_commit, d.cap_n_commit = self.commit_c.data_ptr(), self.nc.data_ptr()
-        d.attn, d.attn_dtype, d.n_lh, d.S = self.attn[r].data_ptr(), 0, self.n_lh, self.S
-        d.batch_stride, d.masked_pos, d.m_max = self.n_lh * self.S * self.S, \
-            self.pos.data_ptr(), self.rows
-        d.dapd_tau, d.dapd_commit, d.dapd_n_commit = R["dapd_tau"], self.commit_d.data_ptr(), \
-            self.nd.data_ptr()
-        d.dapd_workspace, d.dapd_workspace_bytes = self.ws.data_ptr(), self.ws_bytes
-        return d
-
-    def fused(self, r, ev=None):
-        """The same step as one dlm_decide_step call (two launches); with
-        `ev` (a pair of raw HIP events), the library records them around its
-        streaming launch."""
-        import ctypes
-        d = self.desc[r]
+    def run(self, i, ev=None):
+        d = self.descs[i % len(self.descs)]
         d.launch1_begin_event = ev[0] if ev is not None else None
         d.launch1_end_event = ev[1] if ev is not None else None
-        st = self.L.dlm_decide_step(ctypes.byref(d), self.stream)
+        st = self.L.dlm_decide_step(self.refs[i % len(self.refs)], self.stream)
         if st:
-            self.check(st, "dlm_decide_step")
+            self.check(st, f"dlm_decide_step ({self.name})")
 
-    def outputs(self):
-        """Copies of every output, as raw bits (so NaN compares equal to NaN)."""
-        out = []
-        for t in (self.conf, self.arg, self.ent, self.kl, self.lse, self.commit_f, self.nf,
-                  self.blen, self.score, self.commit_c, self.nc, self.commit_d, self.nd):
-            out.append(t.view(torch_int_view(t)).clone())
-        return out
-
-    def stats(self, r):
-        st = self.L.dlm_step_stats(self.cur[r].data_ptr(), self.prev[r].data_ptr(), 0, self.V,
-                                   self.V, self.ri.data_ptr(), self.rows, self.conf.data_ptr(),
-                                   self.arg.data_ptr(), self.ent.data_ptr(), self.kl.data_ptr(),
-                                   self.lse.data_ptr(), self.sws.data_ptr(), self.sws_bytes,
-                                   self.stream)
-        if st:
-            self.check(st, "dlm_step_stats")
-
-    def fastdllm(self, r):
-        st = self.L.dlm_fastdllm_select(self.conf.data_ptr(), self.block.data_ptr(),
-                                        self.so.data_ptr(), 1, self.R["tau"],
-                                        self.commit_f.data_ptr(), self.nf.data_ptr(), self.stream)
-        if st:
-            self.check(st, "dlm_fastdllm_select")
-
-    def depcap(self, r):
-        st = self.L.dlm_depcap_boundary(self.kl.data_ptr(), self.ent.data_ptr(), self.so.data_ptr(),
-                                        1, None, self.R["lam"], self.R["l_min"], self.R["l_max"], 1,
-                                        1e-12, self.blen.data_ptr(), self.score.data_ptr(),
-                                        self.stream)
-        if st:
-            self.check(st, "dlm_depcap_boundary")
-
-    def cap(self, r):
-        R = self.R
-        st = self.L.dlm_cap_select(self.cur[r].data_ptr(), 0, self.V, self.V, self.ri.data_ptr(),
-                                   self.so.data_ptr(), 1, self.conf.data_ptr(), self.arg.data_ptr(),
-                                   self.lse.data_ptr(), self.block.data_ptr(), R["tau_low"],
-                                   R["tau_high"], R["gamma"], R["k_max"],
-                                   self.commit_c.data_ptr(), self.nc.data_ptr(), None, None,
-                                   self.stream)
-        if st:
-            self.check(st, "dlm_cap_select")
-
-    def dapd(self, r):
-        st = self.L.dlm_dapd_select(self.attn[r].data_ptr(), 0, self.n_lh, self.S,
-                                    self.n_lh * self.S * self.S, self.pos.data_ptr(),
-                                    self.offs.data_ptr(), 1, self.rows, self.conf.data_ptr(),
-                                    self.R["dapd_tau"], self.commit_d.data_ptr(),
-                                    self.nd.data_ptr(), None, None, None, self.ws.data_ptr(),
-                                    self.ws_bytes, self.stream)
-        if st:
-            self.check(st, "dlm_dapd_select")
-
-    def step(self, r, ev=None, events=None):
-        if ev is not None:
-            events.record(ev[0], self.stream)
-        self.stats(r)
-        if ev is not None:
-            events.record(ev[1], self.stream)
-        self.fastdllm(r)
-        self.depcap(r)
-        self.cap(r)
-        self.dapd(r)
+    def out(self, i=0):
+        return self.built[i % len(self.built)][1]
 
 
-def cpu_baseline(step: LladaStep, seconds: float):
-    """Time the CPU oracle (as it stands) on the same step, on host copies."""
-    import numpy as np
+def time_step(step: Step, steps: int, warmup: int):
+    """ms per step over `steps` back-to-back steps (events around the batch,
+    device synchronized on both sides), then the average duration of launch 1
+    over a second run of the same steps (events set by the launch itself)."""
+    import torch
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        step.run(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s = torch.cuda.ExternalStream(step.stream)
+    t0.record(s)
+    for i in range(steps):
+        step.run(i)
+    t1.record(s)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    ev = TimingEvents(steps)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step.run(i, ev.pairs[i])
+    torch.cuda.synchronize()
+    us = ev.mean_us()
+    ev.close()
+    for d in step.descs:
+        d.launch1_begin_event = d.launch1_end_event = None
+    return ms, us
 
-    import oracle
 
-    cur = step.cur[0].cpu()
-    prev = step.prev[0].cpu()
-    attn = step.attn[0].cpu()
-    pos = step.pos.cpu().numpy()
-    offs = step.offs.cpu().numpy()
-    so = step.so.cpu().numpy()
-    ri = step.ri.cpu().numpy()
-    block = step.block.cpu().numpy()
-    R = step.R
-    threads = oracle.default_threads()
-    f = lambda x: float(np.float32(x))  # noqa: E731  (the GPU receives f32 thresholds)
+def result(step: Step, ms, us, kernel, extra=None):
+    r = {"rows": step.rows, "ms_per_step": round(ms, 5),
+         "decisions_per_s": round(step.rows / (ms * 1e-3), 1),
+         "launch1": {"kernel": kernel, "avg_us": round(us, 3),
+                     "algorithmic_bytes": step.launch1_bytes,
+                     "GB/s": round(gbs(step.launch1_bytes, us), 1),
+                     "frac_of_peak": round(gbs(step.launch1_bytes, us) / PEAK_HBM_GBS, 4)}}
+    if extra:
+        r.update(extra)
+    return r
 
-    def one():
-        st = oracle.step_stats(cur, prev, n_threads=threads)
-        oracle.fastdllm_select(st["conf"], so, f(R["tau"]), block)
-        oracle.depcap_boundary(st["kl"], st["entropy"], so, R["l_max"], R["l_min"], R["lam"])
-        oracle.cap_select(cur, ri, so, st["conf"], st["argmax"], st["lse"], f(R["tau_low"]),
-                          f(R["tau_high"]), f(R["gamma"]), R["k_max"], eligible=block,
-                          n_threads=threads)
-        oracle.dapd_select(attn, pos, offs, st["conf"], f(R["dapd_tau"]), n_threads=threads)
 
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        one()
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    model = ""
+def replicas_of(x, n):
+    return [x] + [x.clone() for _ in range(n - 1)]
+
+
+def block_mask(n, lo, hi, dev):
+    import torch
+    m = torch.zeros(n, device=dev, dtype=torch.uint8)
+    m[lo:hi] = 1
+    return m
+
+
+def cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
                 if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": step.rows * reps / el, "unit": "decisions/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"the full step ({step.rows} rows, all five calls) repeated {reps} times "
-                      f"in {el:.1f} s on {threads} threads; host CPU: {model}"}
+    return "unknown"
 
+
+def _timed_reps(fn, seconds, min_reps=1):
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and reps >= min_reps:
+            return reps, el
+
+
+def f32(x):
+    import numpy as np
+    return float(np.float32(x))
+
+
+# ---------------------------------------------------------------- workloads
+
+def llada_workloads(dev, stream, args, res):
+    """The headline step and the all-rules LLaDA step; returns the headline
+    pieces (step, inputs, rules) for the CPU baseline."""
+    from diffusion_lm_unmask_amd import api, synth
+    R = synth.RULES["llada"]
+    spec = synth.SPECS["llada"]
+    cur, prev, so, ri = synth.logits("llada", dev)
+    n = spec.rows
+    block = block_mask(n, *R["fast_block"], dev)
+    curs, prevs = replicas_of(cur, args.replicas), replicas_of(prev, args.replicas)
+    reps = [dict(logits=c, prev=p, seq_offsets=so, row_index=ri) for c, p in zip(curs, prevs)]
+    fast = dict(eligible=block, tau=R["tau"])
+    depcap = dict(lam=R["lam"], l_min=R["l_min"], l_max=R["l_max"])
+    stats_bytes = n * spec.vocab * 2 * 2
+    head = Step("llada", n, reps, stream, stats_bytes, fast=fast, depcap=depcap)
+    ms, us = time_step(head, args.steps, args.warmup)
+    res["llada"] = result(head, ms, us, "k_step_rows (the statistics kernel)",
+                          {"workload": "1 x 256 rows, V=126464 bf16 cur+prev; statistics + "
+                                       "Fast-dLLM 0.9 on block 0 + DepCap (lambda 1.2, L_min 8, "
+                                       "L_max 128)"})
+    # the statistics call on its own (no workspace: the same kernel), back to
+    # back through the C entry point with preallocated outputs
+    import torch
+    from diffusion_lm_unmask_amd import _lib
+    L = _lib.lib()
+    o = head.out(0)
+    outs = [o[k].data_ptr() for k in ("conf", "argmax", "entropy", "kl", "lse")]
+    calls = [(c.data_ptr(), p.data_ptr()) for c, p in zip(curs, prevs)]
+
+    def stats_call(i):
+        c, p = calls[i % len(calls)]
+        st = L.dlm_step_stats(c, p, _lib.BF16, spec.vocab, spec.vocab, ri.data_ptr(), n, *outs,
+                              None, 0, stream)
+        if st:
+            _lib.check(st, "dlm_step_stats")
+
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        stats_call(i)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        stats_call(i)
+    t1.record()
+    torch.cuda.synchronize()
+    call_us = t0.elapsed_time(t1) * 1000.0 / args.steps
+    res["llada"]["stats_call_back_to_back_us"] = round(call_us, 3)
+    print(f"[bench] llada: {res['llada']}", file=sys.stderr, flush=True)
+
+    # every rule on the same rows, with DAPD over [1, 320, 768, 768] attention
+    pos, offs = synth.gen_positions("llada", dev, batch=1)
+    attns = [synth.attention("llada", dev, batch=1) for _ in range(args.replicas)]
+    ws = torch.empty(api.dapd_workspace_bytes(1, n), device=dev, dtype=torch.uint8)
+    cap = dict(eligible=block, tau_low=R["tau_low"], tau_high=R["tau_high"], gamma=R["gamma"],
+               k_max=R["k_max"])
+    avg_bytes = spec.n_lh * n * n * 2 + n * n * 4
+    # the attention replica follows the logits replica
+    reps_a = [dict(r, dapd=dict(attn=a, masked_pos=pos, m_max=n, tau=R["dapd_tau"],
+                                workspace=ws)) for r, a in zip(reps, attns)]
+    allr = Step("llada_all_rules", n, reps_a, stream, stats_bytes + avg_bytes, fast=fast,
+                depcap=depcap, cap=cap)
+    ms2, us2 = time_step(allr, args.steps, args.warmup)
+    res["llada_all_rules"] = result(allr, ms2, us2, "k_step_stream (statistics rows + DAPD "
+                                                    "attention tiles)",
+                                    {"workload": "the llada step + CAP on block 0 (K 32) + DAPD "
+                                                 "over 256 rows, [1, 320, 768, 768] bf16 "
+                                                 "attention, tau 0.01"})
+    print(f"[bench] llada_all_rules: {res['llada_all_rules']}", file=sys.stderr, flush=True)
+    del attns, allr, ws
+    return head, (cur, prev, so, ri, block, R)
+
+
+def dapd_workloads(dev, stream, args, res, cpu):
+    import torch
+    from diffusion_lm_unmask_amd import api, synth
+    spec = synth.SPECS["dapd"]
+    cur, _, so, ri = synth.logits("dapd", dev)
+    n = spec.n_rows
+    pos, offs = synth.gen_positions("dapd", dev)
+    attn = synth.attention("dapd", dev)
+    ws = torch.empty(api.dapd_workspace_bytes(spec.batch, spec.rows), device=dev,
+                     dtype=torch.uint8)
+    stats_bytes = n * spec.vocab * 2
+    avg_bytes = spec.batch * (spec.n_lh * spec.rows * spec.rows * 2 + spec.rows * spec.rows * 4)
+    base = dict(logits=cur, prev=None, seq_offsets=so, row_index=ri)
+    st = Step("dapd_stats", n, [base], stream, stats_bytes)
+    ms0, us0 = time_step(st, args.steps, args.warmup)
+    stats_only = result(st, ms0, us0, "k_step_rows (the statistics kernel)")
+    dp = dict(attn=attn, masked_pos=pos, m_max=spec.rows, tau=synth.RULES["dapd"]["dapd_tau"],
+              workspace=ws)
+    step = Step("dapd", n, [base], stream, stats_bytes + avg_bytes, dapd=dp)
+    ms, us = time_step(step, args.steps, args.warmup)
+    res["dapd"] = result(step, ms, us, "k_step_stream (statistics rows + DAPD attention tiles)",
+                         {"workload": "8 x 256 rows, V=126464 bf16 (no prev) + DAPD over "
+                                      "[8, 320, 768, 768] bf16 attention, 256 masked positions "
+                                      "each, tau 0.01 (no edge: the graph is empty)",
+                          "statistics_only": stats_only})
+    print(f"[bench] dapd: {res['dapd']}", file=sys.stderr, flush=True)
+    if cpu is not None:
+        cpu["dapd"] = (step, cur, attn, pos, offs, so)
+    # the same step on the edge-rich attention (partner covariance): the greedy runs
+    attn_cov = synth.attention("dapd", dev, variant="cov", masked_pos=pos[:spec.rows])
+    dpc = dict(dp, attn=attn_cov)
+    stepc = Step("dapd_cov", n, [base], stream, stats_bytes + avg_bytes, dapd=dpc)
+    msc, usc = time_step(stepc, args.steps, args.warmup)
+    o = stepc.out()
+    torch.cuda.synchronize()
+    n_commit = o["dapd"][1].cpu().tolist()
+    res["dapd_cov"] = result(stepc, msc, usc, "k_step_stream (statistics rows + DAPD attention "
+                                              "tiles)",
+                             {"workload": "the dapd step on the partner-covariance attention "
+                                          "(3 masked partners per position, +4 logits): an "
+                                          "edge-rich graph, so the Welsh-Powell greedy runs",
+                              "dapd_committed_per_sequence": n_commit})
+    print(f"[bench] dapd_cov: {res['dapd_cov']}", file=sys.stderr, flush=True)
+    del attn_cov, stepc
+    if cpu is None:
+        del attn
+    torch.cuda.empty_cache()
+
+
+def stress_workload(dev, stream, args, res, cpu):
+    import torch
+    from diffusion_lm_unmask_amd import synth
+    spec = synth.SPECS["stress"]
+    R = synth.RULES["stress"]
+    cur, prev, so, ri = synth.logits("stress", dev)
+    n = spec.n_rows
+    step = Step("stress", n, [dict(logits=cur, prev=prev, seq_offsets=so, row_index=ri)], stream,
+                n * spec.vocab * 2 * 2,
+                depcap=dict(lam=R["lam"], l_min=R["l_min"], l_max=R["l_max"]),
+                cap=dict(tau_low=R["tau_low"], tau_high=R["tau_high"], gamma=R["gamma"],
+                         k_max=R["k_max"]))
+    steps = max(3, min(args.steps, 10))
+    ms, us = time_step(step, steps, min(args.warmup, 2))
+    res["stress"] = result(step, ms, us, "k_step_rows (the statistics kernel)",
+                           {"workload": "64 x 1024 rows, V=126464 bf16 cur+prev (33.15 GB) + "
+                                        "DepCap (defaults) + CAP (0.8 / 0.95 / -16, K 128) over "
+                                        "every row",
+                            "steps": steps})
+    print(f"[bench] stress: {res['stress']}", file=sys.stderr, flush=True)
+    if cpu is not None:
+        # the oracle's sample: every 8th sequence (8 of 64), copied to the host
+        sample = list(range(0, spec.batch, 8))
+        o = step.out()
+        torch.cuda.synchronize()
+        rows = [slice(b * spec.rows, (b + 1) * spec.rows) for b in sample]
+        cpu["stress"] = dict(
+            sample=sample,
+            cur=torch.cat([cur[r].cpu() for r in rows]), prev=torch.cat([prev[r].cpu() for r in rows]),
+            gpu={k: (None if o[k] is None else torch.cat([o[k][r].cpu() for r in rows]))
+                 for k in ("conf", "entropy", "kl", "lse", "argmax")},
+            depcap=o["depcap"][0][sample].cpu(),
+            cap=torch.cat([o["cap"][0][r].cpu() for r in rows]), R=R, rows=spec.rows)
+    del cur, prev, step
+    torch.cuda.empty_cache()
+
+
+def dream_workload(dev, stream, args, res):
+    import torch
+    from diffusion_lm_unmask_amd import synth
+    spec = synth.SPECS["dream"]
+    R = synth.RULES["dream"]
+    cur, _, so, ri = synth.logits("dream", dev)
+    n = spec.n_rows
+    step = Step("dream", n, [dict(logits=cur, prev=None, seq_offsets=so, row_index=ri)], stream,
+                n * spec.vocab * 2,
+                cap=dict(tau_low=R["tau_low"], tau_high=R["tau_high"], gamma=R["gamma"],
+                         k_max=R["k_max"]))
+    ms, us = time_step(step, args.steps, args.warmup)
+    res["dream"] = result(step, ms, us, "k_step_rows (the statistics kernel)",
+                          {"workload": "16 x 256 rows, V=151936 bf16 (no prev) + CAP (0.7 / 0.95 "
+                                       "/ -16, K 64) over every row"})
+    print(f"[bench] dream: {res['dream']}", file=sys.stderr, flush=True)
+    del cur, step
+    torch.cuda.empty_cache()
+
+
+def tiny_workload(dev, stream, args, res):
+    from diffusion_lm_unmask_amd import synth
+    R = synth.RULES["tiny"]
+    cur, prev, so, ri = synth.logits("tiny", dev)
+    n = cur.shape[0]
+    block = block_mask(n, 0, n, dev)
+    attn = synth.attention("tiny", dev)
+    pos, offs = synth.gen_positions("tiny", dev)
+    step = Step("tiny", n, [dict(logits=cur, prev=prev, seq_offsets=so, row_index=ri)], stream,
+                cur.numel() * 4 * 2 + 32 * 32 * 4 + 32 * 32 * 4,
+                fast=dict(eligible=block, tau=R["tau"]),
+                depcap=dict(lam=R["lam"], l_min=R["l_min"], l_max=R["l_max"]),
+                cap=dict(eligible=block, tau_low=R["tau_low"], tau_high=R["tau_high"],
+                         gamma=R["gamma"], k_max=R["k_max"]),
+                dapd=dict(attn=attn, masked_pos=pos, m_max=32, tau=R["dapd_tau"]))
+    ms, us = time_step(step, args.steps, args.warmup)
+    r = result(step, ms, us, "k_step_stream")
+    r["workload"] = "1 x 32 rows, V=4096 fp32 cur+prev, every rule (latency-bound)"
+    r["us_per_step"] = round(ms * 1000.0, 2)
+    res["tiny"] = r
+    print(f"[bench] tiny: {r}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- oracle leg
+
+def _stats_err(g, o, keys):
+    import numpy as np
+    w = 0.0
+    for k in keys:
+        a = g[k].double().numpy() if hasattr(g[k], "double") else np.asarray(g[k], np.float64)
+        b = np.asarray(o[k], np.float64)
+        m = np.isfinite(b)
+        if m.any():
+            w = max(w, float(np.max(np.abs(a[m] - b[m]))))
+    return w
+
+
+def cpu_leg(head, head_inputs, cpu, seconds):
+    """The oracle (as it stands) on host copies of the exact inputs: timed on
+    the LLaDA step (all threads and one thread), on the DAPD step and on an
+    8-of-64-sequence sample of the stress step; its decisions are compared
+    with the GPU's."""
+    import numpy as np
+    import torch
+
+    import oracle
+    threads = oracle.default_threads()
+    cur, prev, so, ri, block, R = head_inputs
+    cur_h, prev_h = cur.cpu(), prev.cpu()
+    so_h, block_h = so.cpu().numpy(), block.cpu().numpy()
+    parity = {}
+    baselines = {}
+
+    def llada_once(nt):
+        st = oracle.step_stats(cur_h, prev_h, n_threads=nt)
+        c, _ = oracle.fastdllm_select(st["conf"], so_h, f32(R["tau"]), block_h)
+        L, _ = oracle.depcap_boundary(st["kl"], st["entropy"], so_h, R["l_max"], R["l_min"],
+                                      R["lam"])
+        return st, c, L
+
+    reps, el = _timed_reps(lambda: llada_once(threads), seconds)
+    main = {"value": round(head.rows * reps / el, 1), "unit": "decisions/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the full llada step (statistics of 256 rows, Fast-dLLM, DepCap) repeated "
+                      f"{reps} times in {el:.1f} s on {threads} threads; host CPU: {cpu_model()}"}
+    reps1, el1 = _timed_reps(lambda: llada_once(1), min(seconds, 4.0))
+    baselines["llada_1_thread"] = {"value": round(head.rows * reps1 / el1, 1),
+                                   "unit": "decisions/s", "cores": 1,
+                                   "sample": f"the same step, {reps1} repetitions in {el1:.1f} s"}
+    # decisions against the GPU's (replica 0)
+    head.run(0)
+    torch.cuda.synchronize()
+    g = head.out(0)
+    st, c_o, L_o = llada_once(threads)
+    gh = {k: g[k].cpu() for k in ("conf", "entropy", "kl", "lse", "argmax")}
+    same = (np.array_equal(g["fast"][0].cpu().numpy(), c_o) and
+            int(g["depcap"][0].cpu()[0]) == int(L_o[0]))
+    parity["llada"] = {"sequences": 1, "identical": int(same), "flagged": int(not same),
+                       "argmax_equal": bool(np.array_equal(gh["argmax"].numpy(), st["argmax"])),
+                       "stats_max_abs_err": _stats_err(gh, st, ("conf", "entropy", "kl"))}
+
+    if "dapd" in cpu:
+        step, dcur, attn, pos, offs, dso = cpu["dapd"]
+        step.run(0)
+        torch.cuda.synchronize()
+        g = step.out(0)
+        dcur_h, attn_h = dcur.cpu(), attn.cpu()
+        pos_h, offs_h = pos.cpu().numpy(), offs.cpu().numpy()
+        t0 = time.perf_counter()
+        st = oracle.step_stats(dcur_h, None, n_threads=threads)
+        d_o = oracle.dapd_select(attn_h, pos_h, offs_h, st["conf"], f32(0.01), m_max=256,
+                                 n_threads=threads)
+        el = time.perf_counter() - t0
+        baselines["dapd"] = {"value": round(step.rows / el, 1), "unit": "decisions/s",
+                             "cores": threads,
+                             "sample": f"the full dapd step (statistics of 2048 rows, DAPD over "
+                                       f"8 sequences) once in {el:.2f} s"}
+        gc = g["dapd"][0].cpu().numpy()
+        ident = sum(int(np.array_equal(gc[offs_h[b]:offs_h[b + 1]],
+                                       d_o["commit"][offs_h[b]:offs_h[b + 1]]))
+                    for b in range(len(offs_h) - 1))
+        gh = {k: g[k].cpu() for k in ("conf", "entropy", "argmax")}
+        parity["dapd"] = {"sequences": len(offs_h) - 1, "identical": ident,
+                          "flagged": len(offs_h) - 1 - ident,
+                          "argmax_equal": bool(np.array_equal(gh["argmax"].numpy(),
+                                                              st["argmax"])),
+                          "stats_max_abs_err": _stats_err(gh, st, ("conf", "entropy"))}
+        del attn_h, dcur_h
+
+    if "stress" in cpu:
+        s = cpu["stress"]
+        Rs, M, B = s["R"], s["rows"], len(s["sample"])
+        so_s = np.arange(0, (B + 1) * M, M, dtype=np.int32)
+        ri_s = np.arange(B * M, dtype=np.int64)
+        t0 = time.perf_counter()
+        st = oracle.step_stats(s["cur"], s["prev"], n_threads=threads)
+        L_o, _ = oracle.depcap_boundary(st["kl"], st["entropy"], so_s, Rs["l_max"], Rs["l_min"],
+                                        Rs["lam"])
+        c_o = oracle.cap_select(s["cur"], ri_s, so_s, st["conf"], st["argmax"], st["lse"],
+                                f32(Rs["tau_low"]), f32(Rs["tau_high"]), f32(Rs["gamma"]),
+                                Rs["k_max"], n_threads=threads)
+        el = time.perf_counter() - t0
+        baselines["stress_sample"] = {
+            "value": round(B * M / el, 1), "unit": "decisions/s", "cores": threads,
+            "sample": f"sequences {s['sample']} of 64 ({B * M} rows, statistics + DepCap + CAP) "
+                      f"in {el:.2f} s",
+            "extrapolated_full_step_s": round(el * 64 / B, 2),
+            "extrapolation": f"x{64 // B}, labelled: the full 64-sequence step was not run"}
+        gd = s["depcap"].numpy()
+        gcap = s["cap"].numpy()
+        ident = 0
+        for b in range(B):
+            r = slice(b * M, (b + 1) * M)
+            ident += int(int(gd[b]) == int(L_o[b]) and
+                         np.array_equal(gcap[r], c_o["commit"][r]))
+        parity["stress_sample"] = {"sequences": B, "identical": ident, "flagged": B - ident,
+                                   "argmax_equal": bool(np.array_equal(
+                                       s["gpu"]["argmax"].numpy(), st["argmax"])),
+                                   "stats_max_abs_err": _stats_err(s["gpu"], st,
+                                                                   ("conf", "entropy", "kl"))}
+    return main, baselines, parity
+
+
+# ------------------------------------------------------------ per-call mode
 
 def per_call(dev: str, iters: int) -> dict:
-    """Time every entry point on the workloads it is defined on (the five
-    workload shapes of the decision step).  Each measurement captures `iters`
-    calls (rotating input replicas where the inputs would fit in the 256 MB
-    Infinity Cache) in a HIP graph and times replays with HIP events, so small
-    kernels are timed on the GPU rather than through host launch latency.
-    HBM-bound calls also report GB/s against the 8 TB/s peak."""
+    """Time every entry point on the workloads it is defined on.  Each
+    measurement captures `iters` calls (rotating input replicas where the
+    inputs would fit in the 256 MB Infinity Cache) in a HIP graph and times
+    replays with HIP events, so small kernels are timed on the GPU rather than
+    through host launch latency.  HBM-bound calls also report GB/s."""
     import torch
     from diffusion_lm_unmask_amd import api, synth
 
@@ -344,8 +580,6 @@ def per_call(dev: str, iters: int) -> dict:
     stream = torch.cuda.Stream(device=dev)
 
     def timed(name, fn, n_rep=1, nbytes=None, note=None):
-        # every input was produced on `stream` (see below); wait for it all
-        # before the first use, and keep every launch on that one stream
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             for i in range(2):
@@ -381,8 +615,8 @@ def per_call(dev: str, iters: int) -> dict:
     def stats_of(name, replicas):
         spec = synth.SPECS[name]
         cur, prev, so, ri = synth.logits(name, dev)
-        curs = [cur] + [cur.clone() for _ in range(replicas - 1)]
-        prevs = None if prev is None else [prev] + [prev.clone() for _ in range(replicas - 1)]
+        curs = replicas_of(cur, replicas)
+        prevs = None if prev is None else replicas_of(prev, replicas)
         nb = cur.numel() * cur.element_size() * (1 if prev is None else 2)
         timed(f"step_stats/{name}",
               lambda r: api.step_stats(curs[r], None if prevs is None else prevs[r]),
@@ -401,105 +635,79 @@ def per_call(dev: str, iters: int) -> dict:
               lambda r: api.fixed_block_eligible(pos, offs, 32, gen_start=gs))
 
     with torch.cuda.stream(stream):
-        return _per_call_body(dev, timed, stats_of, schedules, res)
-
-
-def _per_call_body(dev, timed, stats_of, schedules, res):
-    """The workloads of per_call, run with its stream current: the inputs,
-    the reference statistics the rules consume and every timed call are
-    ordered on one stream."""
-    import torch
-    from diffusion_lm_unmask_amd import api, synth
-
-    # tiny
-    spec, cur, prev, so, ri, st, _ = stats_of("tiny", 4)
-    del cur, prev, st
-    # llada-shaped step inputs
-    spec, cur, prev, so, ri, st, curs = stats_of("llada", 4)
-    R = synth.RULES["llada"]
-    block = torch.zeros(cur.shape[0], device=dev, dtype=torch.uint8)
-    block[R["fast_block"][0]:R["fast_block"][1]] = 1
-    pos, offs = synth.gen_positions("llada", dev)
-    schedules("llada", st, so, block, pos, offs)
-    timed("depcap_boundary/llada", lambda r: api.depcap_boundary(st["kl"], st["entropy"], so))
-    timed("cap_select/llada", lambda r: api.cap_select(
-        curs[r], ri, so, st["conf"], st["argmax"], st["lse"], eligible=block, k_max=R["k_max"]), 4)
-    attn = [synth.attention("llada", dev, batch=1) for _ in range(4)]
-    ws = torch.empty(api.dapd_workspace_bytes(1, 256), device=dev, dtype=torch.uint8)
-    nb = 320 * 256 * 256 * 2 + 256 * 256 * 4
-    timed("dapd_select/llada", lambda r: api.dapd_select(attn[r], pos, offs, st["conf"], 0.01,
-                                                         m_max=256, workspace=ws), 4, nb,
-          "1 x [320, 768, 768] bf16 maps, 256 masked")
-    # the whole step as one call (two launches)
-    prevs = [prev] + [prev.clone() for _ in range(3)]
-    parts = dict(fast=dict(eligible=block, tau=R["tau"]),
-                 depcap=dict(lam=R["lam"], l_min=R["l_min"], l_max=R["l_max"]),
-                 cap=dict(eligible=block, tau_low=R["tau_low"], tau_high=R["tau_high"],
-                          gamma=R["gamma"], k_max=R["k_max"]))
-    timed("decide_step/llada", lambda r: api.decide_step(
-        curs[r], prevs[r], so, row_index=ri, **parts,
-        dapd=dict(attn=attn[r], masked_pos=pos, m_max=256, tau=R["dapd_tau"], workspace=ws)),
-          4, cur.numel() * 2 * 2 + nb, "statistics, Fast-dLLM, DepCap, CAP and DAPD in one call")
-    del cur, prev, curs, prevs, attn, st
-    torch.cuda.empty_cache()
-    # dream: CAP with K_max 64 over every row
-    spec, cur, prev, so, ri, st, _ = stats_of("dream", 1)
-    Rd = synth.RULES["dream"]
-    timed("cap_select/dream", lambda r: api.cap_select(
-        cur, ri, so, st["conf"], st["argmax"], st["lse"], tau_low=Rd["tau_low"],
-        k_max=Rd["k_max"]))
-    del cur, st
-    torch.cuda.empty_cache()
-    # dapd: 8 sequences, plain selection and the full step (half of them late)
-    spec, cur, prev, so, ri, st, _ = stats_of("dapd", 2)
-    pos, offs = synth.gen_positions("dapd", dev)
-    attn = [synth.attention("dapd", dev, variant="cov", masked_pos=pos[:spec.rows])]
-    ws = torch.empty(api.dapd_workspace_bytes(spec.batch, 256), device=dev, dtype=torch.uint8)
-    nb = spec.batch * (320 * 256 * 256 * 2 + 256 * 256 * 4)
-    timed("dapd_select/dapd", lambda r: api.dapd_select(attn[0], pos, offs, st["conf"], 0.01,
-                                                        m_max=256, workspace=ws), 1, nb,
-          "8 x [320, 768, 768] bf16 maps, 256 masked each, partner-covariance variant")
-    gen_len = torch.tensor([256, 384, 512, 600, 256, 700, 1000, 400], device=dev,
-                           dtype=torch.int32)
-    timed("dapd_step/dapd", lambda r: api.dapd_step(attn[0], pos, offs, st["conf"], 0.01,
-                                                    gen_len=gen_len, m_max=256, workspace=ws),
-          1, None, "same, 3 of 8 sequences in the late stage")
-    timed("decide_step/dapd", lambda r: api.decide_step(
-        cur, None, offs, row_index=ri, fast=dict(tau=0.9), cap=dict(k_max=64),
-        dapd=dict(attn=attn[0], masked_pos=pos, m_max=256, tau=0.01, workspace=ws)),
-          1, cur.numel() * 2 + nb, "statistics, Fast-dLLM, CAP (every row) and DAPD, 8 sequences")
-    del cur, attn, st
-    torch.cuda.empty_cache()
-    # stress: 64 x 1024 rows with prev (33 GB)
-    spec, cur, prev, so, ri, st, _ = stats_of("stress", 1)
-    pos = (torch.arange(1024, device=dev, dtype=torch.int32) + 512).repeat(spec.batch)
-    schedules("stress", st, so, None, pos, so)
-    timed("depcap_boundary/stress", lambda r: api.depcap_boundary(st["kl"], st["entropy"], so))
-    timed("cap_select/stress", lambda r: api.cap_select(cur, ri, so, st["conf"], st["argmax"],
-                                                        st["lse"], k_max=128))
-    del cur, prev, st
-    torch.cuda.empty_cache()
+        spec, cur, prev, so, ri, st, _ = stats_of("tiny", 4)
+        del cur, prev, st
+        spec, cur, prev, so, ri, st, curs = stats_of("llada", 4)
+        R = synth.RULES["llada"]
+        block = block_mask(cur.shape[0], *R["fast_block"], dev)
+        pos, offs = synth.gen_positions("llada", dev)
+        schedules("llada", st, so, block, pos, offs)
+        timed("depcap_boundary/llada", lambda r: api.depcap_boundary(st["kl"], st["entropy"], so))
+        timed("cap_select/llada", lambda r: api.cap_select(
+            curs[r], ri, so, st["conf"], st["argmax"], st["lse"], eligible=block,
+            k_max=R["k_max"]), 4)
+        attn = [synth.attention("llada", dev, batch=1) for _ in range(4)]
+        ws = torch.empty(api.dapd_workspace_bytes(1, 256), device=dev, dtype=torch.uint8)
+        nb = 320 * 256 * 256 * 2 + 256 * 256 * 4
+        timed("dapd_select/llada", lambda r: api.dapd_select(attn[r], pos, offs, st["conf"], 0.01,
+                                                             m_max=256, workspace=ws), 4, nb,
+              "1 x [320, 768, 768] bf16 maps, 256 masked")
+        timed("dapd_select_static/llada", lambda r: api.dapd_select_static(
+            attn[r], pos, offs, st["conf"], 0.01, m_max=256), 4, nb,
+              "the same with the library's static workspace")
+        del cur, prev, curs, attn, st
+        torch.cuda.empty_cache()
+        spec, cur, prev, so, ri, st, _ = stats_of("dream", 1)
+        Rd = synth.RULES["dream"]
+        timed("cap_select/dream", lambda r: api.cap_select(
+            cur, ri, so, st["conf"], st["argmax"], st["lse"], tau_low=Rd["tau_low"],
+            k_max=Rd["k_max"]))
+        del cur, st
+        torch.cuda.empty_cache()
+        spec, cur, prev, so, ri, st, _ = stats_of("dapd", 2)
+        pos, offs = synth.gen_positions("dapd", dev)
+        attn = synth.attention("dapd", dev, variant="cov", masked_pos=pos[:spec.rows])
+        ws = torch.empty(api.dapd_workspace_bytes(spec.batch, 256), device=dev,
+                         dtype=torch.uint8)
+        nb = spec.batch * (320 * 256 * 256 * 2 + 256 * 256 * 4)
+        timed("dapd_select/dapd", lambda r: api.dapd_select(attn, pos, offs, st["conf"], 0.01,
+                                                            m_max=256, workspace=ws), 1, nb,
+              "8 x [320, 768, 768] bf16 maps, 256 masked each, partner-covariance variant")
+        gen_len = torch.tensor([256, 384, 512, 600, 256, 700, 1000, 400], device=dev,
+                               dtype=torch.int32)
+        timed("dapd_step/dapd", lambda r: api.dapd_step(attn, pos, offs, st["conf"], 0.01,
+                                                        gen_len=gen_len, m_max=256, workspace=ws),
+              1, None, "same, 3 of 8 sequences in the late stage")
+        del cur, attn, st
+        torch.cuda.empty_cache()
+        spec, cur, prev, so, ri, st, _ = stats_of("stress", 1)
+        pos = (torch.arange(1024, device=dev, dtype=torch.int32) + 512).repeat(spec.batch)
+        schedules("stress", st, so, None, pos, so)
+        timed("depcap_boundary/stress", lambda r: api.depcap_boundary(st["kl"], st["entropy"],
+                                                                      so))
+        timed("cap_select/stress", lambda r: api.cap_select(cur, ri, so, st["conf"],
+                                                            st["argmax"], st["lse"], k_max=128))
+        del cur, prev, st
+        torch.cuda.empty_cache()
     return res
 
+
+# ---------------------------------------------------------------------- main
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown-iters", type=int, default=200)
+    ap.add_argument("--only", default="",
+                    help="comma-separated sub-workloads to run besides the headline "
+                         "(llada_all_rules is always run): dapd,stress,dream,tiny; default all")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 10 plain device-to-device copies of MIB MiB (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
-    ap.add_argument("--mode", choices=("fused", "fused-graph", "graph", "eager"),
-                    default="fused",
-                    help="fused: one dlm_decide_step call (two launches) per step; "
-                         "fused-graph: that call captured once per input replica and "
-                         "replayed; graph: the five individual calls captured and replayed; "
-                         "eager: the five calls launched one by one")
     ap.add_argument("--calls", action="store_true",
                     help="only time every entry point on its workloads and print one JSON line")
     ap.add_argument("--call-iters", type=int, default=20)
@@ -530,146 +738,46 @@ def main() -> int:
         print(json.dumps({"calls": per_call(dev, args.call_iters), "n_gpus": 1,
                           "data": "synthetic"}), flush=True)
         return 0
-    step = LladaStep(args.replicas, dev)
-    R = args.replicas
-    sm = step.torch_stream
+
+    only = set(w for w in args.only.split(",") if w) or {"dapd", "stress", "dream", "tiny"}
+    # every launch goes to this stream (default priority)
+    ts = torch.cuda.Stream(device=dev)
+    stream = ts.cuda_stream
+    cpu = None if args.no_cpu_baseline else {}
+    res = {}
+    with torch.cuda.stream(ts):
+        head, head_inputs = llada_workloads(dev, stream, args, res)
+        if "tiny" in only:
+            tiny_workload(dev, stream, args, res)
+        if "dapd" in only:
+            dapd_workloads(dev, stream, args, res, cpu)
+        if "dream" in only:
+            dream_workload(dev, stream, args, res)
+        if "stress" in only:
+            stress_workload(dev, stream, args, res, cpu)
     torch.cuda.synchronize()
 
-    def timed_eager(n_steps, fused):
-        """Eager run of n_steps steps with HIP events on the dominant launch
-        of each step (set by the fused streaming launch itself, else recorded
-        around the statistics call), on the launch stream."""
-        events = TimingEvents(n_steps)
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(sm):
-            t0.record()
-            for i in range(n_steps):
-                if fused:
-                    step.fused(i % R, events.pairs[i])
-                else:
-                    step.step(i % R, events.pairs[i], events)
-            t1.record()
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / n_steps
-        us = events.mean_us()
-        events.close()
-        return ms, us
-
-    fused = args.mode in ("fused", "fused-graph")
-    run = step.fused if fused else step.step
-    with torch.cuda.stream(sm):
-        for i in range(args.warmup):
-            run(i % R)
-    torch.cuda.synchronize()
-
-    # on replica 0: the fused step's decisions against the four rule calls run
-    # on the fused statistics (bitwise), and its statistics against the
-    # statistics call (argmax identical, floats to the last bits)
-    with torch.cuda.stream(sm):
-        step.fused(0)
-    torch.cuda.synchronize()
-    fused_out = step.outputs()
-    with torch.cuda.stream(sm):
-        for name in ("fastdllm", "depcap", "cap", "dapd"):
-            getattr(step, name)(0)
-    torch.cuda.synchronize()
-    rules_out = step.outputs()
-    decisions_idx = (5, 6, 7, 8, 9, 10, 11, 12)     # every commit, count, length and score
-    fused_match = all(torch.equal(rules_out[i], fused_out[i]) for i in decisions_idx)
-    with torch.cuda.stream(sm):
-        step.stats(0)
-    torch.cuda.synchronize()
-    calls_out = step.outputs()
-    fused_match = fused_match and torch.equal(calls_out[1], fused_out[1])
-    stats_diff = max(float((calls_out[i].view(torch.float32).double() -
-                            fused_out[i].view(torch.float32).double()).abs().max())
-                     for i in (0, 2, 3, 4))
-
-    def timed_plain(fn):
-        """K steps back to back on the launch stream, bracketed by events."""
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(sm):
-            t0.record()
-            for i in range(args.steps):
-                fn(i % R)
-            t1.record()
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / args.steps
-
-    graph_ok = None
-    if args.mode in ("graph", "fused-graph"):
-        # one captured step per input replica; replays run its kernels back
-        # to back without host launch overhead
-        graphs = []
-        for r in range(R):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=sm):
-                run(r)
-            graphs.append(g)
-        torch.cuda.synchronize()
-        # replay correctness: each replica's replay equals its eager step
-        graph_ok = True
-        for r in range(R):
-            with torch.cuda.stream(sm):
-                run(r)
-            torch.cuda.synchronize()
-            want = step.outputs()
-            graphs[r].replay()
-            torch.cuda.synchronize()
-            got = step.outputs()
-            graph_ok = graph_ok and all(torch.equal(a, b) for a, b in zip(want, got))
-        for i in range(args.warmup):
-            graphs[i % R].replay()
-        ms_per_step = timed_plain(lambda r: graphs[r].replay())
-    else:
-        ms_per_step = timed_plain(run)
-    # the dominant kernel's live duration over a second run of the same steps:
-    # HIP events on its launch stream, which the fused step's launch sets to
-    # the kernel's own start and end (the five-call step records them around
-    # the statistics call instead)
-    events_ms, dom_us = timed_eager(args.steps, fused)
-    # the statistics call on its own (the five calls, eager), for reference
-    calls_events_ms, stats_us = timed_eager(args.steps, False)
-
-    # per-call breakdown (untimed region, same rotation)
-    breakdown = {}
-    for name in ("stats", "fastdllm", "depcap", "cap", "dapd"):
-        fn = getattr(step, name)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(sm):
-            for i in range(10):
-                step.step(i % R)
-            torch.cuda.synchronize()
-            acc = 0.0
-            for i in range(args.breakdown_iters):
-                e0.record()
-                fn(i % R)
-                e1.record()
-                e1.synchronize()
-                acc += e0.elapsed_time(e1)
-                step.step((i + 1) % R)          # keep the inputs cold in cache
-        breakdown[name] = round(acc / args.breakdown_iters * 1000.0, 2)
-
-    if fused:
-        dom, dom_label = "k_step_stream", "dlm_decide_step launch 1 (k_step_stream)"
-        dom_bytes = step.bytes_stats + step.bytes_avg
-    else:
-        dom, dom_label = "k_stats", "dlm_step_stats (k_stats)"
-        dom_bytes = step.bytes_stats
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    st_achieved = step.bytes_stats / (stats_us * 1e-6) / 1e9
-    decisions = step.rows
-    value = decisions / (ms_per_step * 1e-3)
+    h = res["llada"]
+    l1 = h["launch1"]
+    stats_kernel = {w: {"kernel": "k_step_rows", "avg_us": r["launch1"]["avg_us"],
+                        "algorithmic_bytes": r["launch1"]["algorithmic_bytes"],
+                        "frac_of_peak": r["launch1"]["frac_of_peak"]}
+                    for w, r in (("llada", h), ("stress", res.get("stress")),
+                                 ("dream", res.get("dream"))) if r}
+    if "dapd" in res:
+        stats_kernel["dapd"] = {k: v for k, v in res["dapd"]["statistics_only"]["launch1"].items()
+                                if k != "GB/s"}
+        stats_kernel["dapd"]["kernel"] = "k_step_rows"
+    v126 = [stats_kernel[w]["frac_of_peak"] for w in ("llada", "dapd", "stress")
+            if w in stats_kernel]
     line = {
-        "metric": "masked-row decisions/sec and achieved HBM GB/s (% of peak), V=126464 bf16",
-        "value": round(value, 1),
+        "metric": METRIC,
+        "value": h["decisions_per_s"],
         "unit": "decisions/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -677,33 +785,29 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": "llada-step: 1 seq x 256 masked rows, V=126464 bf16 cur+prev logits; "
-                        "Fast-dLLM + DepCap boundary + CAP on block 0 + DAPD over 256 rows",
-            "rows": step.rows, "vocab": step.V, "attention": [1, step.n_lh, step.S, step.S],
-            "replicas": args.replicas, "mode": args.mode,
+                        "statistics + Fast-dLLM threshold 0.9 on block 0 + DepCap boundary "
+                        "(lambda 1.2, L_min 8, L_max 128), one dlm_decide_step per step",
+            "rows": 256, "vocab": 126464, "replicas": args.replicas,
         },
-        "events_run_ms_per_step": round(events_ms, 5),
-        "graph_replay_matches_eager": graph_ok,
-        "fused_decisions_match_rule_calls": fused_match,
-        "fused_stats_max_abs_diff_vs_stats_call": stats_diff,
-        "calls_events_run_ms_per_step": round(calls_events_ms, 5),
         "roofline": {
-            "bound": "hbm", "kernel": dom_label,
-            "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(dom), "traffic_unit": "bytes/launch",
-            "algorithmic_bytes_per_launch": dom_bytes,
-            "avg_launch_us": round(dom_us, 3),
+            "bound": "hbm", "kernel": "k_step_rows (dlm_decide_step launch 1: the statistics "
+                                      "kernel of dlm_step_stats)",
+            "achieved": l1["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": l1["frac_of_peak"],
+            "traffic": measured_traffic("llada/k_step_rows", "k_step_rows"),
+            "traffic_unit": "bytes/launch",
+            "algorithmic_bytes_per_launch": l1["algorithmic_bytes"],
+            "avg_launch_us": l1["avg_us"],
         },
-        "stats_call_roofline": {
-            "kernel": "dlm_step_stats (k_stats)", "achieved": round(st_achieved, 1),
-            "frac": round(st_achieved / PEAK_HBM_GBS, 4), "avg_launch_us": round(stats_us, 3),
-            "algorithmic_bytes_per_launch": step.bytes_stats,
-            "traffic": measured_traffic("k_stats"),
-        },
-        "breakdown_us": breakdown,
+        "stats_kernel": dict(stats_kernel, target_frac=0.70,
+                             min_frac_over_v126464=min(v126) if v126 else None),
+        "workloads": res,
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)
+    if cpu is not None:
+        main_b, baselines, parity = cpu_leg(head, head_inputs, cpu, args.cpu_seconds)
+        line["cpu_baseline"] = main_b
+        line["cpu_baselines"] = baselines
+        line["oracle_parity"] = parity
     print(json.dumps(line), flush=True)
     return 0
 

@@ -391,9 +391,13 @@ def fixed_block_eligible(masked_pos, seq_offsets, block_len, gen_start=None):
     return el
 
 
-def decide_step(logits, prev=None, seq_offsets=None, row_index=None, vocab=None, fast=None,
-                depcap=None, cap=None, dapd=None):
-    """dlm_decide_step: statistics plus the enabled rules in two launches.
+def step_descriptor(logits, prev=None, seq_offsets=None, row_index=None, vocab=None, fast=None,
+                    depcap=None, cap=None, dapd=None):
+    """The dlm_step_desc of a dlm_decide_step call, without calling it.
+    Returns (desc, out, keep): the filled descriptor, the output tensors it
+    points into (the dict decide_step returns) and the input tensors it
+    points into (keep both alive while the descriptor is used).  For callers
+    that issue the same step many times (a decoding loop, the benchmark).
 
     Each rule part is None (off) or a dict of its parameters, named as in the
     individual wrappers:
@@ -401,7 +405,7 @@ def decide_step(logits, prev=None, seq_offsets=None, row_index=None, vocab=None,
       depcap = dict(has_prev=None, lam=1.2, l_min=8, l_max=128, radius=1, eps=1e-12)
       cap    = dict(eligible=None, tau_low=0.8, tau_high=0.95, gamma=-16.0, k_max=64)
       dapd   = dict(attn=..., masked_pos=..., m_max=..., tau=0.01, workspace=None)
-    Returns a dict with the statistics (conf, argmax, entropy, kl, lse) and, per
+    `out` holds the statistics (conf, argmax, entropy, kl, lse) and, per
     enabled part, its outputs (fast / depcap / cap / dapd)."""
     ld = _rows2d(logits, "logits")
     dev = logits.device
@@ -486,6 +490,16 @@ def decide_step(logits, prev=None, seq_offsets=None, row_index=None, vocab=None,
         d.dapd_commit, d.dapd_n_commit = out["dapd"][0].data_ptr(), out["dapd"][1].data_ptr()
         d.dapd_workspace, d.dapd_workspace_bytes = ws.data_ptr(), ws.numel()
         keep += [attn, pos, ws]
+    keep += [logits, prev]
+    return d, out, keep
+
+
+def decide_step(logits, prev=None, seq_offsets=None, row_index=None, vocab=None, fast=None,
+                depcap=None, cap=None, dapd=None):
+    """dlm_decide_step: statistics plus the enabled rules in two launches.
+    Arguments and the returned dict as for step_descriptor (see there)."""
+    d, out, keep = step_descriptor(logits, prev, seq_offsets, row_index, vocab, fast, depcap, cap,
+                                   dapd)
     st = _lib.lib().dlm_decide_step(ctypes.byref(d), _stream(logits))
     _lib.check(st, "dlm_decide_step")
     return out
