@@ -100,18 +100,32 @@ def _rows2d(logits, name):
 
 
 _WORKSPACES: dict = {}
+_RETIRED: list = []
 
 
 def stats_workspace(n_rows: int, device) -> torch.Tensor:
     """Zero-filled dlm_step_stats workspace for `n_rows` rows, cached per
     (device, current stream): the library leaves it zero-filled after every
-    call, and calls on one stream never overlap."""
+    call, and calls on one stream never overlap.
+
+    A workspace is never freed: when a call needs a larger one, the smaller
+    one is kept alive (a HIP graph captured earlier may still point at it).
+    A new workspace is never made during stream capture, where its zero fill
+    would only be recorded: call once eagerly on the stream first, or pass
+    split=False."""
     dev = torch.device(device)
     key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
     need = int(_lib.lib().dlm_step_stats_workspace_bytes(int(n_rows)))
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < need:
+        if torch.cuda.is_current_stream_capturing():
+            raise DLMError("the statistics workspace for this many rows does not exist yet and "
+                           "cannot be created under graph capture: call step_stats once "
+                           "eagerly on this stream first, or pass split=False")
+        if ws is not None:
+            _RETIRED.append(ws)
         ws = torch.zeros(max(need, 256), device=dev, dtype=torch.uint8)
+        torch.cuda.synchronize(dev)          # zeroed before any kernel can use it
         _WORKSPACES[key] = ws
     return ws
 
