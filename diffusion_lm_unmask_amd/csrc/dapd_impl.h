@@ -487,6 +487,7 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
     }
     if (tid < kWords) chosen[tid] = 0ull;
     for (int e = tid; e < kWords * kWords; e += NT) bmk[e / kWords][e % kWords] = 0ull;
+    for (int t = tid; t < M; t += NT) lmask[t] = 0ull;
   }
   const int flags = dlm::block_or_i<NT>(bad_pos | (any_edge << 1), shi);  // ends with a barrier
   if (flags & 1) {
@@ -560,43 +561,69 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
 
   // ---- each node's earlier neighbours inside its block of 64 ranks, as lane
   // bits.  They do not depend on what earlier blocks chose, so every node is
-  // done at once here rather than inside the sequential greedy.
-  for (int v = tid; v < M; v += NT) {
+  // done at once here rather than inside the sequential greedy: one
+  // (node, adjacency word) pair per thread, ORed into the node's mask
+  // (zeroed with the loads).
+  for (int e = tid; e < M * nw; e += NT) {
+    const int v = e / nw, w = e - v * nw;
+    if (!has_edge[v]) continue;
     const int t = rank_of[v], k = t >> 6;
+    uint64_t m = adj[v][w] & bmk[k][w];
     uint64_t loc = 0ull;
-    if (has_edge[v]) {
-      for (int w = 0; w < nw; ++w) {
-        uint64_t m = adj[v][w] & bmk[k][w];
-        while (m) {
-          const int ru = rank_of[w * 64 + __builtin_ctzll(m)];
-          m &= m - 1;
-          if (ru < t) loc |= 1ull << (ru & 63);
-        }
-      }
+    while (m) {
+      const int ru = rank_of[w * 64 + __builtin_ctzll(m)];
+      m &= m - 1;
+      if (ru < t) loc |= 1ull << (ru & 63);
     }
-    lmask[t] = loc;
+    if (loc) atomicOr(reinterpret_cast<unsigned long long*>(&lmask[t]), loc);
   }
   __syncthreads();
 
-  // ---- greedy on wave 0, 64 nodes of the order at a time
+  // ---- greedy on wave 0, 64 nodes of the order at a time.  A block's inputs
+  // (its nodes, their in-block masks, edge flags and adjacency rows) do not
+  // depend on what earlier blocks chose, so block k+1's are read from LDS
+  // while block k decides; only the chosen set is read on the sequential path.
   if (wv == 0) {
-    for (int base = 0; base < M; base += 64) {
+    constexpr int kPW = 4;  // adjacency words held in registers (256 nodes)
+    auto fetch = [&](int base, int& v, uint64_t& local, bool& he, uint64_t* av) {
       const int t = base + ln;
-      int v = -1;
-      uint64_t local = 0ull;  // earlier neighbours in this block (lane bits)
+      v = -1;
+      local = 0ull;
+      he = false;
       if (t < M) {
         const int cand = order[t];
         if (cand >= 0) v = cand;  // NaN keys never chosen
         local = lmask[t];
       }
+      if (v >= 0) {
+        he = has_edge[v] != 0;
+#pragma unroll
+        for (int w = 0; w < kPW; ++w) av[w] = w < nw ? adj[v][w] : 0ull;
+      }
+    };
+    int nv;
+    uint64_t nlocal, nav[kPW];
+    bool nhe;
+    fetch(0, nv, nlocal, nhe, nav);
+    for (int base = 0; base < M; base += 64) {
+      const int v = nv;
+      const uint64_t local = nlocal;  // earlier neighbours in this block (lane bits)
+      const bool he = nhe;
+      uint64_t av[kPW];
+#pragma unroll
+      for (int w = 0; w < kPW; ++w) av[w] = nav[w];
+      if (base + 64 < M) fetch(base + 64, nv, nlocal, nhe, nav);
       uint64_t sel;
-      if (__ballot(v >= 0 && has_edge[v]) == 0ull) {
+      if (__ballot(v >= 0 && he) == 0ull) {
         sel = __ballot(v >= 0);  // no node of this block has an edge: all chosen
       } else {
         // blocked by a node chosen in an earlier block
         bool blocked = false;
-        if (v >= 0)
-          for (int w = 0; w < nw; ++w) blocked |= (adj[v][w] & chosen[w]) != 0ull;
+        if (v >= 0) {
+#pragma unroll
+          for (int w = 0; w < kPW; ++w) blocked |= (av[w] & chosen[w]) != 0ull;
+          for (int w = kPW; w < nw; ++w) blocked |= (adj[v][w] & chosen[w]) != 0ull;
+        }
         const uint64_t cand = __ballot(v >= 0 && !blocked);
         if (__ballot(local != 0ull) == 0ull) {
           sel = cand;  // no conflicts inside the block
