@@ -253,7 +253,8 @@ def llada_workloads(dev, stream, args, res):
     n = spec.rows
     block = block_mask(n, *R["fast_block"], dev)
     curs, prevs = replicas_of(cur, args.replicas), replicas_of(prev, args.replicas)
-    reps = [dict(logits=c, prev=p, seq_offsets=so, row_index=ri) for c, p in zip(curs, prevs)]
+    # the rows are the logits' rows in order: no row-index array (NULL)
+    reps = [dict(logits=c, prev=p, seq_offsets=so, row_index=None) for c, p in zip(curs, prevs)]
     fast = dict(eligible=block, tau=R["tau"])
     depcap = dict(lam=R["lam"], l_min=R["l_min"], l_max=R["l_max"])
     stats_bytes = n * spec.vocab * 2 * 2
@@ -274,7 +275,7 @@ def llada_workloads(dev, stream, args, res):
 
     def stats_call(i):
         c, p = calls[i % len(calls)]
-        st = L.dlm_step_stats(c, p, _lib.BF16, spec.vocab, spec.vocab, ri.data_ptr(), n, *outs,
+        st = L.dlm_step_stats(c, p, _lib.BF16, spec.vocab, spec.vocab, None, n, *outs,
                               None, 0, stream)
         if st:
             _lib.check(st, "dlm_step_stats")
@@ -328,7 +329,7 @@ def dapd_workloads(dev, stream, args, res, cpu):
                      dtype=torch.uint8)
     stats_bytes = n * spec.vocab * 2
     avg_bytes = spec.batch * (spec.n_lh * spec.rows * spec.rows * 2 + spec.rows * spec.rows * 4)
-    base = dict(logits=cur, prev=None, seq_offsets=so, row_index=ri)
+    base = dict(logits=cur, prev=None, seq_offsets=so, row_index=None)
     st = Step("dapd_stats", n, [base], stream, stats_bytes)
     ms0, us0 = time_step(st, args.steps, args.warmup)
     stats_only = result(st, ms0, us0, "k_step_rows (the statistics kernel)")
@@ -372,7 +373,7 @@ def stress_workload(dev, stream, args, res, cpu):
     R = synth.RULES["stress"]
     cur, prev, so, ri = synth.logits("stress", dev)
     n = spec.n_rows
-    step = Step("stress", n, [dict(logits=cur, prev=prev, seq_offsets=so, row_index=ri)], stream,
+    step = Step("stress", n, [dict(logits=cur, prev=prev, seq_offsets=so, row_index=None)], stream,
                 n * spec.vocab * 2 * 2,
                 depcap=dict(lam=R["lam"], l_min=R["l_min"], l_max=R["l_max"]),
                 cap=dict(tau_low=R["tau_low"], tau_high=R["tau_high"], gamma=R["gamma"],
@@ -409,7 +410,7 @@ def dream_workload(dev, stream, args, res):
     R = synth.RULES["dream"]
     cur, _, so, ri = synth.logits("dream", dev)
     n = spec.n_rows
-    step = Step("dream", n, [dict(logits=cur, prev=None, seq_offsets=so, row_index=ri)], stream,
+    step = Step("dream", n, [dict(logits=cur, prev=None, seq_offsets=so, row_index=None)], stream,
                 n * spec.vocab * 2,
                 cap=dict(tau_low=R["tau_low"], tau_high=R["tau_high"], gamma=R["gamma"],
                          k_max=R["k_max"]))
@@ -430,7 +431,7 @@ def tiny_workload(dev, stream, args, res):
     block = block_mask(n, 0, n, dev)
     attn = synth.attention("tiny", dev)
     pos, offs = synth.gen_positions("tiny", dev)
-    step = Step("tiny", n, [dict(logits=cur, prev=prev, seq_offsets=so, row_index=ri)], stream,
+    step = Step("tiny", n, [dict(logits=cur, prev=prev, seq_offsets=so, row_index=None)], stream,
                 cur.numel() * 4 * 2 + 32 * 32 * 4 + 32 * 32 * 4,
                 fast=dict(eligible=block, tau=R["tau"]),
                 depcap=dict(lam=R["lam"], l_min=R["l_min"], l_max=R["l_max"]),
@@ -644,7 +645,7 @@ def per_call(dev: str, iters: int) -> dict:
         schedules("llada", st, so, block, pos, offs)
         timed("depcap_boundary/llada", lambda r: api.depcap_boundary(st["kl"], st["entropy"], so))
         timed("cap_select/llada", lambda r: api.cap_select(
-            curs[r], ri, so, st["conf"], st["argmax"], st["lse"], eligible=block,
+            curs[r], None, so, st["conf"], st["argmax"], st["lse"], eligible=block,
             k_max=R["k_max"]), 4)
         attn = [synth.attention("llada", dev, batch=1) for _ in range(4)]
         ws = torch.empty(api.dapd_workspace_bytes(1, 256), device=dev, dtype=torch.uint8)
@@ -660,7 +661,7 @@ def per_call(dev: str, iters: int) -> dict:
         spec, cur, prev, so, ri, st, _ = stats_of("dream", 1)
         Rd = synth.RULES["dream"]
         timed("cap_select/dream", lambda r: api.cap_select(
-            cur, ri, so, st["conf"], st["argmax"], st["lse"], tau_low=Rd["tau_low"],
+            cur, None, so, st["conf"], st["argmax"], st["lse"], tau_low=Rd["tau_low"],
             k_max=Rd["k_max"]))
         del cur, st
         torch.cuda.empty_cache()
@@ -685,7 +686,7 @@ def per_call(dev: str, iters: int) -> dict:
         schedules("stress", st, so, None, pos, so)
         timed("depcap_boundary/stress", lambda r: api.depcap_boundary(st["kl"], st["entropy"],
                                                                       so))
-        timed("cap_select/stress", lambda r: api.cap_select(cur, ri, so, st["conf"],
+        timed("cap_select/stress", lambda r: api.cap_select(cur, None, so, st["conf"],
                                                             st["argmax"], st["lse"], k_max=128))
         del cur, prev, st
         torch.cuda.empty_cache()

@@ -144,17 +144,16 @@ def step_stats(logits: torch.Tensor, prev: torch.Tensor | None = None,
         _rows2d(prev, "prev")
         if prev.dtype != logits.dtype or prev.stride(0) != ld or prev.shape != logits.shape:
             raise DLMError("prev must match logits in dtype, shape and strides")
-    if row_index is None:
-        row_index = torch.arange(logits.shape[0], device=dev, dtype=torch.int64)
-    _vec(row_index, "row_index", torch.int64, dev)
-    n = row_index.numel()
+    if row_index is not None:
+        _vec(row_index, "row_index", torch.int64, dev)
+    n = logits.shape[0] if row_index is None else row_index.numel()
     f = dict(device=dev, dtype=torch.float32)
     conf, ent, lse = torch.empty(n, **f), torch.empty(n, **f), torch.empty(n, **f)
     kl = torch.empty(n, **f) if prev is not None else None
     arg = torch.empty(n, device=dev, dtype=torch.int32)
     ws = stats_workspace(n, dev) if split else None
     st = _lib.lib().dlm_step_stats(logits.data_ptr(), _ptr(prev), _dtype_code(logits), vocab, ld,
-                                   row_index.data_ptr(), n, conf.data_ptr(), arg.data_ptr(),
+                                   _ptr(row_index), n, conf.data_ptr(), arg.data_ptr(),
                                    ent.data_ptr(), _ptr(kl), lse.data_ptr(), _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream(logits))
     _lib.check(st, "dlm_step_stats")
@@ -204,11 +203,12 @@ def cap_select(logits, row_index, seq_offsets, conf, argmax, lse, eligible=None,
                tau_low=DEFAULTS["cap_tau_low"], tau_high=DEFAULTS["cap_tau_high"],
                gamma=DEFAULTS["cap_gamma"], k_max=64, vocab=None, want_cand=False,
                want_dmat=False):
-    """dlm_cap_select -> dict(commit, n_commit, cand or None, dmat or None)."""
+    """dlm_cap_select -> dict(commit, n_commit, cand or None, dmat or None).
+    row_index None: row r of logits is candidate row r."""
     ld = _rows2d(logits, "logits")
     dev = logits.device
     vocab = _vocab(vocab, logits)
-    _vec(row_index, "row_index", torch.int64, dev)
+    _opt(row_index, "row_index", torch.int64, dev)
     _vec(seq_offsets, "seq_offsets", torch.int32, dev)
     _vec(conf, "conf", torch.float32, dev)
     _vec(argmax, "argmax", torch.int32, dev)
@@ -225,7 +225,7 @@ def cap_select(logits, row_index, seq_offsets, conf, argmax, lse, eligible=None,
     dmat = (torch.empty(max(n_seq, 0), k_max, k_max, device=dev, dtype=torch.float32)
             if want_dmat else None)
     st = _lib.lib().dlm_cap_select(_rows(logits), _dtype_code(logits), vocab, ld,
-                                   _rows(row_index), seq_offsets.data_ptr(), n_seq,
+                                   _ptr(row_index), seq_offsets.data_ptr(), n_seq,
                                    _rows(conf), _rows(argmax), _rows(lse),
                                    _ptr(eligible), float(tau_low), float(tau_high), float(gamma),
                                    k_max, _rows(commit), n_commit.data_ptr(), _ptr(cand),
@@ -428,13 +428,12 @@ def step_descriptor(logits, prev=None, seq_offsets=None, row_index=None, vocab=N
         _rows2d(prev, "prev")
         if prev.dtype != logits.dtype or prev.stride(0) != ld or prev.shape != logits.shape:
             raise DLMError("prev must match logits in dtype, shape and strides")
-    if row_index is None:
-        row_index = torch.arange(logits.shape[0], device=dev, dtype=torch.int64)
-    _vec(row_index, "row_index", torch.int64, dev)
+    if row_index is not None:
+        _vec(row_index, "row_index", torch.int64, dev)
+    n = logits.shape[0] if row_index is None else row_index.numel()
     if seq_offsets is None:
-        seq_offsets = torch.tensor([0, row_index.numel()], device=dev, dtype=torch.int32)
+        seq_offsets = torch.tensor([0, n], device=dev, dtype=torch.int32)
     _vec(seq_offsets, "seq_offsets", torch.int32, dev)
-    n = row_index.numel()
     n_seq = seq_offsets.numel() - 1
     f = dict(device=dev, dtype=torch.float32)
     i32 = dict(device=dev, dtype=torch.int32)
@@ -445,7 +444,7 @@ def step_descriptor(logits, prev=None, seq_offsets=None, row_index=None, vocab=N
     d = _lib.StepDesc()
     d.logits, d.prev_logits = logits.data_ptr(), _ptr(prev)
     d.dtype, d.vocab, d.ld = _dtype_code(logits), vocab, ld
-    d.row_index, d.n_rows = row_index.data_ptr(), n
+    d.row_index, d.n_rows = _ptr(row_index), n
     d.conf, d.argmax = out["conf"].data_ptr(), out["argmax"].data_ptr()
     d.entropy, d.kl, d.lse = out["entropy"].data_ptr(), _ptr(out["kl"]), out["lse"].data_ptr()
     d.seq_offsets, d.n_seq = seq_offsets.data_ptr(), n_seq

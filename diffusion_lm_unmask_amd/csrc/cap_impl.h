@@ -112,7 +112,7 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
     const bool el = eligible ? eligible[lo + r] != 0 : true;
     const int32_t y = argmax[lo + r];
     const float l = lse[lo + r];
-    const int64_t ri = row_index[lo + r];
+    const int64_t ri = row_index ? row_index[lo + r] : static_cast<int64_t>(lo + r);
     if (!el || c != c) continue;
     if (bidx == INT32_MAX || c > best) {
       best = c;

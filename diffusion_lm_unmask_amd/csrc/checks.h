@@ -12,7 +12,7 @@ namespace dlmh {
 inline int check_stats(const void* logits, const void* prev, int dtype, int64_t vocab,
                        int64_t ld, const int64_t* row_index, int64_t n_rows, const void* conf,
                        const void* argmax, const void* entropy, const void* kl, const void* lse) {
-  if (!logits || !row_index || !conf || !argmax || !entropy || !lse) return DLM_ERR_ARG;
+  if (!logits || !conf || !argmax || !entropy || !lse) return DLM_ERR_ARG;
   if ((prev == nullptr) != (kl == nullptr)) return DLM_ERR_ARG;
   if (dtype != DLM_BF16 && dtype != DLM_F32) return DLM_ERR_UNSUPPORTED;
   if (vocab <= 0 || n_rows <= 0 || ld < vocab) return DLM_ERR_ARG;
@@ -46,8 +46,7 @@ inline int check_cap(const void* logits, int dtype, int64_t vocab, int64_t ld,
                      const void* conf, const void* argmax, const void* lse, float tau_low,
                      float tau_high, float gamma, int32_t k_max, const void* commit,
                      const void* n_commit) {
-  if (!logits || !row_index || !seq_offsets || !conf || !argmax || !lse || !commit ||
-      !n_commit)
+  if (!logits || !seq_offsets || !conf || !argmax || !lse || !commit || !n_commit)
     return DLM_ERR_ARG;
   if (n_seq <= 0 || vocab <= 0 || ld < vocab || k_max <= 0) return DLM_ERR_ARG;
   if (tau_low != tau_low || tau_high != tau_high || gamma != gamma) return DLM_ERR_ARG;

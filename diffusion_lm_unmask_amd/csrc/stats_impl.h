@@ -489,7 +489,8 @@ __device__ __forceinline__ void stats_block(const StatsArgs& p, int64_t r, int s
 
   const int S = p.splits;
   const int64_t V = p.V;
-  const int64_t off = p.row_index[r] * p.ld;
+  // no index array: row r itself (no dependent load before the stream starts)
+  const int64_t off = (p.row_index ? p.row_index[r] : r) * p.ld;
   const char* cur = static_cast<const char*>(p.logits) + off * ES;
   const char* prv = PREV ? static_cast<const char*>(p.prev) + off * ES : nullptr;
   const int tid = threadIdx.x;

@@ -113,9 +113,11 @@ extern "C" {
  *   aligned and ld*element_size is a multiple of 16; otherwise a slower
  *   element-wise path is used.
  * vocab: 1 <= vocab < 2^31; ld >= vocab.
- * row_index (device int64 [n_rows]); n_rows >= 1.  Each entry must name a row
- *   of logits (and of prev_logits): 0 <= row_index[r] and the row's vocab
- *   elements inside the caller's allocation, which the library cannot see.
+ * row_index (device int64 [n_rows], or NULL); n_rows >= 1.  Each entry must
+ *   name a row of logits (and of prev_logits): 0 <= row_index[r] and the
+ *   row's vocab elements inside the caller's allocation, which the library
+ *   cannot see.  NULL means row_index[r] = r (the first n_rows rows, in
+ *   order), with no index read.
  * conf, entropy, kl, lse (device f32 [n_rows]); argmax (device int32 [n_rows]).
  * workspace (device, optional): NULL, or at least
  *   dlm_step_stats_workspace_bytes(n_rows) bytes, 16-byte aligned and
@@ -181,8 +183,9 @@ int dlm_depcap_boundary(const float* kl, const float* entropy, const int32_t* se
  * (log p_a(yhat_b) + log p_b(yhat_a)), a conflict is D_ab > gamma (a reading);
  * rows with conf > tau_high are committed first, then the rest in priority
  * order are added when they conflict with nothing chosen.
- * logits (device, dtype, same layout as dlm_step_stats) and row_index: only
- * gathered at (candidate row, candidate argmax).  conf, argmax, lse: the
+ * logits (device, dtype, same layout as dlm_step_stats) and row_index (as
+ * there; NULL is row r itself): only gathered at (candidate row, candidate
+ * argmax).  conf, argmax, lse: the
  * outputs of dlm_step_stats for the same rows.
  * Limits: rows per sequence <= 1024 (else n_commit[b] = -1 and no commit);
  * 1 <= k_max <= 128.  Before any gather, every candidate's argmax is checked
@@ -357,7 +360,7 @@ typedef struct dlm_step_desc {
   const void* prev_logits; /* NULL: no KL */
   int32_t dtype;
   int64_t vocab, ld;
-  const int64_t* row_index;
+  const int64_t* row_index; /* NULL: rows 0..n_rows-1 in order */
   int64_t n_rows;
   float* conf;
   int32_t* argmax;

@@ -252,3 +252,41 @@ def test_fused_without_dapd_statistics_equal_the_call_bitwise(name):
     for k in ("conf", "entropy", "kl", "lse", "argmax"):
         assert torch.equal(f[k].view(torch.int32), g[k].view(torch.int32)), f"{name}: {k}"
     _check(cur, prev, so, ri, fast=fast, depcap=depcap, tag=f"{name} as configured")
+
+
+@pytest.mark.parametrize("name", ["llada", "tiny"])
+def test_null_row_index_is_the_identity(name):
+    # row_index NULL means row r itself: every output equals the call with an
+    # explicit 0..n-1 index bit for bit (fused step, statistics with and
+    # without a workspace, CAP)
+    cur, prev, so, ri = synth.logits(name, DEV)
+    assert torch.equal(ri, torch.arange(cur.shape[0], device=DEV))
+    R = synth.RULES[name]
+    fast, depcap, cap = _llada_parts(cur, R)
+    pos, offs = synth.gen_positions(name, DEV, batch=1)
+    attn = synth.attention(name, DEV, batch=1)
+    dapd = dict(attn=attn, masked_pos=pos, m_max=cur.shape[0], tau=R["dapd_tau"])
+    parts = dict(fast=fast, depcap=depcap, cap=cap, dapd=dapd)
+    a = api.decide_step(cur, prev, so, row_index=ri, **parts)
+    b = api.decide_step(cur, prev, so, row_index=None, **parts)
+    torch.cuda.synchronize()
+    for k in ("conf", "argmax", "entropy", "kl", "lse"):
+        _same(a[k], b[k], f"{name} fused {k}")
+    for part in ("fast", "depcap", "cap", "dapd"):
+        for x, y in zip(a[part], b[part]):
+            _same(x, y, f"{name} fused {part}")
+    for split in (False, True):
+        s1 = api.step_stats(cur, prev, row_index=ri, split=split)
+        s2 = api.step_stats(cur, prev, split=split)
+        for k in ("conf", "argmax", "entropy", "kl", "lse"):
+            _same(s1[k], s2[k], f"{name} stats split={split} {k}")
+    c1 = api.cap_select(cur, ri, so, s1["conf"], s1["argmax"], s1["lse"], eligible=cap["eligible"],
+                        tau_low=0.3, tau_high=0.95, gamma=cap["gamma"], k_max=cap["k_max"],
+                        want_cand=True, want_dmat=True)
+    c2 = api.cap_select(cur, None, so, s1["conf"], s1["argmax"], s1["lse"],
+                        eligible=cap["eligible"], tau_low=0.3, tau_high=0.95, gamma=cap["gamma"],
+                        k_max=cap["k_max"], want_cand=True, want_dmat=True)
+    torch.cuda.synchronize()
+    for k in ("commit", "n_commit", "cand", "dmat"):
+        _same(c1[k], c2[k], f"{name} cap {k}")
+    assert int(host(c1["cand"][0] >= 0).sum()) > 1      # several candidates gathered
