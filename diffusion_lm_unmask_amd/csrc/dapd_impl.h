@@ -54,7 +54,7 @@ namespace {
 #define DLM_DAPD_GROUPS 16
 #endif
 #ifndef DLM_DAPD_UNR_BF16
-#define DLM_DAPD_UNR_BF16 5
+#define DLM_DAPD_UNR_BF16 4
 #endif
 constexpr int kGroups = DLM_DAPD_GROUPS;  // map groups per workgroup
 constexpr int kAvgNT = 512;
@@ -89,10 +89,10 @@ __device__ __forceinline__ float ld1(const void* base, int64_t idx) {
   return static_cast<const float*>(base)[idx];
 }
 
-// UNR_BF16: bf16 maps a lane keeps in flight.  It changes no summation
-// order (each lane adds its maps in map order), only how hard one tile
-// presses on the memory system.
-template <bool BF16, int UNR_BF16 = DLM_DAPD_UNR_BF16>
+// UNR_BF16: bf16 maps per batch; PIPE: two batches in flight (else one).
+// Neither changes the summation order (each lane adds its maps in map order),
+// only how hard one tile presses on the memory system.
+template <bool BF16, int UNR_BF16 = DLM_DAPD_UNR_BF16, bool PIPE = true>
 __device__ __forceinline__ void dapd_avg_tile(int b, int tile, const void* __restrict__ attn,
     int n_lh, int64_t S, int64_t batch_stride, const int32_t* __restrict__ masked_pos,
     const int32_t* __restrict__ seq_offsets, int m_max, int n_tc, int vec_ok,
@@ -130,46 +130,87 @@ __device__ __forceinline__ void dapd_avg_tile(int b, int tile, const void* __res
                        static_cast<int64_t>(b) * batch_stride * (BF16 ? 2 : 4);
     const int64_t map_stride = S * S;
     if (contig) {
-      // UNR maps per lane in flight, then summed in map order
+      // Lane maps g, g + kGroups, ... in batches of UNR.  PIPE: double-
+      // buffered, the loads of batch k+1 issued before batch k is added, so
+      // loads stay in flight while the lane adds; else one batch at a time.
+      // Either way each lane adds its maps in map order.  Loads are
+      // branch-free (an index past the last map reads the last map, and its
+      // add is skipped by a select), which keeps the compiler's waits per
+      // load rather than per loop trip.
       constexpr int UNR = BF16 ? UNR_BF16 : 2;
-      for (int lh0 = g; lh0 < n_lh; lh0 += kGroups * UNR) {
-        uint4 q[UNR][BF16 ? 1 : 2];
+      constexpr int NQ = BF16 ? 1 : 2;  // 16-byte loads per map row piece
+      constexpr int ES = BF16 ? 2 : 4;
+      const char* rowp = base + (prow + pj[0]) * ES;
+      const int64_t mbytes = map_stride * ES;
+      const int last = n_lh - 1;
+      auto load = [&](uint4 (&q)[UNR][NQ], int m0) {
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
-          const int lh = lh0 + kGroups * u;
-          const int64_t e = static_cast<int64_t>(lh) * map_stride + prow + pj[0];
-          if constexpr (BF16) {
-            q[u][0] = lh < n_lh ? *reinterpret_cast<const uint4*>(base + e * 2)
-                                : make_uint4(0u, 0u, 0u, 0u);
-          } else {
-            q[u][0] = lh < n_lh ? *reinterpret_cast<const uint4*>(base + e * 4)
-                                : make_uint4(0u, 0u, 0u, 0u);
-            q[u][1] = lh < n_lh ? *reinterpret_cast<const uint4*>(base + e * 4 + 16)
-                                : make_uint4(0u, 0u, 0u, 0u);
-          }
+          const char* p = rowp + min(g + kGroups * (m0 + u), last) * mbytes;
+#pragma unroll
+          for (int h = 0; h < NQ; ++h) q[u][h] = *reinterpret_cast<const uint4*>(p + 16 * h);
         }
+      };
+      auto add = [&](const uint4 (&q)[UNR][NQ], int m0) {
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
-          if (lh0 + kGroups * u >= n_lh) break;
+          const bool on = g + kGroups * (m0 + u) < n_lh;
+          float v[8];
           if constexpr (BF16) {
-            acc[0] += dlm::bf16_lo(q[u][0].x);
-            acc[1] += dlm::bf16_hi(q[u][0].x);
-            acc[2] += dlm::bf16_lo(q[u][0].y);
-            acc[3] += dlm::bf16_hi(q[u][0].y);
-            acc[4] += dlm::bf16_lo(q[u][0].z);
-            acc[5] += dlm::bf16_hi(q[u][0].z);
-            acc[6] += dlm::bf16_lo(q[u][0].w);
-            acc[7] += dlm::bf16_hi(q[u][0].w);
+            v[0] = dlm::bf16_lo(q[u][0].x);
+            v[1] = dlm::bf16_hi(q[u][0].x);
+            v[2] = dlm::bf16_lo(q[u][0].y);
+            v[3] = dlm::bf16_hi(q[u][0].y);
+            v[4] = dlm::bf16_lo(q[u][0].z);
+            v[5] = dlm::bf16_hi(q[u][0].z);
+            v[6] = dlm::bf16_lo(q[u][0].w);
+            v[7] = dlm::bf16_hi(q[u][0].w);
           } else {
-            acc[0] += __uint_as_float(q[u][0].x);
-            acc[1] += __uint_as_float(q[u][0].y);
-            acc[2] += __uint_as_float(q[u][0].z);
-            acc[3] += __uint_as_float(q[u][0].w);
-            acc[4] += __uint_as_float(q[u][1].x);
-            acc[5] += __uint_as_float(q[u][1].y);
-            acc[6] += __uint_as_float(q[u][1].z);
-            acc[7] += __uint_as_float(q[u][1].w);
+            v[0] = __uint_as_float(q[u][0].x);
+            v[1] = __uint_as_float(q[u][0].y);
+            v[2] = __uint_as_float(q[u][0].z);
+            v[3] = __uint_as_float(q[u][0].w);
+            v[4] = __uint_as_float(q[u][1].x);
+            v[5] = __uint_as_float(q[u][1].y);
+            v[6] = __uint_as_float(q[u][1].z);
+            v[7] = __uint_as_float(q[u][1].w);
           }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[k] = on ? acc[k] + v[k] : acc[k];
+        }
+      };
+      const int nm = (n_lh + kGroups - 1) / kGroups;  // maps of the fullest group
+      const int nb = (nm + UNR - 1) / UNR;
+      uint4 qa[UNR][NQ], qb[UNR][NQ];
+      // the scheduling barriers keep each batch's loads ahead of the adds
+      // that are meant to overlap them
+      if constexpr (PIPE) {
+        load(qa, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        int k = 0;
+        // the last trip is peeled, so every trip of the loop enters with the
+        // same loads outstanding and the waits stay per load
+        for (; k + 2 < nb; k += 2) {
+          load(qb, (k + 1) * UNR);
+          __builtin_amdgcn_sched_barrier(0);
+          add(qa, k * UNR);
+          load(qa, (k + 2) * UNR);
+          __builtin_amdgcn_sched_barrier(0);
+          add(qb, (k + 1) * UNR);
+        }
+        if (k + 1 < nb) {
+          load(qb, (k + 1) * UNR);
+          __builtin_amdgcn_sched_barrier(0);
+          add(qa, k * UNR);
+          add(qb, (k + 1) * UNR);
+        } else {
+          add(qa, k * UNR);
+        }
+      } else {
+        for (int k = 0; k < nb; ++k) {
+          load(qa, k * UNR);
+          __builtin_amdgcn_sched_barrier(0);
+          add(qa, k * UNR);
         }
       }
     } else {

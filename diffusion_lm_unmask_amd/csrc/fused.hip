@@ -45,6 +45,11 @@
 #ifndef DLM_STEP_TILE_UNR
 #define DLM_STEP_TILE_UNR 2
 #endif
+// The tile's maps one batch at a time (0) or double-buffered (1), as the
+// averaging call streams them; the summation order is the same.
+#ifndef DLM_STEP_TILE_PIPE
+#define DLM_STEP_TILE_PIPE 0
+#endif
 
 namespace {
 
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(kStepNT) void k_step_stream(const StreamArgs a) {
   }
   const int64_t t = g - a.n_rows;
   if (threadIdx.x == 0 && t % a.tiles_per_seq == 0) a.tally[t / a.tiles_per_seq] = 0ull;
-  dapd_avg_tile<ABF16, DLM_STEP_TILE_UNR>(
+  dapd_avg_tile<ABF16, DLM_STEP_TILE_UNR, DLM_STEP_TILE_PIPE != 0>(
       static_cast<int>(t / a.tiles_per_seq), static_cast<int>(t % a.tiles_per_seq), a.attn, a.n_lh,
       a.S, a.batch_stride, a.masked_pos, a.seq_offsets, a.m_max, a.n_tc, a.vec_ok, a.ws_a, a.P);
 }
