@@ -113,15 +113,20 @@ class TimingEvents:
                 pair.append(e.value)
             self.pairs.append(tuple(pair))
 
-    def mean_us(self):
-        """Average interval in microseconds (call after the device is synchronized)."""
-        ms, acc = ctypes.c_float(), 0.0
+    def durations_us(self):
+        """Each pair's interval in microseconds (call after the device is synchronized)."""
+        ms, out = ctypes.c_float(), []
         for a, b in self.pairs:
             if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
                                             ctypes.c_void_p(b)):
                 raise RuntimeError("hipEventElapsedTime failed")
-            acc += ms.value
-        return acc / len(self.pairs) * 1000.0
+            out.append(ms.value * 1000.0)
+        return out
+
+    def mean_us(self):
+        """Average interval in microseconds (call after the device is synchronized)."""
+        d = self.durations_us()
+        return sum(d) / len(d)
 
     def close(self):
         for pair in self.pairs:
@@ -185,7 +190,12 @@ def time_step(step: Step, steps: int, warmup: int):
     for i in range(steps):
         step.run(i, ev.pairs[i])
     torch.cuda.synchronize()
-    us = ev.mean_us()
+    d = sorted(ev.durations_us())
+    us = sum(d) / len(d)
+    # the spread of the launches behind the average (reported beside it)
+    step.launch1_spread = {"min_us": round(d[0], 3), "p50_us": round(d[len(d) // 2], 3),
+                           "p90_us": round(d[min(len(d) - 1, (9 * len(d)) // 10)], 3),
+                           "max_us": round(d[-1], 3)}
     ev.close()
     for d in step.descs:
         d.launch1_begin_event = d.launch1_end_event = None
@@ -198,7 +208,8 @@ def result(step: Step, ms, us, kernel, extra=None):
          "launch1": {"kernel": kernel, "avg_us": round(us, 3),
                      "algorithmic_bytes": step.launch1_bytes,
                      "GB/s": round(gbs(step.launch1_bytes, us), 1),
-                     "frac_of_peak": round(gbs(step.launch1_bytes, us) / PEAK_HBM_GBS, 4)}}
+                     "frac_of_peak": round(gbs(step.launch1_bytes, us) / PEAK_HBM_GBS, 4),
+                     **getattr(step, "launch1_spread", {})}}
     if extra:
         r.update(extra)
     return r
