@@ -29,6 +29,7 @@
 #include "cap_impl.h"
 #include "checks.h"
 #include "dapd_impl.h"
+#include "devinfo.h"
 #include "rules_impl.h"
 #include "stats_impl.h"
 
@@ -55,28 +56,6 @@ namespace {
 
 constexpr int kStepNT = 512;
 
-// Compute units of the current device, queried once per device and cached
-// (the step asks before its first launch, so an error returns before anything
-// is enqueued, and repeated steps make no device query).
-int cu_count(int* cus) {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return DLM_ERR_HIP;
-  if (dev >= 0 && dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) {
-      *cus = c;
-      return DLM_OK;
-    }
-  }
-  int c = 0;
-  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      c <= 0)
-    return DLM_ERR_HIP;
-  if (dev >= 0 && dev < 64) cache[dev].store(c, std::memory_order_relaxed);
-  *cus = c;
-  return DLM_OK;
-}
 static_assert(kAvgNT == kStepNT, "an attention tile must use the statistics workgroup size");
 static_assert(kRuleNT == 256 && kCapNT == 256 && kSymNT <= 256, "rules run with 256 threads");
 constexpr int kRulesNT = 256;
@@ -95,12 +74,11 @@ struct StreamArgs {
 };
 
 // Launch 1 without attention tiles: exactly the statistics call's kernel and
-// launch shape (one workgroup per row, stats_threads(n_rows) threads), so
+// launch shape (one workgroup per row, stats_threads threads), so
 // these statistics are bitwise those of dlm_step_stats without a workspace.
 template <int NT, bool BF16, bool PREV>
 __global__ __launch_bounds__(NT) void k_step_rows(const StatsArgs p) {
-  stats_block<NT, BF16, PREV, NT == 256 ? DLM_STATS_U_BF16_256 : DLM_STATS_U_BF16>(p, blockIdx.x,
-                                                                                 0);
+  stats_block<NT, BF16, PREV, stats_unroll<NT>()>(p, blockIdx.x, 0);
 }
 
 template <bool BF16, bool PREV, bool ABF16>
@@ -208,10 +186,18 @@ void launch_rows_k(int64_t n_rows, hipStream_t s, const StatsArgs& a, hipEvent_t
     hipLaunchKernelGGL((k_step_rows<NT, BF16, PREV>), grid, dim3(NT), 0, s, a);
 }
 template <bool BF16, bool PREV>
-void launch_rows(int64_t n_rows, hipStream_t s, const StatsArgs& a, hipEvent_t e0,
+void launch_rows(int64_t n_rows, int cus, hipStream_t s, const StatsArgs& a, hipEvent_t e0,
                  hipEvent_t e1) {
-  if (stats_threads(n_rows) == 256) launch_rows_k<256, BF16, PREV>(n_rows, s, a, e0, e1);
-  else launch_rows_k<512, BF16, PREV>(n_rows, s, a, e0, e1);
+  switch (stats_threads(n_rows, PREV, BF16, cus)) {
+    case 256:
+      launch_rows_k<256, BF16, PREV>(n_rows, s, a, e0, e1);
+      break;
+    case 768:
+      launch_rows_k<768, BF16, PREV>(n_rows, s, a, e0, e1);
+      break;
+    default:
+      launch_rows_k<512, BF16, PREV>(n_rows, s, a, e0, e1);
+  }
 }
 template <bool BF16, bool PREV>
 void launch_stream(bool abf16, dim3 grid, hipStream_t s, const StreamArgs& a, hipEvent_t e0,
@@ -251,7 +237,7 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
     return rc;
 
   int cus = 0;
-  if (dapd && (rc = cu_count(&cus)) != DLM_OK) return rc;
+  if ((rc = dlmh::cu_count(&cus)) != DLM_OK) return rc;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = d->dtype == DLM_BF16, prev = d->prev_logits != nullptr;
@@ -296,11 +282,11 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
   const hipEvent_t e1 = static_cast<hipEvent_t>(d->launch1_end_event);
   if (!dapd) {  // statistics only: the statistics call's own kernel and shape
     if (bf16) {
-      if (prev) launch_rows<true, true>(d->n_rows, s, sa.st, e0, e1);
-      else launch_rows<true, false>(d->n_rows, s, sa.st, e0, e1);
+      if (prev) launch_rows<true, true>(d->n_rows, cus, s, sa.st, e0, e1);
+      else launch_rows<true, false>(d->n_rows, cus, s, sa.st, e0, e1);
     } else {
-      if (prev) launch_rows<false, true>(d->n_rows, s, sa.st, e0, e1);
-      else launch_rows<false, false>(d->n_rows, s, sa.st, e0, e1);
+      if (prev) launch_rows<false, true>(d->n_rows, cus, s, sa.st, e0, e1);
+      else launch_rows<false, false>(d->n_rows, cus, s, sa.st, e0, e1);
     }
   } else if (bf16) {
     if (prev) launch_stream<true, true>(abf16, grid1, s, sa, e0, e1);

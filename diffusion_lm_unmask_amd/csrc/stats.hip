@@ -2,14 +2,15 @@
 // the device code and its design notes are in stats_impl.h) and the host
 // entry points: launch shape, split-row workspace, validation.
 #include "checks.h"
+#include "devinfo.h"
 #include "stats_impl.h"
 
 namespace {
 
 template <int NT, bool BF16, bool PREV>
 __global__ __launch_bounds__(NT) void k_stats(const StatsArgs p) {
-  stats_block<NT, BF16, PREV, NT == 256 ? DLM_STATS_U_BF16_256 : DLM_STATS_U_BF16>(
-      p, blockIdx.x / p.splits, static_cast<int>(blockIdx.x % p.splits));
+  stats_block<NT, BF16, PREV, stats_unroll<NT>()>(p, blockIdx.x / p.splits,
+                                                  static_cast<int>(blockIdx.x % p.splits));
 }
 
 template <int NT, bool BF16>
@@ -27,6 +28,8 @@ hipError_t launch_dt(int nt, const StatsArgs& a, int64_t n_rows, hipStream_t s) 
   switch (nt) {
     case 256:
       return launch_nt<256, BF16>(a, n_rows, s);
+    case 768:
+      return launch_nt<768, BF16>(a, n_rows, s);
     default:
       return launch_nt<512, BF16>(a, n_rows, s);
   }
@@ -56,10 +59,12 @@ int64_t workspace_rows(size_t bytes) {
 // workgroup per CU.  Splitting more rows than that costs more than it gains:
 // each split's agent-scope release/acquire writes back / invalidates its
 // XCD's L2 while the other workgroups stream through it.
-void launch_shape(int64_t n_rows, int64_t n_chunks, bool can_split, int* nt, int* splits) {
-  *nt = stats_threads(n_rows);
+void launch_shape(int64_t n_rows, int64_t n_chunks, bool can_split, bool prev, bool bf16, int cus,
+                  int* nt, int* splits) {
+  *nt = stats_threads(n_rows, prev, bf16, cus);
   int sp = 1;
   if (can_split && n_rows <= 64) {
+    *nt = 512;  // split rows: the cap below assumes 512-thread splits
     sp = static_cast<int>((256 + n_rows - 1) / n_rows);
     if (sp > kMaxSplits) sp = kMaxSplits;
     // each split should keep every lane busy for at least two segments
@@ -92,8 +97,12 @@ extern "C" int dlm_step_stats(const void* logits, const void* prev_logits, int d
     if (workspace_bytes < dlm_step_stats_workspace_bytes(n_rows)) return DLM_ERR_ARG;
   }
   const int aligned = (a % 16 == 0) && (b % 16 == 0) && ((ld * es) % 16 == 0);
+  int cus = 0;
+  const int rc2 = dlmh::cu_count(&cus);
+  if (rc2 != DLM_OK) return rc2;
   int nt, splits;
-  launch_shape(n_rows, vocab / (16 / es), workspace != nullptr && aligned, &nt, &splits);
+  launch_shape(n_rows, vocab / (16 / es), workspace != nullptr && aligned,
+               prev_logits != nullptr, dtype == DLM_BF16, cus, &nt, &splits);
   StatsArgs args{logits, prev_logits, vocab, ld, row_index, conf, entropy, kl, lse, argmax,
                  aligned, splits, static_cast<int*>(workspace),
                  workspace ? reinterpret_cast<Partial*>(

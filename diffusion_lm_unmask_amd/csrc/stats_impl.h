@@ -56,15 +56,30 @@ __device__ __forceinline__ float ex2(float t) { return __builtin_amdgcn_exp2f(t)
 #ifndef DLM_STATS_NT_LOADS
 #define DLM_STATS_NT_LOADS 1
 #endif
-// Rows from which a row takes a 256-thread workgroup instead of 512 (many
-// rows: more workgroups per compute unit; 1024 threads on 256 rows measured
-// 27.2 against 25.8 us).  The statistics call and the fused step's
-// statistics-only launch share this rule, so their results are bitwise equal.
+// Chunks per lane per segment for 768-thread workgroups.
+#ifndef DLM_STATS_U_BF16_768
+#define DLM_STATS_U_BF16_768 1
+#endif
+// Threads of a row's workgroup.  Many rows (from DLM_STATS_NT256_ROWS): 256,
+// more workgroups per compute unit.  bf16 rows with a previous row, at most
+// one per compute unit: 768 (12 waves, three per SIMD), whose extra waves
+// overlap the fold's arithmetic (two exponentials per element pair) with the
+// loads better when each compute unit streams a single row; same-process A/B,
+// 256 x 126464 with prev: 21.9 against 22.5 us at 512 threads; without prev,
+// or with two or more rows per compute unit, 512 stays ahead (256 rows
+// without prev: 15.2 against 17.1 us).  Otherwise 512.  The statistics call
+// and the fused step's statistics-only launch share this rule, so their
+// results are bitwise equal.
 #ifndef DLM_STATS_NT256_ROWS
 #define DLM_STATS_NT256_ROWS 4096
 #endif
-__host__ __device__ constexpr int stats_threads(int64_t n_rows) {
-  return n_rows >= DLM_STATS_NT256_ROWS ? 256 : 512;
+__host__ __device__ constexpr int stats_threads(int64_t n_rows, bool prev, bool bf16, int cus) {
+  return n_rows >= DLM_STATS_NT256_ROWS ? 256 : (prev && bf16 && n_rows <= cus) ? 768 : 512;
+}
+// bf16 chunks per lane per segment for a workgroup of NT threads.
+template <int NT>
+constexpr int stats_unroll() {
+  return NT == 256 ? DLM_STATS_U_BF16_256 : NT == 768 ? DLM_STATS_U_BF16_768 : DLM_STATS_U_BF16;
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

@@ -265,3 +265,21 @@ def test_closed_forms_256_thread_rows():
     out = api.step_stats(cur, cur)
     torch.cuda.synchronize()
     _check_closed_forms(out, kind, want, "4096 x 1000 bf16")
+
+
+@pytest.mark.parametrize("extra", [0, 1])
+def test_thread_counts_at_the_compute_unit_count(extra):
+    # bf16 rows with a previous row, at most one per compute unit, take the
+    # 768-thread workgroups; one row more takes 512.  Both against the oracle
+    # on a ragged vocabulary (a partial last segment and a tail element), and
+    # the fused step's launch 1 bitwise equal to the call in both shapes
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    spec = synth.Spec("cus", 11, 1, cus + extra, 20011, torch.bfloat16, 2.0, 0.6, 12.0, 0.5)
+    cur, prev, so, ri = synth.logits(spec, DEV)
+    out, _ = _compare(cur, prev, tag=f"{cus + extra} rows ")
+    fused = api.decide_step(cur, prev)
+    solo = api.step_stats(cur, prev, split=False)
+    torch.cuda.synchronize()
+    for k in ("conf", "argmax", "entropy", "kl", "lse"):
+        assert torch.equal(fused[k].view(torch.int32), solo[k].view(torch.int32)), k
+        assert torch.equal(out[k].view(torch.int32), solo[k].view(torch.int32)), k
