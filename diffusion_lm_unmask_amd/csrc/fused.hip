@@ -78,7 +78,7 @@ struct StreamArgs {
 // these statistics are bitwise those of dlm_step_stats without a workspace.
 template <int NT, bool BF16, bool PREV>
 __global__ __launch_bounds__(NT) void k_step_rows(const StatsArgs p) {
-  stats_block<NT, BF16, PREV, stats_unroll<NT>()>(p, blockIdx.x, 0);
+  stats_block<NT, BF16, PREV, stats_unroll<NT>(), stats_ping<NT, BF16>()>(p, blockIdx.x, 0);
 }
 
 template <bool BF16, bool PREV, bool ABF16>

@@ -9,8 +9,8 @@ namespace {
 
 template <int NT, bool BF16, bool PREV>
 __global__ __launch_bounds__(NT) void k_stats(const StatsArgs p) {
-  stats_block<NT, BF16, PREV, stats_unroll<NT>()>(p, blockIdx.x / p.splits,
-                                                  static_cast<int>(blockIdx.x % p.splits));
+  stats_block<NT, BF16, PREV, stats_unroll<NT>(), stats_ping<NT, BF16>()>(
+      p, blockIdx.x / p.splits, static_cast<int>(blockIdx.x % p.splits));
 }
 
 template <int NT, bool BF16>

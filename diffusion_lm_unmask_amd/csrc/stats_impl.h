@@ -81,6 +81,12 @@ template <int NT>
 constexpr int stats_unroll() {
   return NT == 256 ? DLM_STATS_U_BF16_256 : NT == 768 ? DLM_STATS_U_BF16_768 : DLM_STATS_U_BF16;
 }
+// Whether a workgroup of NT threads keeps two segments in flight (the
+// statistics block's PING form): bf16 rows outside the 768-thread shape.
+template <int NT, bool BF16>
+constexpr bool stats_ping() {
+  return BF16 && NT != 768;
+}
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load16(const uint4* p) {
@@ -142,15 +148,16 @@ struct LaneState {
   uint4 bq;         // raw bits of that chunk (VEC > 1)
 };
 
-// Fold NSUB sub-blocks of W values into the lane state.  qc/qp hold the raw
-// chunks (W values each; qc is unused for W == 1); x is the unpacked current
-// row; `valid` masks whole sub-blocks; start[u] is the element index of
-// sub-block u (argmax record).
+// Fold NSUB sub-blocks of W values into the lane state, in two parts.
+// fold_head: the sub-blocks' maxima, the first-strict-increase chunk record
+// (qc holds the raw chunks, unused for W == 1) and the exact power-of-two
+// rescale of the running sums to the new integer reference.  fold_tail: the
+// sums; the previous row's values come from yf (unpacked), else ys (one
+// value per sub-block), else the raw chunks qp.  `valid` masks whole
+// sub-blocks; start[u] is the element index of sub-block u.
 template <int NSUB, int W, bool BF16, bool PREV>
-__device__ __forceinline__ void fold(LaneState& c, const float (*x)[W], const uint4* qc,
-                                     const uint4* qp, const float* ys, const bool* valid,
-                                     const int* start) {
-  // segment maxima and the first-strict-increase chunk record
+__device__ __forceinline__ void fold_head(LaneState& c, const float (*x)[W], const uint4* qc,
+                                          const bool* valid, const int* start) {
   float mr = c.m;
 #pragma unroll
   for (int u = 0; u < NSUB; ++u) {
@@ -166,19 +173,23 @@ __device__ __forceinline__ void fold(LaneState& c, const float (*x)[W], const ui
       mr = fmaxf(mr, cm);
     }
   }
-  {  // rescale running sums to the new integer reference (exact: a power of two)
-    const float hn = ceilf(mr * kL2E);
-    const float dh = c.h - hn;  // integer <= 0 (or a huge negative from the sentinel)
-    const int di = static_cast<int>(fmaxf(dh, -256.f));
-    c.A = ldexpf(fmaf(dh, c.Z, c.A), di);
-    c.Z = ldexpf(c.Z, di);
-    if constexpr (PREV) {
-      c.B = ldexpf(c.B, di);
-      c.Z2 = ldexpf(c.Z2, di);
-    }
-    c.h = hn;
-    c.m = mr;
+  // rescale running sums to the new integer reference (exact: a power of two)
+  const float hn = ceilf(mr * kL2E);
+  const float dh = c.h - hn;  // integer <= 0 (or a huge negative from the sentinel)
+  const int di = static_cast<int>(fmaxf(dh, -256.f));
+  c.A = ldexpf(fmaf(dh, c.Z, c.A), di);
+  c.Z = ldexpf(c.Z, di);
+  if constexpr (PREV) {
+    c.B = ldexpf(c.B, di);
+    c.Z2 = ldexpf(c.Z2, di);
   }
+  c.h = hn;
+  c.m = mr;
+}
+template <int NSUB, int W, bool BF16, bool PREV>
+__device__ __forceinline__ void fold_tail(LaneState& c, const float (*x)[W],
+                                          const float (*yf)[W], const uint4* qp,
+                                          const float* ys, const bool* valid) {
   float z = 0.f, a = 0.f, b = 0.f, z2 = 0.f;
 #pragma unroll
   for (int u = 0; u < NSUB; ++u) {
@@ -190,7 +201,7 @@ __device__ __forceinline__ void fold(LaneState& c, const float (*x)[W], const ui
       z += e;
       a = fmaf(e, t, a);
       if constexpr (PREV) {
-        const float y = ys ? ys[u * W + k] : elem_of<BF16>(qp[u], k);
+        const float y = yf ? yf[u][k] : ys ? ys[u * W + k] : elem_of<BF16>(qp[u], k);
         b = fmaf(e, x[u][k] - y, b);
         z2 += ex2(fmaf(y, kL2E, -c.h));
       }
@@ -202,6 +213,13 @@ __device__ __forceinline__ void fold(LaneState& c, const float (*x)[W], const ui
     c.B += b;
     c.Z2 += z2;
   }
+}
+template <int NSUB, int W, bool BF16, bool PREV>
+__device__ __forceinline__ void fold(LaneState& c, const float (*x)[W], const uint4* qc,
+                                     const uint4* qp, const float* ys, const bool* valid,
+                                     const int* start) {
+  fold_head<NSUB, W, BF16, PREV>(c, x, qc, valid, start);
+  fold_tail<NSUB, W, BF16, PREV>(c, x, nullptr, qp, ys, valid);
 }
 
 // Sum four doubles over the workgroup in a fixed order.  Only thread 0
@@ -495,7 +513,7 @@ __device__ __forceinline__ T ld_agent(T* a) {
 // UB: 16-byte chunks per lane per segment for bf16 rows (fp32 rows use 4).
 // More chunks keep more bytes in flight per workgroup at the cost of
 // registers; the value changes the summation order, not the definitions.
-template <int NT, bool BF16, bool PREV, int UB = DLM_STATS_U_BF16>
+template <int NT, bool BF16, bool PREV, int UB = DLM_STATS_U_BF16, bool PING = false>
 __device__ __forceinline__ void stats_block(const StatsArgs& p, int64_t r, int s) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int VEC = 16 / ES;          // elements per 16-byte chunk
@@ -533,13 +551,81 @@ __device__ __forceinline__ void stats_block(const StatsArgs& p, int64_t r, int s
   // software-pipelined full segments: the loads of segment it+1 are issued
   // before segment it is folded
   uint4 qc[U], qp[U];
-  if (n_full > 0) {
+  if (!PING && n_full > 0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       qc[u] = load16(cur4 + c_lo + u * NT + tid);
       if constexpr (PREV) qp[u] = load16(prv4 + c_lo + u * NT + tid);
     }
   }
+  if constexpr (PING) {
+    // two segments in flight: segment it+1 is issued into the other
+    // register set before segment it is folded, and the last trip is peeled,
+    // so every trip of the loop enters with one set outstanding.  The empty
+    // asm statements fix where values exist: the unpacked rows right after
+    // unpacking (the compiler would otherwise rederive them from the raw
+    // chunk after the next loads were issued into it, and then copy the
+    // loaded registers at the loop's end behind a full wait), and the
+    // running sums before the next issue (else the folds sink below the
+    // waits).  Same-process A/B, bitwise-equal outputs: 2048 x 126464
+    // without prev 78.1 against 80.5 us, 4096 x 151936 184.2 against 185.9,
+    // 65536 x 126464 with prev 4786 against 4817, 1024 with prev 81.4
+    // against 82.5.  The 768-thread rows keep the single buffer: 22.5
+    // against 21.8 us, their arithmetic sets their pace.
+    uint4 ca[U], pa[U], cb[U], pb[U];
+    auto issue = [&](uint4 (&qc2)[U], uint4 (&qp2)[U], int64_t it) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t ch = c_lo + it * SEG + u * NT + tid;
+        qc2[u] = load16(cur4 + ch);
+        if constexpr (PREV) qp2[u] = load16(prv4 + ch);
+      }
+    };
+    auto consume = [&](const uint4 (&qc2)[U], const uint4 (&qp2)[U], int64_t it) {
+      float x[U][VEC], y[U][VEC];
+      int st[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        unpack<BF16>(qc2[u], x[u]);
+        if constexpr (PREV) unpack<BF16>(qp2[u], y[u]);
+        st[u] = static_cast<int>((c_lo + it * SEG + u * NT + tid) * VEC);
+        // the unpacked values exist from here on: the compiler may not
+        // rederive them from the raw chunk later, so the chunk's registers
+        // are free for the next loads once the head has read them
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+          asm volatile("" : "+v"(x[u][k]));
+          if constexpr (PREV) asm volatile("" : "+v"(y[u][k]));
+        }
+      }
+      fold_head<U, VEC, BF16, PREV>(c, x, qc2, allv, st);
+      fold_tail<U, VEC, BF16, PREV>(c, x, PREV ? y : nullptr, nullptr, nullptr, allv);
+      // the sums are complete here, before the next loads are issued
+      asm volatile("" : "+v"(c.Z), "+v"(c.A));
+      if constexpr (PREV) asm volatile("" : "+v"(c.B), "+v"(c.Z2));
+    };
+    int64_t it = 0;
+    if (n_full > 0) issue(ca, pa, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    for (; it + 2 < n_full; it += 2) {
+      issue(cb, pb, it + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(ca, pa, it);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ca, pa, it + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(cb, pb, it + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (it + 1 < n_full) {
+      issue(cb, pb, it + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(ca, pa, it);
+      consume(cb, pb, it + 1);
+    } else if (it < n_full) {
+      consume(ca, pa, it);
+    }
+  } else
   for (int64_t it = 0; it < n_full; ++it) {
     float x[U][VEC];
     uint4 xq[U], yq[U];
