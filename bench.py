@@ -227,14 +227,29 @@ def block_mask(n, lo, hi, dev):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it (model name, family / model /
+    stepping, clock and cache of the first processor entry) and the logical
+    CPUs this process may run on and the machine has."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    if info:
+                        break
+                    continue
+                k, _, v = line.partition(":")
+                info.setdefault(k.strip(), v.strip())
     except OSError:
         pass
-    return "unknown"
+    name = info.get("model name", "unknown")
+    extra = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    if "cpu MHz" in info:
+        extra.append(f"{float(info['cpu MHz']):.0f} MHz")
+    if "cache size" in info:
+        extra.append(f"cache {info['cache size']}")
+    extra.append(f"{len(os.sched_getaffinity(0))} of {os.cpu_count()} logical CPUs usable")
+    return f"{name} ({', '.join(extra)})"
 
 
 def _timed_reps(fn, seconds, min_reps=1):

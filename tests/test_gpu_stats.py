@@ -17,8 +17,8 @@ pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("poisoned_outputs")]
 DEV = "cuda"
 
 
-def _compare(cur, prev, row_index=None, vocab=None, tag=""):
-    out = api.step_stats(cur, prev, row_index=row_index, vocab=vocab)
+def _compare(cur, prev, row_index=None, vocab=None, tag="", split=True):
+    out = api.step_stats(cur, prev, row_index=row_index, vocab=vocab, split=split)
     torch.cuda.synchronize()
     ri = None if row_index is None else host(row_index).numpy()
     ref = oracle.step_stats(host(cur), host(prev) if prev is not None else None, row_index=ri,
@@ -80,6 +80,8 @@ def test_non_finite_rows():
         c = cur.to(dt)
         p = prev.to(dt)
         _compare(c, p, tag=f"non-finite {dt} ")
+        # one workgroup per row: bf16 with prev takes the 768-thread rows
+        _compare(c, p, tag=f"non-finite {dt} unsplit ", split=False)
 
 
 def test_argmax_ties_lowest_index():
