@@ -53,12 +53,14 @@ def test_padded_ld_and_row_gather():
     prev[:, 3000:] = -50.0
     idx = torch.tensor([5, 63, 0, 5, 17, 40], device=DEV, dtype=torch.int64)
     _compare(cur, prev, row_index=idx, vocab=3000, tag="ld-pad ")
+    _compare(cur, prev, row_index=idx, vocab=3000, tag="ld-pad unsplit ", split=False)
     # leading dimension that breaks 16-byte row alignment -> element-wise path
     big = torch.zeros(64, 3003, device=DEV, dtype=torch.bfloat16)
     big2 = torch.zeros_like(big)
     big[:, :3000] = cur[:, :3000]
     big2[:, :3000] = prev[:, :3000]
     _compare(big, big2, row_index=idx, vocab=3000, tag="ld-unaligned ")
+    _compare(big, big2, row_index=idx, vocab=3000, tag="ld-unaligned unsplit ", split=False)
 
 
 def test_non_finite_rows():
