@@ -32,6 +32,35 @@ __device__ __forceinline__ float gather(const void* logits, int64_t idx) {
   return static_cast<const float*>(logits)[idx];
 }
 
+// G[a][b] = logit_a[yhat_b] - lse_a for a, b < K, kGU loads in flight per
+// lane.  The loads carry no branch: an index past the end gathers the lane's
+// own first pair again (tid < K*K inside the loop; unused, and a different
+// address in every lane).  Guarded loads each ended in a wait for every load.
+template <int kGU, bool BF16>
+__device__ __forceinline__ void cap_gathers(const void* __restrict__ logits,
+                                            const int64_t* coff, const int32_t* cy,
+                                            const float* clse, float (*G)[kKM + 1], int K,
+                                            int tid) {
+  const int KK = K * K;
+  for (int base = tid; base < KK; base += kGU * kCapNT) {
+    float v[kGU];
+#pragma unroll
+    for (int u = 0; u < kGU; ++u) {
+      const int p = base + u * kCapNT < KK ? base + u * kCapNT : tid;
+      const int a = p / K, e = p - a * K;
+      v[u] = gather<BF16>(logits, coff[a] + cy[e]);
+    }
+#pragma unroll
+    for (int u = 0; u < kGU; ++u) {
+      const int p = base + u * kCapNT;
+      if (p < KK) {
+        const int a = p / K, e = p - a * K;
+        G[a][e] = v[u] - clse[a];
+      }
+    }
+  }
+}
+
 // The workgroup's LDS.  The caller declares it (__shared__), so that a kernel
 // running other roles in other workgroups can overlay their LDS on it.
 struct CapSmem {
@@ -173,29 +202,13 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
     return;
   }
 
-  // 3. gathers G[a][b] = log p_a(yhat_b), eight in flight per lane
-  constexpr int kGU = 8;
-  const int KK = K * K;
-  for (int base = tid; base < KK; base += kGU * kCapNT) {
-    float v[kGU];
-#pragma unroll
-    for (int u = 0; u < kGU; ++u) {
-      const int p = base + u * kCapNT;
-      v[u] = 0.f;
-      if (p < KK) {
-        const int a = p / K, e = p - a * K;
-        v[u] = gather<BF16>(logits, coff[a] + cy[e]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kGU; ++u) {
-      const int p = base + u * kCapNT;
-      if (p < KK) {
-        const int a = p / K, e = p - a * K;
-        G[a][e] = v[u] - clse[a];
-      }
-    }
-  }
+  // 3. gathers G[a][b] = log p_a(yhat_b): eight in flight per lane, or four
+  // when the K*K gathers fit in four per lane (an eight-wide batch would then
+  // be half filler loads)
+  if (K * K <= 4 * kCapNT)
+    cap_gathers<4, BF16>(logits, coff, cy, clse, G, K, tid);
+  else
+    cap_gathers<8, BF16>(logits, coff, cy, clse, G, K, tid);
   __syncthreads();
 
   // conflict words.  Up to 32 candidates: wave w builds the words of
