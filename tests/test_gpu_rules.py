@@ -279,12 +279,13 @@ def test_cap_pool_sizes_around_the_ordering_paths(k_max):
     # one 1024-row sequence; tau_low set at the P-th largest confidence gives a
     # pool of exactly P rows: up to 64 (one wave sorts), 65-256 (per-wave runs
     # and rank searches), above 256 (the LDS sort); k_max 64 takes the greedy
-    # in rounds, 128 the candidate-order scan
+    # in rounds, 128 the candidate-order scan; 32 and 33 candidates sit on
+    # either side of the switch from four to eight gathers per lane and batch
     cur, prev, so, ri, g, o = _stats("stress", batch=1)
     R = dict(synth.RULES["stress"], k_max=k_max)
     conf = np.sort(f64(g["conf"]))[::-1]
     done = 0
-    for P in (1, 63, 64, 65, 128, 129, 255, 256, 257, 700):
+    for P in (1, 32, 33, 63, 64, 65, 128, 129, 255, 256, 257, 700):
         if not conf[P - 1] > conf[P]:
             continue                                   # a tie at the cut: pool size not exact
         tl = float(conf[P - 1])
