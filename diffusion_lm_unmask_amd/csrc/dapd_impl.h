@@ -420,6 +420,88 @@ struct SelSmem {
   int last;                      // the fused step: this workgroup counted in last
 };
 
+// A sequence of at most 64 masked positions outside the late stage, on one
+// wave: node r on lane r, then rank t on lane t.  The keys sort in registers,
+// each rank fetches its node's adjacency word from that node's lane, and the
+// earlier neighbours of rank t become rank bits in one pass over the ranks.
+// The greedy then runs in rounds as in the workgroup path (a candidate decides
+// once its earlier neighbours have, and is taken unless one of them was), so
+// the chosen set is the one the order defines.  No LDS and no barrier.
+__device__ __forceinline__ void dapd_select_wave(int b, int lo, int M, int m_max,
+    const char* __restrict__ ws, Layout L, const float* __restrict__ conf,
+    uint8_t* __restrict__ commit, int32_t* __restrict__ n_commit, float* __restrict__ degree,
+    float* __restrict__ sym, float* __restrict__ key_out, Policy P) {
+  const int ln = threadIdx.x % DLM_WAVE;
+  const bool in = ln < M;
+  const int r = in ? ln : 0;  // lanes past the sequence read its first entry (unused)
+  const int64_t row = static_cast<int64_t>(b) * m_max;
+  uint64_t kk = reinterpret_cast<const uint64_t*>(ws + L.keys)[row + r];
+  uint32_t he = reinterpret_cast<const uint8_t*>(ws + L.has_edge)[row + r];
+  uint64_t adj = reinterpret_cast<const uint64_t*>(ws + L.adj)[(row + r) * L.words];
+  const float cf = (P.pre_unmask && in) ? conf[lo + ln] : 0.f;  // an empty last sequence has lo = rows
+  if (!in) {
+    kk = ~0ull;  // padding keys sort after every node
+    he = 0u;
+    adj = 0ull;
+  }
+  if (__ballot(in && (he & 2u))) {  // a position out of range: report
+    if (in) {
+      commit[lo + ln] = 0;
+      if (degree) degree[lo + ln] = NAN;
+      if (key_out) key_out[lo + ln] = NAN;
+    }
+    if (sym)
+      for (int64_t e = ln; e < static_cast<int64_t>(m_max) * m_max; e += DLM_WAVE)
+        sym[static_cast<int64_t>(b) * m_max * m_max + e] = NAN;
+    if (ln == 0) {
+      n_commit[b] = -1;
+      if (P.stage) P.stage[b] = 0;
+    }
+    return;
+  }
+  if (ln == 0 && P.stage) P.stage[b] = 0;
+  uint64_t take;  // chosen nodes, as node bits
+  if (__ballot(in && (he & 1u)) == 0ull) {
+    take = __ballot(in && (kk >> 32) != 0xffffffffull);  // no edge: every node with a key
+  } else {
+    const uint64_t sk = dlm::wave_sort_asc(kk, DLM_WAVE);  // lane t: the key of rank t
+    const bool valid = ln < M;
+    const bool nan = (sk >> 32) == 0xffffffffull;  // NaN key: never chosen
+    const int v = valid ? static_cast<int>(sk & 0xffffffffu) : 0;
+    // rank t's adjacency word (node bits), from lane v
+    const uint32_t alo = static_cast<uint32_t>(
+        __builtin_amdgcn_ds_bpermute(v << 2, static_cast<int>(adj)));
+    const uint32_t ahi = static_cast<uint32_t>(
+        __builtin_amdgcn_ds_bpermute(v << 2, static_cast<int>(adj >> 32)));
+    const uint64_t at = valid ? (static_cast<uint64_t>(ahi) << 32) | alo : 0ull;
+    // earlier neighbours of rank t, as rank bits
+    uint64_t E = 0ull;
+    for (int t = 0; t < M; ++t) {
+      const int vt = dlm::rdlane(v, t);
+      if (t < ln && ((at >> vt) & 1ull)) E |= 1ull << t;
+    }
+    const uint64_t cand = __ballot(valid && !nan);
+    uint64_t sel = 0ull, open = cand;
+    while (open) {
+      const bool ready = ((open >> ln) & 1ull) && (E & open) == 0ull;
+      sel |= __ballot(ready && (E & sel) == 0ull);
+      open &= ~__ballot(ready);
+    }
+    // rank bits to node bits
+    take = (valid && ((sel >> ln) & 1ull)) ? (1ull << v) : 0ull;
+    take |= dlm::xor_lane64<1>(take);
+    take |= dlm::xor_lane64<2>(take);
+    take |= dlm::xor_lane64<4>(take);
+    take |= dlm::xor_lane64<8>(take);
+    take |= dlm::xor_lane64<16>(take);
+    take |= dlm::xor_lane64<32>(take);
+  }
+  const bool c = in && (((take >> ln) & 1ull) || (P.pre_unmask && cf == 1.0f));
+  if (in) commit[lo + ln] = static_cast<uint8_t>(c);
+  const uint64_t cb = __ballot(c);
+  if (ln == 0) n_commit[b] = __popcll(cb);
+}
+
 // Per sequence: load the graph into LDS, order the nodes, run the greedy
 // (NT threads).  The result does not depend on NT.
 template <int NT>
@@ -463,6 +545,11 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
     return;
   }
   const bool late = late_stage(P, b, M);  // uniform over the workgroup
+  if (M <= DLM_WAVE && !late) {  // uniform: one wave decides, the others leave
+    if (wv == 0)
+      dapd_select_wave(b, lo, M, m_max, ws, L, conf, commit, n_commit, degree, sym, key_out, P);
+    return;
+  }
   // a masked position outside [0, S) reports the sequence.  In the graph
   // stage the scores kernel has checked every row (bit 1 of has_edge), so
   // the graph's loads below are the only trip to memory before the check.
