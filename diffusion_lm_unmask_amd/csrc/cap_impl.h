@@ -12,9 +12,9 @@
 //   3. G[a][b] = logit_a[yhat_b] - lse_a gathered from HBM into LDS
 //      (k_max^2 two-byte gathers), D_ab = G[a][b] + G[b][a] (bit-symmetric),
 //      conflict bits (D_ab > gamma) as two 64-bit words per candidate;
-//   4. the greedy in candidate order on one wave (readlane of each
-//      candidate's conflict words): tau_high members unconditionally, the
-//      rest when their conflict words do not meet the chosen set.
+//   4. the greedy in candidate order, in rounds on one wave (lane l holds
+//      candidates l and l + 64): tau_high members unconditionally, the rest
+//      when no earlier candidate they conflict with is chosen.
 #include <math.h>
 
 #pragma once
@@ -255,12 +255,12 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
   __syncthreads();
 
   // 4. greedy on wave 0, in rounds: lane l holds candidates l and l + 64
-  // (their conflict words and forced flags, conf > tau_high).  A candidate
-  // decides once every earlier candidate it conflicts with has decided (a
-  // forced one at once), and is taken when forced or when none of those was
-  // taken.  The lowest undecided candidate is always ready, and each
-  // decision is the candidate-order scan's.  s0 / s1: chosen candidates
-  // 0..63 / 64..127 as bitsets.
+  // (their conflict words and forced flags, conf > tau_high).  A forced
+  // candidate is taken at once; any other is out as soon as an earlier
+  // candidate it conflicts with is taken, and taken once all of those have
+  // decided and none was taken.  The lowest undecided candidate always
+  // decides, and each decision is the candidate-order scan's.  s0 / s1:
+  // chosen candidates 0..63 / 64..127 as bitsets.
   if (tid < DLM_WAVE) {
     uint64_t w00 = 0, w10 = 0, w11 = 0;
     bool f0 = false, f1 = false;
@@ -280,20 +280,22 @@ __device__ __forceinline__ void cap_seq(int b, const void* __restrict__ logits, 
     uint64_t open1 = K <= DLM_WAVE ? 0ull : (K >= 2 * DLM_WAVE ? ~0ull : (1ull << (K - DLM_WAVE)) - 1ull);
     uint64_t s0 = 0, s1 = 0;
     while (K <= DLM_WAVE && open0) {  // one word: half the ballots per round
-      const bool r0 = ((open0 >> tid) & 1ull) && (f0 || (e0 & open0) == 0ull);
-      s0 |= __ballot(r0 && (f0 || (e0 & s0) == 0ull));
-      open0 &= ~__ballot(r0);
+      const bool m0 = (open0 >> tid) & 1ull;
+      const bool x0 = m0 && !f0 && (e0 & s0) != 0ull;
+      const bool t0 = m0 && !x0 && (f0 || (e0 & open0) == 0ull);
+      s0 |= __ballot(t0);
+      open0 &= ~__ballot(t0 || x0);
     }
     while (open0 | open1) {
-      const bool r0 = ((open0 >> tid) & 1ull) && (f0 || (e0 & open0) == 0ull);
-      const bool r1 = ((open1 >> tid) & 1ull) &&
-                      (f1 || ((w10 & open0) == 0ull && (e1 & open1) == 0ull));
-      const bool t0 = r0 && (f0 || (e0 & s0) == 0ull);
-      const bool t1 = r1 && (f1 || ((w10 & s0) == 0ull && (e1 & s1) == 0ull));
+      const bool m0 = (open0 >> tid) & 1ull, m1 = (open1 >> tid) & 1ull;
+      const bool x0 = m0 && !f0 && (e0 & s0) != 0ull;
+      const bool x1 = m1 && !f1 && ((w10 & s0) | (e1 & s1)) != 0ull;
+      const bool t0 = m0 && !x0 && (f0 || (e0 & open0) == 0ull);
+      const bool t1 = m1 && !x1 && (f1 || ((w10 & open0) | (e1 & open1)) == 0ull);
       s0 |= __ballot(t0);
       s1 |= __ballot(t1);
-      open0 &= ~__ballot(r0);
-      open1 &= ~__ballot(r1);
+      open0 &= ~__ballot(t0 || x0);
+      open1 &= ~__ballot(t1 || x1);
     }
     if ((s0 >> tid) & 1ull) {
       const int lr = crow[tid] - lo;

@@ -420,13 +420,34 @@ struct SelSmem {
   int last;                      // the fused step: this workgroup counted in last
 };
 
+// Exclusive OR scan over the wave: lane l gets the OR of lanes 0 .. l-1.
+// An xor butterfly: at distance d, a lane in the upper half of its aligned
+// 2d-lane segment takes the lower half's total, and both halves' totals
+// merge.
+template <int D>
+__device__ __forceinline__ void or_scan_step(uint64_t& seg, uint64_t& below, int l) {
+  const uint64_t o = dlm::xor_lane64<D>(seg);
+  if (l & D) below |= o;
+  seg |= o;
+}
+__device__ __forceinline__ uint64_t wave_or_scan_excl(uint64_t v, int l) {
+  uint64_t below = 0ull;
+  or_scan_step<1>(v, below, l);
+  or_scan_step<2>(v, below, l);
+  or_scan_step<4>(v, below, l);
+  or_scan_step<8>(v, below, l);
+  or_scan_step<16>(v, below, l);
+  or_scan_step<32>(v, below, l);
+  return below;
+}
+
 // A sequence of at most 64 masked positions outside the late stage, on one
-// wave: node r on lane r, then rank t on lane t.  The keys sort in registers,
-// each rank fetches its node's adjacency word from that node's lane, and the
-// earlier neighbours of rank t become rank bits in one pass over the ranks.
-// The greedy then runs in rounds as in the workgroup path (a candidate decides
-// once its earlier neighbours have, and is taken unless one of them was), so
-// the chosen set is the one the order defines.  No LDS and no barrier.
+// wave, node r on lane r.  The keys sort in registers (rank t on lane t); an
+// OR scan over the ranks gives each rank the nodes ordered before it, which
+// goes back to that rank's node lane, where it masks the node's adjacency
+// word into its earlier neighbours.  The greedy then runs in rounds on node
+// bits, so the chosen set is the one the order defines.  No LDS and no
+// barrier.
 __device__ __forceinline__ void dapd_select_wave(int b, int lo, int M, int m_max,
     const char* __restrict__ ws, Layout L, const float* __restrict__ conf,
     uint8_t* __restrict__ commit, int32_t* __restrict__ n_commit, float* __restrict__ degree,
@@ -464,37 +485,36 @@ __device__ __forceinline__ void dapd_select_wave(int b, int lo, int M, int m_max
   if (__ballot(in && (he & 1u)) == 0ull) {
     take = __ballot(in && (kk >> 32) != 0xffffffffull);  // no edge: every node with a key
   } else {
-    const uint64_t sk = dlm::wave_sort_asc(kk, DLM_WAVE);  // lane t: the key of rank t
+    // lane t: the key of rank t (a power-of-two run of at least M lanes; the
+    // padding keys above it sort among themselves)
+    const int n = M <= 16 ? 16 : M <= 32 ? 32 : DLM_WAVE;
+    const uint64_t sk = dlm::wave_sort_asc(kk, n);
     const bool valid = ln < M;
-    const bool nan = (sk >> 32) == 0xffffffffull;  // NaN key: never chosen
-    const int v = valid ? static_cast<int>(sk & 0xffffffffu) : 0;
-    // rank t's adjacency word (node bits), from lane v
-    const uint32_t alo = static_cast<uint32_t>(
-        __builtin_amdgcn_ds_bpermute(v << 2, static_cast<int>(adj)));
-    const uint32_t ahi = static_cast<uint32_t>(
-        __builtin_amdgcn_ds_bpermute(v << 2, static_cast<int>(adj >> 32)));
-    const uint64_t at = valid ? (static_cast<uint64_t>(ahi) << 32) | alo : 0ull;
-    // earlier neighbours of rank t, as rank bits
-    uint64_t E = 0ull;
-    for (int t = 0; t < M; ++t) {
-      const int vt = dlm::rdlane(v, t);
-      if (t < ln && ((at >> vt) & 1ull)) E |= 1ull << t;
-    }
-    const uint64_t cand = __ballot(valid && !nan);
-    uint64_t sel = 0ull, open = cand;
+    const int v = static_cast<int>(sk & 0xffffffffu);
+    // the nodes of the ranks below t
+    const uint64_t below = wave_or_scan_excl(valid ? 1ull << v : 0ull, ln);
+    // back to node lanes: rank t sends its set to lane v (the padding ranks,
+    // t >= M, to themselves, so every lane receives exactly one)
+    const int dst = (valid ? v : ln) << 2;
+    const uint32_t blo = static_cast<uint32_t>(
+        __builtin_amdgcn_ds_permute(dst, static_cast<int>(below)));
+    const uint32_t bhi = static_cast<uint32_t>(
+        __builtin_amdgcn_ds_permute(dst, static_cast<int>(below >> 32)));
+    // node ln's earlier neighbours, as node bits
+    const uint64_t E = in ? adj & ((static_cast<uint64_t>(bhi) << 32) | blo) : 0ull;
+    // rounds: a node with a chosen earlier neighbour is out at once; one whose
+    // earlier neighbours have all decided, none chosen, is chosen.  The
+    // lowest undecided node always decides, and every decision is the one
+    // the node-by-node scan in key order makes.  A NaN key is never chosen.
+    uint64_t sel = 0ull, open = __ballot(in && (kk >> 32) != 0xffffffffull);
     while (open) {
-      const bool ready = ((open >> ln) & 1ull) && (E & open) == 0ull;
-      sel |= __ballot(ready && (E & sel) == 0ull);
-      open &= ~__ballot(ready);
+      const bool mine = (open >> ln) & 1ull;
+      const bool out = mine && (E & sel) != 0ull;
+      const bool pick = mine && !out && (E & open) == 0ull;
+      sel |= __ballot(pick);
+      open &= ~__ballot(pick || out);
     }
-    // rank bits to node bits
-    take = (valid && ((sel >> ln) & 1ull)) ? (1ull << v) : 0ull;
-    take |= dlm::xor_lane64<1>(take);
-    take |= dlm::xor_lane64<2>(take);
-    take |= dlm::xor_lane64<4>(take);
-    take |= dlm::xor_lane64<8>(take);
-    take |= dlm::xor_lane64<16>(take);
-    take |= dlm::xor_lane64<32>(take);
+    take = sel;
   }
   const bool c = in && (((take >> ln) & 1ull) || (P.pre_unmask && cf == 1.0f));
   if (in) commit[lo + ln] = static_cast<uint8_t>(c);
@@ -756,16 +776,19 @@ __device__ __forceinline__ void dapd_select_seq(int b, const int32_t* __restrict
         if (__ballot(local != 0ull) == 0ull) {
           sel = cand;  // no conflicts inside the block
         } else {
-          // in rounds: a candidate whose earlier in-block neighbours are all
-          // decided decides now (taken unless one of them was taken).  The
-          // lowest undecided candidate is always ready, and each decision is
-          // the one the node-by-node scan makes.
+          // in rounds: a candidate with a chosen earlier in-block neighbour
+          // is out at once; one whose earlier in-block neighbours have all
+          // decided, none chosen, is chosen.  The lowest undecided candidate
+          // always decides, and each decision is the one the node-by-node
+          // scan makes.
           sel = 0ull;
           uint64_t open = cand;
           while (open) {
-            const bool ready = ((open >> ln) & 1ull) && (local & open) == 0ull;
-            sel |= __ballot(ready && (local & sel) == 0ull);
-            open &= ~__ballot(ready);
+            const bool mine = (open >> ln) & 1ull;
+            const bool out = mine && (local & sel) != 0ull;
+            const bool pick = mine && !out && (local & open) == 0ull;
+            sel |= __ballot(pick);
+            open &= ~__ballot(pick || out);
           }
         }
       }
