@@ -11,9 +11,10 @@
 //                512-byte row segments of two maps; its 512 lanes are 16 map
 //                groups x 32 items (the statistics kernel's workgroup size, so
 //                the fused step can run both in one launch), and a single
-//                sequence already fills every CU.  A lane keeps 5 maps in
-//                flight (more only queues up behind the memory system).  Map
-//                groups are summed in LDS in a fixed order.
+//                sequence already fills every CU.  A lane streams its maps
+//                in double-buffered batches of DLM_DAPD_UNR_BF16 (more in
+//                flight only queue up behind the memory system).  Map groups
+//                are summed in LDS in a fixed order.
 //  k_dapd_sym    grid-wide: s = (a + aT)/2 for 4 rows per workgroup (one
 //                wave), one 16-lane team per row, lane l taking the 16
 //                consecutive columns 16l .. 16l+15 of each 256 (four 16-byte
@@ -24,7 +25,8 @@
 //                degree and the ordering key.
 //  k_dapd_select one workgroup (1024 threads) per sequence (the fused step
 //                runs it at 256 threads, in the sequence's last scores
-//                workgroup; see dapd_scores_select):
+//                workgroup; see dapd_scores_select; up to 64 rows, one wave
+//                decides, see dapd_select_wave and dapd_small_select):
 //                1. the adjacency bitset and keys into LDS;
 //                2. order by the 64-bit keys (key desc, position asc): each
 //                   wave sorts a run of 64 in registers, and a key's rank is
@@ -448,17 +450,15 @@ __device__ __forceinline__ uint64_t wave_or_scan_excl(uint64_t v, int l) {
 // word into its earlier neighbours.  The greedy then runs in rounds on node
 // bits, so the chosen set is the one the order defines.  No LDS and no
 // barrier.
-__device__ __forceinline__ void dapd_select_wave(int b, int lo, int M, int m_max,
-    const char* __restrict__ ws, Layout L, const float* __restrict__ conf,
-    uint8_t* __restrict__ commit, int32_t* __restrict__ n_commit, float* __restrict__ degree,
-    float* __restrict__ sym, float* __restrict__ key_out, Policy P) {
+// The decision itself, given node ln's key, edge flags (bit 0: an edge, bit
+// 1: position out of range) and adjacency word on lane ln (lanes >= M:
+// anything).
+__device__ __forceinline__ void dapd_decide_wave(int b, int lo, int M, int m_max, uint64_t kk,
+    uint32_t he, uint64_t adj, const float* __restrict__ conf, uint8_t* __restrict__ commit,
+    int32_t* __restrict__ n_commit, float* __restrict__ degree, float* __restrict__ sym,
+    float* __restrict__ key_out, Policy P) {
   const int ln = threadIdx.x % DLM_WAVE;
   const bool in = ln < M;
-  const int r = in ? ln : 0;  // lanes past the sequence read its first entry (unused)
-  const int64_t row = static_cast<int64_t>(b) * m_max;
-  uint64_t kk = reinterpret_cast<const uint64_t*>(ws + L.keys)[row + r];
-  uint32_t he = reinterpret_cast<const uint8_t*>(ws + L.has_edge)[row + r];
-  uint64_t adj = reinterpret_cast<const uint64_t*>(ws + L.adj)[(row + r) * L.words];
   const float cf = (P.pre_unmask && in) ? conf[lo + ln] : 0.f;  // an empty last sequence has lo = rows
   if (!in) {
     kk = ~0ull;  // padding keys sort after every node
@@ -520,6 +520,18 @@ __device__ __forceinline__ void dapd_select_wave(int b, int lo, int M, int m_max
   if (in) commit[lo + ln] = static_cast<uint8_t>(c);
   const uint64_t cb = __ballot(c);
   if (ln == 0) n_commit[b] = __popcll(cb);
+}
+__device__ __forceinline__ void dapd_select_wave(int b, int lo, int M, int m_max,
+    const char* __restrict__ ws, Layout L, const float* __restrict__ conf,
+    uint8_t* __restrict__ commit, int32_t* __restrict__ n_commit, float* __restrict__ degree,
+    float* __restrict__ sym, float* __restrict__ key_out, Policy P) {
+  const int ln = threadIdx.x % DLM_WAVE;
+  const int r = ln < M ? ln : 0;  // lanes past the sequence read its first entry (unused)
+  const int64_t row = static_cast<int64_t>(b) * m_max;
+  const uint64_t kk = reinterpret_cast<const uint64_t*>(ws + L.keys)[row + r];
+  const uint32_t he = reinterpret_cast<const uint8_t*>(ws + L.has_edge)[row + r];
+  const uint64_t adj = reinterpret_cast<const uint64_t*>(ws + L.adj)[(row + r) * L.words];
+  dapd_decide_wave(b, lo, M, m_max, kk, he, adj, conf, commit, n_commit, degree, sym, key_out, P);
 }
 
 // Per sequence: load the graph into LDS, order the nodes, run the greedy
@@ -879,6 +891,82 @@ __device__ __forceinline__ void dapd_scores_select(int b, int wg, int waves, int
   }
   dapd_select_seq<NT>(b, masked_pos, S, seq_offsets, m_max, ws, L, conf, commit, n_commit,
                       nullptr, nullptr, nullptr, P, sm);
+}
+
+// The fused step's DAPD part for sequences of at most 64 rows (m_max <= 64):
+// one 256-thread workgroup scores every row of sequence b and decides it, so
+// the graph passes through LDS, with no workspace round trip and no tally.
+// Rows take 4-lane teams (16 rows per wave); lane tl of a team takes
+// columns 16tl .. 16tl+15 with the loads, masks and fixed-order fp64 sum of
+// dapd_sym_rows.  There the other twelve lanes of a 16-lane team hold
+// columns >= 64 >= M and add exactly +0.0, so the degrees, keys and
+// adjacency words are bitwise the same, and so is the decision
+// (dapd_decide_wave, as in the selection call).  Over-long sequences and the
+// late stage go to dapd_select_seq, which reads no graph for them.
+template <int NT>
+__device__ __forceinline__ void dapd_small_select(int b, const int32_t* __restrict__ seq_offsets,
+    const int32_t* __restrict__ masked_pos, int64_t S, int m_max, const float* __restrict__ conf,
+    float tau, const char* __restrict__ ws, Layout L, uint8_t* __restrict__ commit,
+    int32_t* __restrict__ n_commit, Policy P, SelSmem<NT>& sm) {
+  constexpr int kSmallTeam = 4, kRowsPerWave = DLM_WAVE / kSmallTeam;
+  static_assert(NT / DLM_WAVE * kRowsPerWave == DLM_WAVE, "one row per team, 64 rows");
+  const int lo = seq_offsets[b], M = seq_offsets[b + 1] - lo;
+  if (M > m_max || M < 0 || late_stage(P, b, M)) {  // uniform over the workgroup
+    dapd_select_seq<NT>(b, masked_pos, S, seq_offsets, m_max, ws, L, conf, commit, n_commit,
+                        nullptr, nullptr, nullptr, P, sm);
+    return;
+  }
+  const int wv = threadIdx.x / DLM_WAVE, ln = threadIdx.x % DLM_WAVE;
+  const int tl = ln % kSmallTeam, i = wv * kRowsPerWave + ln / kSmallTeam;
+  if (i < M) {  // whole teams
+    const int pos_i = masked_pos[lo + i];
+    const float conf_i = conf[lo + i];
+    const float* A =
+        reinterpret_cast<const float*>(ws + L.a) + static_cast<int64_t>(b) * m_max * L.ld;
+    const int j0 = 16 * tl;
+    float va[16], vt[16];
+    const float4* rp = reinterpret_cast<const float4*>(A + static_cast<int64_t>(i) * L.ld +
+                                                       min(j0, L.ld - 16));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = rp[q];
+      va[4 * q] = f.x;
+      va[4 * q + 1] = f.y;
+      va[4 * q + 2] = f.z;
+      va[4 * q + 3] = f.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) vt[e] = A[static_cast<int64_t>(min(j0 + e, M - 1)) * L.ld + i];
+    const int lim = M - j0, di = i - j0;
+    uint32_t valid = lim >= 16 ? 0xffffu : (lim <= 0 ? 0u : (1u << lim) - 1u);
+    if (di >= 0 && di < 16) valid &= ~(1u << di);
+    double dsum = 0.0;
+    uint32_t gt = 0u;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float sv = 0.5f * (va[e] + vt[e]);
+      gt |= static_cast<uint32_t>(sv > tau) << e;
+      dsum += static_cast<double>(((valid >> e) & 1u) ? sv : 0.0f);
+    }
+    const uint32_t mine = gt & valid;
+    reinterpret_cast<uint16_t*>(&sm.adj[i][0])[tl] = static_cast<uint16_t>(mine);
+    dsum += dlm::xor_val<2>(dsum);
+    dsum += dlm::xor_val<1>(dsum);
+    uint32_t anyb = mine != 0u ? 1u : 0u;
+    anyb |= dlm::xor_val<2>(anyb);
+    anyb |= dlm::xor_val<1>(anyb);
+    if (tl == 0) {
+      const float kk = static_cast<float>(dsum) * conf_i;
+      const uint64_t hi = (kk != kk) ? 0xffffffffull : static_cast<uint64_t>(dlm::desc_bits(kk));
+      sm.keys[i] = (hi << 32) | static_cast<uint32_t>(i);
+      sm.has_edge[i] = static_cast<uint8_t>(anyb | (static_cast<uint32_t>(pos_i < 0 || pos_i >= S) << 1));
+    }
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  const int r = ln < M ? ln : 0;
+  dapd_decide_wave(b, lo, M, m_max, sm.keys[r], sm.has_edge[r], sm.adj[r][0], conf, commit,
+                   n_commit, nullptr, nullptr, nullptr, P);
 }
 
 }  // namespace

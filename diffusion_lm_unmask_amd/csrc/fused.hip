@@ -17,6 +17,8 @@
 //            four waves per workgroup), side by side.  The workgroup that
 //            finishes a sequence's last block of scores (an atomic tally per
 //            sequence) runs that sequence's greedy (dapd_scores_select).
+//            With at most 64 rows per sequence, one workgroup per sequence
+//            scores every row and decides (dapd_small_select).
 //
 // No workgroup waits for another: the statistics reach the rules through
 // the launch boundary, and the scores reach the greedy through the tally's
@@ -124,6 +126,7 @@ struct RulesArgs {
   const int32_t* masked_pos;
   int64_t S;
   int m_max, blocks, waves, wg_per_seq;  // row blocks per sequence, blocks per workgroup
+  int small;                             // m_max <= 64: one workgroup per sequence
   float tau;
   const char* ws;
   Layout L;
@@ -161,9 +164,13 @@ __global__ __launch_bounds__(kRulesNT) void k_step_rules(const RulesArgs a) {
     return;
   }
   g -= a.nc;
-  dapd_scores_select<kRulesNT>(g / a.wg_per_seq, g % a.wg_per_seq, a.waves, a.blocks,
-                               a.seq_offsets, a.masked_pos, a.S, a.m_max, a.conf, a.tau, a.ws,
-                               a.L, a.p_commit, a.p_n, a.P, sm.sel);
+  if (a.small)
+    dapd_small_select<kRulesNT>(g, a.seq_offsets, a.masked_pos, a.S, a.m_max, a.conf, a.tau, a.ws,
+                                a.L, a.p_commit, a.p_n, a.P, sm.sel);
+  else
+    dapd_scores_select<kRulesNT>(g / a.wg_per_seq, g % a.wg_per_seq, a.waves, a.blocks,
+                                 a.seq_offsets, a.masked_pos, a.S, a.m_max, a.conf, a.tau, a.ws,
+                                 a.L, a.p_commit, a.p_n, a.P, sm.sel);
 }
 
 // With events, the launch itself sets them to the kernel's start and end
@@ -308,7 +315,10 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
   ra.nf = fast ? d->n_seq : 0;
   ra.nd = dep ? d->n_seq : 0;
   ra.nc = cap ? d->n_seq : 0;
-  if (dapd) {
+  if (dapd && d->m_max <= DLM_WAVE) {
+    ra.small = 1;  // one workgroup per sequence: scores and decision
+    ra.ns = d->n_seq;
+  } else if (dapd) {
     // one block of kSymRows rows per wave; with more blocks than free compute
     // units (every launch-2 workgroup takes a whole compute unit's LDS), a
     // workgroup scores up to four blocks, so that the scores finish in one

@@ -237,6 +237,28 @@ def test_fused_dapd_bad_position_and_empty_sequence():
         assert int(host(f["dapd"][0][:40]).sum()) == 0
 
 
+def test_fused_dapd_short_sequences_at_the_one_workgroup_limit():
+    # with m_max <= 64 one launch-2 workgroup scores and decides each
+    # sequence: lengths 64 (the limit), 1, 0, 17 and 65 (longer than m_max:
+    # reported, n_commit -1), edge-rich and edgeless, bitwise the selection
+    # call's outputs
+    lens = [64, 1, 0, 17, 65]
+    spec = synth.Spec("short", 29, len(lens), 65, 900, torch.bfloat16, 2.0, 0.6, 12.0, None,
+                      n_lh=4, seq_len=80, attn_sigma=2.0)
+    cur, _, _, _ = synth.logits(spec, DEV)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), device=DEV, dtype=torch.int32)
+    masked = torch.cat([torch.arange(80 - n, 80) for n in lens]).to(DEV, torch.int32)
+    ri = torch.cat([torch.arange(b * 65, b * 65 + n) for b, n in enumerate(lens)]).to(DEV)
+    attn = synth.attention(spec, DEV)
+    for tau in (0.005, 0.02, 0.5):
+        dapd = dict(attn=attn, masked_pos=masked, m_max=64, tau=tau)
+        f = _check(cur, None, offs, ri, fast=dict(eligible=None, tau=0.9), dapd=dapd,
+                   tag=f"short sequences, m_max 64, tau {tau}")
+        n = host(f["dapd"][1]).tolist()
+        assert n[0] > 0 and n[1] == 1 and n[2] == 0 and n[3] > 0 and n[4] == -1, n
+        assert int(host(f["dapd"][0][82:]).sum()) == 0
+
+
 @pytest.mark.parametrize("name", ["llada", "tiny"])
 def test_fused_without_dapd_statistics_equal_the_call_bitwise(name):
     # without DAPD, launch 1 is the statistics call's own kernel and launch
