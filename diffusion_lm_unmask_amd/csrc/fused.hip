@@ -99,6 +99,7 @@ __global__ __launch_bounds__(kStepNT) void k_step_stream(const StreamArgs a) {
 
 struct RulesArgs {
   const int32_t* seq_offsets;
+  RowGuess guess;  // equal-length sequences: each one's rows read with its offsets
   const float *conf, *ent, *kl, *lse;
   const int32_t* argmax;
   int nf, nd, nc, ns;  // workgroups of each part (0 = off)
@@ -147,13 +148,13 @@ __global__ __launch_bounds__(kRulesNT) void k_step_rules(const RulesArgs a) {
   __shared__ RulesSmem sm;
   int g = blockIdx.x;
   if (g < a.nf) {
-    fastdllm_seq(g, a.conf, a.f_el, a.seq_offsets, a.f_tau, a.f_commit, a.f_n);
+    fastdllm_seq<true>(g, a.conf, a.f_el, a.seq_offsets, a.f_tau, a.f_commit, a.f_n, a.guess);
     return;
   }
   g -= a.nf;
   if (g < a.nd) {
-    depcap_seq(g, a.kl, a.ent, a.seq_offsets, a.d_has_prev, a.d_lambda, a.d_lmin, a.d_lmax,
-               a.d_radius, a.d_eps, a.d_block_len, a.d_score, sm.dep);
+    depcap_seq<true>(g, a.kl, a.ent, a.seq_offsets, a.d_has_prev, a.d_lambda, a.d_lmin, a.d_lmax,
+               a.d_radius, a.d_eps, a.d_block_len, a.d_score, sm.dep, a.guess);
     return;
   }
   g -= a.nd;
@@ -307,6 +308,9 @@ extern "C" int dlm_decide_step(const dlm_step_desc* d, void* stream) {
   // ---- launch 2: the per-sequence rules, the DAPD scores and greedy
   RulesArgs ra{};
   ra.seq_offsets = d->seq_offsets;
+  ra.guess = RowGuess{0, d->n_rows};  // n_rows >= 1 (checked)
+  if (d->n_seq > 0 && d->n_rows % d->n_seq == 0 && d->n_rows / d->n_seq <= 2147483647LL)
+    ra.guess.len = static_cast<int>(d->n_rows / d->n_seq);
   ra.conf = d->conf;
   ra.ent = d->entropy;
   ra.kl = d->kl;

@@ -14,31 +14,78 @@ namespace {
 
 constexpr int kRuleNT = 256;
 
+// The fused step knows the statistics' row count (n_rows >= 1).  When every
+// sequence has the same number of rows (len), sequence b's rows are guessed
+// as b * len .. before its offsets arrive, and read in the same trip to
+// memory as the offsets; a guess that the offsets contradict is read again.
+// With GUESS the first rows are read whatever the guess (from row 0 when
+// len = 0), so that the loads carry no branch: a branch made the compiler
+// wait for them before the offsets' load.  Rows at or above n_rows are never
+// read.  The entry points do without (GUESS false).
+struct RowGuess {
+  int len;
+  int64_t n_rows;
+};
+
 // Fast-dLLM: commit conf > tau inside the eligible set; if nothing passes,
 // commit the top-1 eligible row (lowest row on ties; NaN never commits).
 // One wave does it (the other waves of the workgroup return at once): the
 // eligible set is an active block of a few rows, and a wave's DPP reductions
 // need no workgroup barrier (the 256-thread version spent six barriers).
+// Rows go in batches of four per lane, each lane in row order.
+template <bool GUESS = false>
 __device__ __forceinline__ void fastdllm_seq(int b, const float* __restrict__ conf,
                                              const uint8_t* __restrict__ eligible,
                                              const int32_t* __restrict__ seq_offsets,
                                              float tau, uint8_t* __restrict__ commit,
-                                             int32_t* __restrict__ n_commit) {
+                                             int32_t* __restrict__ n_commit,
+                                             RowGuess gs = {0, 1}) {
   if (threadIdx.x >= DLM_WAVE) return;
+  constexpr int U = 4;
   const int lane = threadIdx.x;
-  const int lo = seq_offsets[b], hi = seq_offsets[b + 1];
+  float c[U];
+  uint8_t e[U];  // compared where used, so that no load waits for its value early
+  // without an eligible set, bytes of conf (rows < n_rows, unused): the
+  // loads carry no branch
+  const uint8_t* ep = eligible ? eligible : reinterpret_cast<const uint8_t*>(conf);
+  // rows base + lane + 64u, clamped below lim (lim > base); branch-free
+  auto load = [&](int64_t base, int64_t lim) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t r = min(base + lane + u * DLM_WAVE, lim - 1);
+      c[u] = conf[r];
+      e[u] = ep[r];
+    }
+  };
+  const int64_t g0 = static_cast<int64_t>(b) * gs.len;
+  const bool guess = GUESS && gs.len > 0 && g0 < gs.n_rows;
+  if constexpr (GUESS) load(guess ? g0 : 0, gs.n_rows);
+  const int lo = seq_offsets[b], hi = seq_offsets[b + 1];  // in flight with the guess
+  // both arrive here: keeps the compiler from moving the guessed loads into
+  // the loop, behind the wait for the offsets
+  if constexpr (GUESS)
+    asm volatile("" ::"v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]), "v"(uint32_t{e[0]}),
+                 "v"(uint32_t{e[1]}), "v"(uint32_t{e[2]}), "v"(uint32_t{e[3]}), "v"(lo), "v"(hi));
   int cnt = 0;
   float best = -INFINITY;
   int bidx = INT32_MAX;
-  for (int r = lo + lane; r < hi; r += DLM_WAVE) {
-    const float c = conf[r];
-    const bool el = eligible ? eligible[r] != 0 : true;
-    const bool take = el && c > tau;
-    commit[r] = take;
-    cnt += take;
-    if (el && c == c && (bidx == INT32_MAX || c > best)) {
-      best = c;
-      bidx = r;
+  bool held = guess && lo == g0 && hi <= gs.n_rows;  // the first batch is already here
+  for (int base = lo; base < hi; base += U * DLM_WAVE) {
+    if (!held) load(base, hi);
+    held = false;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = base + lane + u * DLM_WAVE;
+      if (r < hi) {
+        const bool el = !eligible || e[u] != 0;
+        const bool take = el && c[u] > tau;
+        commit[r] = take;
+        cnt += take;
+        if (el && c[u] == c[u] && (bidx == INT32_MAX || c[u] > best)) {
+          best = c[u];
+          bidx = r;
+        }
+      }
     }
   }
   const int total = dlm::wave_reduce(cnt, dlm::OpAdd{});
@@ -68,21 +115,23 @@ struct DepSmem {
 // above the writes) replace a workgroup barrier.  The sums are DPP
 // reductions: the 256-thread version spent seven barriers on a 128-row window.
 constexpr int kDepWaveRows = 4 * DLM_WAVE;
+constexpr int kDepKPT = kDepWaveRows / DLM_WAVE;
 __device__ __forceinline__ void depcap_window_wave(int lo, int W, int R,
                                                    const float* __restrict__ kl,
                                                    const float* __restrict__ ent, double lambda,
                                                    int l_min, double eps,
                                                    int32_t* __restrict__ block_len,
-                                                   double* __restrict__ score, DepSmem& sm) {
+                                                   double* __restrict__ score, DepSmem& sm,
+                                                   const float* gI, const float* gH, bool held) {
   if (threadIdx.x >= DLM_WAVE) return;
   const int lane = threadIdx.x;
-  constexpr int KPT = kDepWaveRows / DLM_WAVE;
+  constexpr int KPT = kDepKPT;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int k = lane + j * DLM_WAVE;
     if (k < W) {
-      sm.sI[k] = static_cast<double>(kl[lo + k]);
-      sm.sH[k] = static_cast<double>(ent[lo + k]);
+      sm.sI[k] = static_cast<double>(held ? gI[j] : kl[lo + k]);
+      sm.sH[k] = static_cast<double>(held ? gH[j] : ent[lo + k]);
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -129,20 +178,42 @@ __device__ __forceinline__ void depcap_window_wave(int lo, int W, int R,
 // DepGA-Block boundary.  Window W = min(l_max, rows); box smoothing of
 // radius R clipped to the window, division by the window mean (+eps),
 // S_k = I~_k - lambda*H~_k in fp64, stored in fp64; k* = first S_k < 0.
+template <bool GUESS = false>
 __device__ __forceinline__ void depcap_seq(int b, const float* __restrict__ kl,
                                            const float* __restrict__ ent,
                                            const int32_t* __restrict__ seq_offsets,
                                            const uint8_t* __restrict__ has_prev,
                                            double lambda, int l_min, int l_max, int R,
                                            double eps, int32_t* __restrict__ block_len,
-                                           double* __restrict__ score, DepSmem& sm) {
+                                           double* __restrict__ score, DepSmem& sm,
+                                           RowGuess gs = {0, 1}) {
   auto& sI = sm.sI;
   auto& sH = sm.sH;
   auto& shd = sm.shd;
   auto& shi = sm.shi;
-  const int lo = seq_offsets[b], n = seq_offsets[b + 1] - lo;
+  // the guessed window (when it fits the one-wave path), read with the
+  // offsets by every wave, so that the loads carry no branch
+  const int64_t g0 = static_cast<int64_t>(b) * gs.len;
+  const int gw = max(0, min(l_max, gs.len));
+  const bool guess =
+      GUESS && gs.len > 0 && gw > 0 && gw <= kDepWaveRows && g0 + gw <= gs.n_rows;
+  float gI[kDepKPT], gH[kDepKPT];
+  if constexpr (GUESS) {
+    const int64_t base = guess ? g0 : 0;
+    const int lim = guess ? gw : 1;
+#pragma unroll
+    for (int j = 0; j < kDepKPT; ++j) {
+      const int64_t r = base + min(static_cast<int>(threadIdx.x % DLM_WAVE) + j * DLM_WAVE, lim - 1);
+      gI[j] = kl[r];
+      gH[j] = ent[r];
+    }
+  }
+  const uint8_t* hpp = has_prev ? has_prev + b : reinterpret_cast<const uint8_t*>(seq_offsets);
+  const uint8_t hraw = *hpp;  // has_prev in the same trip (no branch: without has_prev, a
+                              // byte of the offsets, unused)
+  const int lo = seq_offsets[b], n = seq_offsets[b + 1] - lo;  // in flight with the guess
   const int W = max(0, min(l_max, n));
-  const bool warm = has_prev ? has_prev[b] != 0 : true;
+  const bool warm = has_prev ? hraw != 0 : true;
   R = min(R, W);  // a wider box covers the whole window anyway (and k + R stays in range)
   if (score)
     for (int k = W + threadIdx.x; k < n; k += kRuleNT) score[lo + k] = NAN;
@@ -153,7 +224,8 @@ __device__ __forceinline__ void depcap_seq(int b, const float* __restrict__ kl,
     return;
   }
   if (W <= kDepWaveRows) {
-    depcap_window_wave(lo, W, R, kl, ent, lambda, l_min, eps, block_len + b, score, sm);
+    depcap_window_wave(lo, W, R, kl, ent, lambda, l_min, eps, block_len + b, score, sm, gI, gH,
+                       guess && lo == g0 && W == gw);
     return;
   }
   for (int k = threadIdx.x; k < W; k += kRuleNT) {

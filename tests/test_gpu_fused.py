@@ -237,6 +237,25 @@ def test_fused_dapd_bad_position_and_empty_sequence():
         assert int(host(f["dapd"][0][:40]).sum()) == 0
 
 
+@pytest.mark.parametrize("lens", [[10, 30, 20, 20], [20, 20, 20, 20], [0, 40, 0, 40]])
+def test_fused_rules_when_row_guesses_hold_or_fail(lens):
+    # the fused step reads each sequence's rows with its offsets when every
+    # sequence would have n_rows / n_seq rows, and again when the offsets
+    # say otherwise: 80 rows in 4 sequences, equal or not; every rule bitwise
+    # its entry point's, statistics against the oracle
+    spec = synth.Spec("guess", 31, 4, 20, 1500, torch.bfloat16, 2.0, 0.6, 12.0, 0.5, n_lh=2,
+                      seq_len=48, attn_sigma=2.0)
+    cur, prev, _, ri = synth.logits(spec, DEV)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), device=DEV, dtype=torch.int32)
+    n = int(sum(lens))
+    el = (torch.arange(n, device=DEV) % 3 != 0).to(torch.uint8)
+    for eligible in (el, None):
+        _check(cur, prev, offs, ri, fast=dict(eligible=eligible, tau=0.8),
+               depcap=dict(lam=1.2, l_min=4, l_max=16),
+               cap=dict(eligible=eligible, tau_low=0.5, tau_high=0.95, gamma=-16.0, k_max=16),
+               tag=f"lengths {lens}, eligible {eligible is not None}")
+
+
 def test_fused_dapd_short_sequences_at_the_one_workgroup_limit():
     # with m_max <= 64 one launch-2 workgroup scores and decides each
     # sequence: lengths 64 (the limit), 1, 0, 17 and 65 (longer than m_max:
