@@ -341,7 +341,8 @@ int dlm_fixed_block_eligible(const int32_t* masked_pos, const int32_t* seq_offse
  *   launch 2: Fast-dLLM, the DepCap boundary, CAP and the DAPD scores, each
  *             part in its own workgroups; the last scores workgroup of a
  *             sequence to finish (a per-sequence counter in the DAPD
- *             workspace, zeroed by launch 1) runs its DAPD selection.
+ *             workspace, zeroed by launch 1) runs its DAPD selection.  With
+ *             m_max <= 64, one workgroup per sequence scores and selects.
  * Each part computes what its own entry point computes.  The statistics are
  * those of dlm_step_stats to its stated accuracy (argmax identical; the
  * streaming order differs, so the floats may differ in the last bits), and
