@@ -256,6 +256,40 @@ def test_fused_rules_when_row_guesses_hold_or_fail(lens):
                tag=f"lengths {lens}, eligible {eligible is not None}")
 
 
+def test_fused_guessed_rows_over_several_batches():
+    # 6 sequences of 300 rows: the guess holds, and Fast-dLLM's guessed first
+    # batch of 256 rows is followed by a second batch read as usual; DepCap's
+    # window (l_max 200) is guessed too
+    spec = synth.Spec("batches", 43, 6, 300, 900, torch.bfloat16, 2.0, 0.6, 12.0, 0.5)
+    cur, prev, so, ri = synth.logits(spec, DEV)
+    n = spec.n_rows
+    el = (torch.arange(n, device=DEV) % 5 != 1).to(torch.uint8)
+    for tau in (0.5, 0.99):
+        _check(cur, prev, so, ri, fast=dict(eligible=el, tau=tau),
+               depcap=dict(lam=1.0, l_min=4, l_max=200), tag=f"6 x 300 rows, tau {tau}")
+
+
+def test_fused_dapd_many_short_sequences():
+    # 40 sequences of 0-64 masked rows (m_max 64): one launch-2 workgroup per
+    # sequence scores and selects; edge-rich and sparse thresholds
+    g = np.random.default_rng(47)
+    lens = g.integers(0, 65, size=40)
+    lens[3], lens[7] = 64, 0
+    spec = synth.Spec("many", 47, 40, 64, 600, torch.float32, 2.0, 0.6, 12.0, None, n_lh=2,
+                      seq_len=72, attn_sigma=2.5, attn_dtype=torch.float32)
+    cur, _, _, _ = synth.logits(spec, DEV)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), device=DEV, dtype=torch.int32)
+    masked = torch.cat([torch.from_numpy(np.sort(g.choice(72, size=int(m), replace=False)))
+                        for m in lens]).to(DEV, torch.int32)
+    ri = torch.cat([torch.arange(b * 64, b * 64 + int(m)) for b, m in enumerate(lens)]).to(DEV)
+    attn = synth.attention(spec, DEV)
+    for tau in (0.005, 0.05):
+        f = _check(cur, None, offs, ri, dapd=dict(attn=attn, masked_pos=masked, m_max=64, tau=tau),
+                   tag=f"40 short sequences, tau {tau}")
+        n = host(f["dapd"][1]).numpy()
+        assert (n[lens > 0] > 0).all() and (n[lens == 0] == 0).all(), n
+
+
 def test_fused_dapd_short_sequences_at_the_one_workgroup_limit():
     # with m_max <= 64 one launch-2 workgroup scores and decides each
     # sequence: lengths 64 (the limit), 1, 0, 17 and 65 (longer than m_max:
