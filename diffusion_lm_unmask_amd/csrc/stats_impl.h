@@ -10,11 +10,13 @@
 //  * one workgroup per row; each lane owns 16-byte chunks tid, tid+NT, ...
 //    so every wave load is a contiguous 1 KiB (global_load_dwordx4);
 //  * a lane processes U chunks per segment: segment maxima first, then one
-//    exp2 per element, t = x*log2(e) - h, with the lane reference
-//    h = ceil(max*log2(e)) an integer, so a rescale of the running sums when
-//    the max grows is an exact power of two (ldexp) and adds no rounding;
+//    exp2 per element, t = x*log2(e) - h, with the lane reference h an
+//    integer (ceil(max*log2(e)) when it is set), so a rescale of the running
+//    sums is an exact power of two (ldexp) and adds no rounding; the
+//    reference trails the max and moves only once the max passes it by a
+//    margin, so most chunks skip the rescale;
 //  * the previous step's row is summed against the same reference, so KL
-//    needs no second maximum: KL = B/Z + log(Z2/Z);
+//    needs no second maximum: KL = ln 2 * (B/Z + log2(Z2/Z));
 //  * sums are fp32 per segment and per lane; lanes are combined exactly
 //    (ldexp) in fp64 relative to the row's integer reference, and the
 //    fractional offset between that reference and the row max is applied
@@ -83,9 +85,12 @@ constexpr int stats_unroll() {
 }
 // Whether a workgroup of NT threads keeps two segments in flight (the
 // statistics block's PING form): bf16 rows outside the 768-thread shape.
+#ifndef DLM_STATS_PING_768
+#define DLM_STATS_PING_768 0
+#endif
 template <int NT, bool BF16>
 constexpr bool stats_ping() {
-  return BF16 && NT != 768;
+  return BF16 && (NT != 768 || DLM_STATS_PING_768);
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -134,19 +139,28 @@ __device__ __forceinline__ float elem_of(const uint4 q, int k) {
   }
 }
 
-// Per-lane running state.  Both rows' sums use the current row's reference
-// h = ceil(m * log2 e) (m = the lane's running max of the current row): the
-// previous row only needs sum 2^(y*log2e - h), and KL = B/Z + log(Z2/Z) then
-// involves no reference at all.  A previous row far above or below the
-// current one overflows or underflows Z2 and is sent to the element-wise path.
+// Per-lane running state.  Both rows' sums use the current row's integer
+// reference h (at most ceil(m * log2 e), m the lane's running max of the
+// current row): the previous row only needs sum 2^(t_y), t_y = y*log2e - h,
+// and KL = ln 2 * (B/Z + log2(Z2/Z)) then involves no reference at all.  A
+// previous row far above or below the current one overflows or underflows Z2
+// and is sent to the element-wise path.
 struct LaneState {
   float m, h;       // running max of the current row, integer reference
-  float Z, A, B;    // sum e, sum e*t (log2 units), sum e*(x - y)
-  float Z2;         // sum 2^(y*log2e - h)
+  float thr;        // the reference moves once the max passes this value
+  float Z, A, B;    // sum e, sum e*t, sum e*(t - t_y) (log2 units)
+  float Z2;         // sum 2^(t_y)
   int best;         // first element index of the chunk holding the lane max
   int bestw;        // width of that chunk (VEC, or 1 for a tail element)
   uint4 bq;         // raw bits of that chunk (VEC > 1)
 };
+
+// The reference trails the running max: it is moved to ceil(m * log2 e) only
+// once the max exceeds it by more than kSlack (log2 units), so every term has
+// t = x*log2e - h <= kSlack (2^t at most 2^kSlack: no overflow) while the
+// rescale, which costs ten instructions, is skipped on almost every chunk.
+constexpr float kSlack = 8.f;
+constexpr float kLn2f = 0.69314718f;  // ln 2 in fp32
 
 // Fold NSUB sub-blocks of W values into the lane state, in two parts.
 // fold_head: the sub-blocks' maxima, the first-strict-increase chunk record
@@ -161,36 +175,45 @@ __device__ __forceinline__ void fold_head(LaneState& c, const float (*x)[W], con
   float mr = c.m;
 #pragma unroll
   for (int u = 0; u < NSUB; ++u) {
-    float cm = x[u][0];
+    if (!valid[u]) continue;
+    float mn = mr;
 #pragma unroll
-    for (int k = 1; k < W; ++k) cm = fmaxf(cm, x[u][k]);
-    if (valid[u]) {
-      if (cm > mr) {
-        c.best = start[u];
-        c.bestw = W;
-        if constexpr (W > 1) c.bq = qc[u];
-      }
-      mr = fmaxf(mr, cm);
+    for (int k = 0; k < W; ++k) mn = fmaxf(mn, x[u][k]);
+    if (mn > mr) {  // the running max grew strictly in this sub-block
+      c.best = start[u];
+      c.bestw = W;
+      if constexpr (W > 1) c.bq = qc[u];
     }
+    mr = mn;
   }
-  // rescale running sums to the new integer reference (exact: a power of two)
-  const float hn = ceilf(mr * kL2E);
-  const float dh = c.h - hn;  // integer <= 0 (or a huge negative from the sentinel)
-  const int di = static_cast<int>(fmaxf(dh, -256.f));
-  c.A = ldexpf(fmaf(dh, c.Z, c.A), di);
-  c.Z = ldexpf(c.Z, di);
-  if constexpr (PREV) {
-    c.B = ldexpf(c.B, di);
-    c.Z2 = ldexpf(c.Z2, di);
-  }
-  c.h = hn;
   c.m = mr;
+  // Move the reference when the max has passed it by more than kSlack: an
+  // exact power-of-two rescale of the running sums.  The wave takes the
+  // branch together (a lane that does not need it rescales to its own
+  // ceil(m * log2e), which is as exact).
+  if (__builtin_amdgcn_ballot_w64(mr > c.thr) != 0) {
+    const float hn = ceilf(mr * kL2E);
+    const float dh = c.h - hn;  // integer <= 0 (or a huge negative from the sentinel)
+    const int di = static_cast<int>(fmaxf(dh, -256.f));
+    c.A = ldexpf(fmaf(dh, c.Z, c.A), di);
+    c.Z = ldexpf(c.Z, di);
+    if constexpr (PREV) {
+      c.B = ldexpf(c.B, di);
+      c.Z2 = ldexpf(c.Z2, di);
+    }
+    c.h = hn;
+    c.thr = (hn + kSlack) * kLn2f;
+  }
 }
 template <int NSUB, int W, bool BF16, bool PREV>
 __device__ __forceinline__ void fold_tail(LaneState& c, const float (*x)[W],
                                           const float (*yf)[W], const uint4* qp,
                                           const float* ys, const bool* valid) {
-  float z = 0.f, a = 0.f, b = 0.f, z2 = 0.f;
+  // sum e*(t - t_y) is taken as sum e*t - sum e*t_y per call: t_y is needed
+  // for the previous row's exponential anyway, and equal rows give bitwise
+  // equal sums (B = 0 exactly).  The sums start at -0.0, the identity of the
+  // addition, so the first term needs no add.
+  float z = -0.f, a = -0.f, ay = -0.f, z2 = -0.f;
 #pragma unroll
   for (int u = 0; u < NSUB; ++u) {
     if (!valid[u]) continue;
@@ -202,15 +225,16 @@ __device__ __forceinline__ void fold_tail(LaneState& c, const float (*x)[W],
       a = fmaf(e, t, a);
       if constexpr (PREV) {
         const float y = yf ? yf[u][k] : ys ? ys[u * W + k] : elem_of<BF16>(qp[u], k);
-        b = fmaf(e, x[u][k] - y, b);
-        z2 += ex2(fmaf(y, kL2E, -c.h));
+        const float ty = fmaf(y, kL2E, -c.h);
+        ay = fmaf(e, ty, ay);
+        z2 += ex2(ty);
       }
     }
   }
   c.Z += z;
   c.A += a;
   if constexpr (PREV) {
-    c.B += b;
+    c.B += a - ay;
     c.Z2 += z2;
   }
 }
@@ -492,7 +516,7 @@ __device__ __forceinline__ bool finalize(const StatsArgs& p, int64_t r, const Pa
   p.lse[r] = static_cast<float>(static_cast<double>(M) + kLN2 * (l2z + cM));
   p.conf[r] = static_cast<float>(static_cast<double>(exp2f(static_cast<float>(-cM))) * iz);
   p.ent[r] = static_cast<float>(kLN2 * (l2z - t.A * iz));
-  if constexpr (PREV) p.kl[r] = static_cast<float>(t.B * iz + kLN2 * log2_split(t.Z2 * iz));
+  if constexpr (PREV) p.kl[r] = static_cast<float>(kLN2 * (t.B * iz + log2_split(t.Z2 * iz)));
   return true;
 }
 
@@ -542,8 +566,8 @@ __device__ __forceinline__ void stats_block(const StatsArgs& p, int64_t r, int s
   constexpr int64_t SEG = static_cast<int64_t>(U) * NT;
   const int64_t n_full = n_c / SEG;
 
-  LaneState c{kLow, kLow * kL2E, 0.f, 0.f, 0.f, 0.f, -1, VEC, make_uint4(0u, 0u, 0u, 0u)};
-  // (the sentinel's h is integral)
+  // (the sentinel's h is integral; any finite max passes thr and sets h)
+  LaneState c{kLow, kLow * kL2E, kLow, 0.f, 0.f, 0.f, 0.f, -1, VEC, make_uint4(0u, 0u, 0u, 0u)};
   bool allv[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) allv[u] = true;
