@@ -287,3 +287,65 @@ def test_thread_counts_at_the_compute_unit_count(extra):
     for k in ("conf", "argmax", "entropy", "kl", "lse"):
         assert torch.equal(fused[k].view(torch.int32), solo[k].view(torch.int32)), k
         assert torch.equal(out[k].view(torch.int32), solo[k].view(torch.int32)), k
+
+
+# Rows that move the lane reference: it trails the running max and moves
+# (an exact power-of-two rescale) only once the max passes it by a margin, so
+# rows whose max keeps rising across a lane's chunks, or jumps in the last
+# chunk, rescale many times or late.  Kinds (r % 6):
+#   0  rising ramp, 60 nats over the row (the max rises in every chunk)
+#   1  falling ramp (the max sits in the first chunk)
+#   2  N(0, 2) with a +40 spike on the last element (a rescale in the tail)
+#   3  N(0, 2) with the first half of the vocabulary at -inf (masked)
+#   4  sawtooth, 30 nats per 4096-element period
+#   5  rising ramp, 200 nats over the row (rescales far apart in value)
+# prev is cur plus N(0, 0.5) noise on every row.
+def _trailing_reference_rows(n_rows, V, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    v = torch.arange(V, dtype=torch.float64)
+    x = torch.empty(n_rows, V, dtype=torch.float64)
+    for r in range(n_rows):
+        k = r % 6
+        if k == 0:
+            x[r] = 60.0 * v / V - 20.0
+        elif k == 1:
+            x[r] = 40.0 - 60.0 * v / V
+        elif k == 2:
+            x[r] = torch.randn(V, generator=g, dtype=torch.float64) * 2.0
+            x[r, V - 1] = 40.0
+        elif k == 3:
+            x[r] = torch.randn(V, generator=g, dtype=torch.float64) * 2.0
+            x[r, : V // 2] = float("-inf")
+        elif k == 4:
+            x[r] = 30.0 * torch.remainder(v, 4096.0) / 4096.0
+        else:
+            x[r] = 200.0 * v / V - 100.0
+    prev = x + torch.randn(n_rows, V, generator=g, dtype=torch.float64) * 0.5
+    return x.to(dtype).to(DEV), prev.to(dtype).to(DEV)
+
+
+@pytest.mark.parametrize("rows,vocab,dtype,with_prev,split", [
+    (256, 126464, torch.bfloat16, True, False),   # 768-thread rows (the LLaDA shape)
+    (300, 20011, torch.bfloat16, True, False),    # 512 threads, two segments in flight
+    (300, 20011, torch.bfloat16, False, False),   # the same without a previous row
+    (4096, 3001, torch.bfloat16, True, False),    # 256-thread rows
+    (64, 20011, torch.float32, True, False),      # fp32 chunks
+    (64, 20011, torch.float32, True, True),       # fp32 rows split over workgroups
+    (12, 126464, torch.bfloat16, True, True),     # bf16 rows split over workgroups
+])
+def test_rows_that_move_the_lane_reference(rows, vocab, dtype, with_prev, split):
+    cur, prev = _trailing_reference_rows(rows, vocab, dtype, seed=rows * 7 + vocab)
+    prev = prev if with_prev else None
+    tag = f"{rows} x {vocab} {dtype} prev={with_prev} split={split} "
+    out = api.step_stats(cur, prev, split=split)
+    torch.cuda.synchronize()
+    ref = oracle.step_stats(host(cur), host(prev) if prev is not None else None)
+    for k in ("conf", "entropy", "lse") + (("kl",) if with_prev else ()):
+        assert_close(out[k], ref[k], f"{tag}{k}")
+    assert np.array_equal(host(out["argmax"]).numpy(), ref["argmax"]), f"{tag}argmax"
+    if with_prev and not split:
+        # the fused step's launch 1 runs the same kernel: bitwise equal
+        fused = api.decide_step(cur, prev)
+        torch.cuda.synchronize()
+        for k in ("conf", "argmax", "entropy", "kl", "lse"):
+            assert torch.equal(fused[k].view(torch.int32), out[k].view(torch.int32)), f"{tag}{k}"
