@@ -164,8 +164,9 @@ constexpr float kLn2f = 0.69314718f;  // ln 2 in fp32
 
 // Fold NSUB sub-blocks of W values into the lane state, in two parts.
 // fold_head: the sub-blocks' maxima, the first-strict-increase chunk record
-// (qc holds the raw chunks, unused for W == 1) and the exact power-of-two
-// rescale of the running sums to the new integer reference.  fold_tail: the
+// (qc holds the raw chunks, unused for W == 1) and, once the max has passed
+// the reference by more than kSlack, the exact power-of-two rescale of the
+// running sums to a new integer reference.  fold_tail: the
 // sums; the previous row's values come from yf (unpacked), else ys (one
 // value per sub-block), else the raw chunks qp.  `valid` masks whole
 // sub-blocks; start[u] is the element index of sub-block u.
