@@ -669,9 +669,17 @@ __device__ __forceinline__ void stats_block(const StatsArgs& p, int64_t r, int s
         qc[u] = load16(cur4 + ch);
         if constexpr (PREV) qp[u] = load16(prv4 + ch);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     fold<U, VEC, BF16, PREV>(c, x, xq, yq, nullptr, allv, st);
+    // 768-thread rows: from the end of the fold until the next loads are
+    // issued the wave runs at a raised priority, so when its segment arrives
+    // it moves the chunk and issues the next loads ahead of the other waves'
+    // folds on its SIMD (the memory stream waits less).  Same-process A/B,
+    // bitwise-equal outputs: 22.20-22.27 against 22.30-22.48 us.
+    if constexpr (NT == 768) __builtin_amdgcn_s_setprio(3);
   }
+  __builtin_amdgcn_s_setprio(0);
   // last, partial segment of this split
   if (n_full * SEG < n_c) {
     float x[U][VEC];
