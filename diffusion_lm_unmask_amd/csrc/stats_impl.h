@@ -67,7 +67,9 @@ __device__ __forceinline__ float ex2(float t) { return __builtin_amdgcn_exp2f(t)
 // one per compute unit: 768 (12 waves, three per SIMD), whose extra waves
 // overlap the fold's arithmetic (two exponentials per element pair) with the
 // loads better when each compute unit streams a single row; same-process A/B,
-// 256 x 126464 with prev: 21.9 against 22.5 us at 512 threads; without prev,
+// 256 x 126464 with prev: 21.9 against 22.5 us at 512 threads (and 832
+// threads, which leave no partial segment at this vocabulary, lose to the
+// uneven split of 13 waves over four SIMDs); without prev,
 // or with two or more rows per compute unit, 512 stays ahead (256 rows
 // without prev: 15.2 against 17.1 us).  Otherwise 512.  The statistics call
 // and the fused step's statistics-only launch share this rule, so their
@@ -595,8 +597,9 @@ __device__ __forceinline__ void stats_block(const StatsArgs& p, int64_t r, int s
     // waits).  Same-process A/B, bitwise-equal outputs: 2048 x 126464
     // without prev 78.1 against 80.5 us, 4096 x 151936 184.2 against 185.9,
     // 65536 x 126464 with prev 4786 against 4817, 1024 with prev 81.4
-    // against 82.5.  The 768-thread rows keep the single buffer: 22.5
-    // against 21.8 us, their arithmetic sets their pace.
+    // against 82.5.  The 768-thread rows keep the single buffer: there
+    // every form with a second segment in flight per wave measured slower
+    // (this one 22.5 against 21.8 us).
     uint4 ca[U], pa[U], cb[U], pb[U];
     auto issue = [&](uint4 (&qc2)[U], uint4 (&qp2)[U], int64_t it) {
 #pragma unroll
