@@ -95,12 +95,13 @@ static void row_max(const void* row, int dtype, int64_t V, double* m_out, int32_
   *idx_out = (int32_t)idx;
 }
 
-/* log-sum-exp of a row by the two-pass definition: m + log(sum exp(x - m)).
- * Any NaN entry, a +inf entry, or a row that is all -inf gives NaN. */
-static double row_lse(const void* row, int dtype, int64_t V, double m) {
+/* The row's log-normaliser relative to its max m: log(sum exp(x - m)), so
+ * that lse = m + row_logz(...) (the two-pass log-sum-exp).  Any NaN entry, a
+ * +inf entry, or a row that is all -inf gives NaN. */
+static double row_logz(const void* row, int dtype, int64_t V, double m) {
   double z = 0.0;
   for (int64_t v = 0; v < V; ++v) z += exp(elem(row, dtype, v) - m);
-  return m + log(z);
+  return log(z);
 }
 
 /*
@@ -123,22 +124,28 @@ static void stats_row(const void* cur, const void* prev, int dtype, int64_t V, d
   double m;
   int32_t idx;
   row_max(cur, dtype, V, &m, &idx);
-  double lse = row_lse(cur, dtype, V, m);
+  /* log p_v = (x_v - m) - logz.  The difference x_v - m is exact in double
+   * for fp32 and bf16 inputs; taking it before the normaliser keeps logz
+   * from being absorbed by a max of huge magnitude (m + logz == m once
+   * |m| > 2^52 logz), which x_v - lse would not. */
+  double logz = row_logz(cur, dtype, V, m);
+  double lse = m + logz;
   *argmax = idx;
   *lse_out = lse;
-  /* conf = max_v p_v = exp(m - lse) */
-  *conf = exp(m - lse);
+  /* conf = max_v p_v = exp((m - m) - logz) */
+  *conf = exp(-logz);
   if (isnan(lse)) { /* no distribution: every statistic is NaN */
+    *conf = NAN;
     *entropy = NAN;
     if (prev) *kl = NAN;
     return;
   }
-  /* H = -sum_v p_v log p_v with log p_v = x_v - lse */
+  /* H = -sum_v p_v log p_v */
   double h = 0.0;
   for (int64_t v = 0; v < V; ++v) {
     double x = elem(cur, dtype, v);
     if (x == -INFINITY) continue; /* p_v = 0 */
-    double lp = x - lse;
+    double lp = (x - m) - logz;
     h -= exp(lp) * lp;
   }
   *entropy = h;
@@ -146,12 +153,12 @@ static void stats_row(const void* cur, const void* prev, int dtype, int64_t V, d
   double mq;
   int32_t idxq;
   row_max(prev, dtype, V, &mq, &idxq);
-  double lseq = row_lse(prev, dtype, V, mq);
-  if (isnan(lse) || isnan(lseq)) {
+  double logzq = row_logz(prev, dtype, V, mq);
+  if (isnan(lse) || isnan(mq + logzq)) {
     *kl = NAN;
     return;
   }
-  /* KL = sum_v p_v (log p_v - log q_v), log q_v = x'_v - lse' */
+  /* KL = sum_v p_v (log p_v - log q_v), log q_v = (x'_v - m') - logz' */
   double d = 0.0;
   int infinite = 0;
   for (int64_t v = 0; v < V; ++v) {
@@ -162,8 +169,8 @@ static void stats_row(const void* cur, const void* prev, int dtype, int64_t V, d
       infinite = 1;
       continue;
     }
-    double lp = x - lse;
-    double lq = xq - lseq;
+    double lp = (x - m) - logz;
+    double lq = (xq - mq) - logzq;
     d += exp(lp) * (lp - lq);
   }
   *kl = infinite ? INFINITY : d;

@@ -33,6 +33,28 @@ def test_uniform_row_closed_form(oracle):
         assert out["kl"][0] == 0.0
 
 
+def test_closed_forms_at_extreme_magnitudes(oracle):
+    # The definitions do not depend on where the logits sit: a uniform row
+    # has conf 1/V and entropy log V whether its value is 0 or 3e38, and
+    # equal rows have KL 0.  At |x| near 3e38 the log-normaliser m + log z
+    # equals m in double, so log p must be formed as (x - m) - log z.
+    V = 4096
+    for dt in (torch.float32, torch.bfloat16):
+        for c in (3.0e38, -3.0e38, 1.0e20, -1.5e30):
+            row = torch.full((1, V), c, dtype=dt)
+            out = oracle.step_stats(row, prev=row.clone())
+            assert abs(out["conf"][0] - 1.0 / V) < 1e-15, (dt, c, out["conf"][0])
+            assert abs(out["entropy"][0] - math.log(V)) < 1e-9, (dt, c, out["entropy"][0])
+            assert out["kl"][0] == 0.0
+            x = float(row[0, 0])
+            assert out["lse"][0] == x + math.log(V)
+        # two entries 1 apart, far from zero: the two-point closed form
+        row = torch.full((1, V), float("-inf"), dtype=dt)
+        row[0, 7], row[0, 9] = 2.0e30, 2.0e30
+        out = oracle.step_stats(row)
+        assert abs(out["conf"][0] - 0.5) < 1e-15 and abs(out["entropy"][0] - math.log(2)) < 1e-15
+
+
 def test_one_hot_rows(oracle):
     V = 4096
     x = torch.zeros((2, V), dtype=torch.float32)
