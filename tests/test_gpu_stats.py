@@ -349,3 +349,40 @@ def test_rows_that_move_the_lane_reference(rows, vocab, dtype, with_prev, split)
         torch.cuda.synchronize()
         for k in ("conf", "argmax", "entropy", "kl", "lse"):
             assert torch.equal(fused[k].view(torch.int32), out[k].view(torch.int32)), f"{tag}{k}"
+
+
+# Finite logits of extreme size: near the bf16 limit, and below the fold's
+# running-max sentinel (-1e30).  Their exponents overflow the fold, so these
+# rows reach the element-wise path, which must still give the definitions'
+# values.  lse is stored in fp32, so it is compared to fp32 rounding of its
+# own size; everything else at 1e-5 absolute, argmax exactly.
+def _extreme_rows(V, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.empty(6, V, dtype=torch.float64)
+    x[0] = -3.0e38                                   # all equal, below the sentinel
+    x[1] = -2.0e38 - torch.rand(V, generator=g, dtype=torch.float64) * 1e38
+    x[2] = 3.0e38                                    # all equal, near the top of the range
+    x[3] = torch.randn(V, generator=g, dtype=torch.float64) * 2.0
+    x[3, V // 3] = 1.0e30                            # one huge finite entry
+    x[4] = -1.5e30 + torch.randn(V, generator=g, dtype=torch.float64) * 1e28
+    x[5] = torch.randn(V, generator=g, dtype=torch.float64) * 1e20
+    return x.to(dtype).to(DEV)
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 126464), (torch.float32, 4099)])
+def test_extreme_finite_logits(dtype, V):
+    cur = _extreme_rows(V, dtype, seed=V)
+    for prev in (None, cur):
+        tag = f"extreme {dtype} V={V} prev={'cur' if prev is not None else 'none'} "
+        out = api.step_stats(cur, prev, split=False)
+        torch.cuda.synchronize()
+        ref = oracle.step_stats(host(cur), host(prev) if prev is not None else None)
+        for k in ("conf", "entropy") + (("kl",) if prev is not None else ()):
+            assert_close(out[k], ref[k], f"{tag}{k}")
+        lse_g = host(out["lse"]).double().numpy()
+        lse_o = np.asarray(ref["lse"], np.float64)
+        tol = np.maximum(1e-5, np.abs(lse_o) * 2.0 ** -23)
+        assert np.all(np.abs(lse_g - lse_o) <= tol), (tag, lse_g, lse_o)
+        assert np.array_equal(host(out["argmax"]).numpy(), ref["argmax"]), f"{tag}argmax"
+        if prev is not None:
+            assert np.all(host(out["kl"]).numpy() == 0.0), f"{tag}KL with prev == cur"
