@@ -540,3 +540,58 @@ def test_binding_rejects_mismatched_lengths():
         with pytest.raises(DLMError):
             call()
             pytest.fail(f"case {k} was accepted")
+
+
+@pytest.mark.parametrize("radius,eps", [(0, 1e-12), (1, 1e-12), (2, 0.0), (5, 1e-6)])
+def test_depcap_non_finite_statistics(radius, eps):
+    # statistics the rule can receive from non-finite logits: KL = +inf (a
+    # previous logit of -inf where the current one is finite), KL or entropy
+    # NaN (a NaN logit).  Every sum here adds non-negative terms, so an inf
+    # stays inf and a NaN stays NaN on both sides; the boundaries must be the
+    # oracle's exactly and the scores equal where finite, NaN where NaN
+    n_per, n_seq = 40, 6
+    g = np.random.default_rng(77 + radius)
+    kl = g.exponential(0.3, n_per * n_seq).astype(np.float32)
+    h = g.uniform(0.0, 3.0, n_per * n_seq).astype(np.float32)
+    kl[0 * n_per + 5] = np.inf
+    kl[1 * n_per + 10] = np.nan
+    h[2 * n_per + 3] = np.nan
+    kl[3 * n_per + 2] = np.inf
+    kl[3 * n_per + 20] = np.inf
+    kl[4 * n_per + 7] = np.inf
+    kl[4 * n_per + 9] = np.nan
+    so_h = np.arange(0, n_per * (n_seq + 1), n_per, dtype=np.int32)
+    kl_g, h_g = torch.from_numpy(kl).to(DEV), torch.from_numpy(h).to(DEV)
+    so = torch.from_numpy(so_h).to(DEV)
+    L, S = api.depcap_boundary(kl_g, h_g, so, lam=1.2, l_min=4, l_max=32, radius=radius, eps=eps)
+    torch.cuda.synchronize()
+    ref, Sref = oracle.depcap_boundary(kl.astype(np.float64), h.astype(np.float64), so_h, 32, 4,
+                                       1.2, radius=radius, eps=eps)
+    assert host(L).tolist() == list(ref), (host(L).tolist(), list(ref))
+    assert_close(S, Sref, f"non-finite S r={radius} eps={eps}")
+
+
+def test_depcap_on_non_finite_logits_in_the_fused_step():
+    # end to end through the fused step: a previous logit of -inf on the
+    # current row's argmax gives KL = +inf, a NaN logit gives NaN statistics;
+    # the step's block lengths and scores against the oracle's statistics fed
+    # to the oracle's rule
+    n_per, n_seq, V = 40, 4, 2000
+    g = torch.Generator().manual_seed(99)
+    cur = torch.randn(n_per * n_seq, V, generator=g) * 2.0
+    prev = cur + torch.randn(n_per * n_seq, V, generator=g) * 0.5
+    am = cur.argmax(dim=1)
+    prev[5, am[5]] = float("-inf")
+    prev[n_per + 12, am[n_per + 12]] = float("-inf")
+    cur[2 * n_per + 3, 17] = float("nan")
+    prev[3 * n_per + 8, 100] = float("nan")
+    cur, prev = cur.to(torch.bfloat16).to(DEV), prev.to(torch.bfloat16).to(DEV)
+    so = torch.arange(0, n_per * (n_seq + 1), n_per, dtype=torch.int32, device=DEV)
+    out = api.decide_step(cur, prev, so, depcap=dict(lam=1.2, l_min=4, l_max=32))
+    torch.cuda.synchronize()
+    st = oracle.step_stats(host(cur), host(prev))
+    assert np.isinf(st["kl"][5]) and np.isinf(st["kl"][n_per + 12])
+    assert np.isnan(st["entropy"][2 * n_per + 3]) and np.isnan(st["kl"][3 * n_per + 8])
+    ref, Sref = oracle.depcap_boundary(st["kl"], st["entropy"], host(so).numpy(), 32, 4, 1.2)
+    assert host(out["depcap"][0]).tolist() == list(ref)
+    assert_close(out["depcap"][1], Sref, "fused non-finite S")
