@@ -595,3 +595,30 @@ def test_depcap_on_non_finite_logits_in_the_fused_step():
     ref, Sref = oracle.depcap_boundary(st["kl"], st["entropy"], host(so).numpy(), 32, 4, 1.2)
     assert host(out["depcap"][0]).tolist() == list(ref)
     assert_close(out["depcap"][1], Sref, "fused non-finite S")
+
+
+@pytest.mark.parametrize("rows", [32, 100])
+def test_dapd_nan_attention(rows):
+    # a NaN attention entry between two masked positions, in one map or in
+    # every map: their averaged score is NaN on both sides, which is no edge,
+    # and the proxy degree that sums it is NaN, so both nodes get NaN keys
+    # and are never chosen.  The single-wave path (32 rows) and the
+    # workgroup path (100 rows), against the oracle
+    spec = synth.Spec(f"nanattn{rows}", 5 + rows, 1, rows, 4096, torch.float32, 2.0, 0.6, 12.0,
+                      None, n_lh=4, seq_len=rows + 8, attn_sigma=2.0,
+                      attn_dtype=torch.float32)
+    cur, _, so, ri = synth.logits(spec, DEV)
+    g = api.step_stats(cur)
+    torch.cuda.synchronize()
+    o = oracle.step_stats(host(cur))
+    attn = synth.attention(spec, DEV)
+    pos, offs = synth.gen_positions(spec, DEV)
+    p = host(pos).tolist()
+    attn[0, 1, p[4], p[9]] = float("nan")
+    attn[0, :, p[20], p[21]] = float("nan")
+    for tau in (0.005, 0.02):
+        out = _dapd_case(attn, pos, offs, g["conf"], np.asarray(o["conf"]), tau, rows,
+                         f"nan attention rows={rows} tau={tau}")
+        deg = f64(out["degree"])
+        assert np.isnan(deg[[4, 9, 20, 21]]).all()
+        assert host(out["commit"])[[4, 9, 20, 21]].sum() == 0
