@@ -622,3 +622,24 @@ def test_dapd_nan_attention(rows):
         deg = f64(out["degree"])
         assert np.isnan(deg[[4, 9, 20, 21]]).all()
         assert host(out["commit"])[[4, 9, 20, 21]].sum() == 0
+
+
+def test_cap_with_masked_vocabulary_entries():
+    # a row whose logit is -inf at another candidate's argmax token (a masked
+    # vocabulary entry): log p_i(y_j) = -inf, so D_ij = -inf, which is no
+    # conflict; D must be -inf at exactly the oracle's pairs and the commits
+    # the oracle's.  The whole LLaDA generation as one pool (K_max 128) on
+    # the covariance variant, where candidates do conflict
+    cur, _, so, ri = synth.logits("llada", DEV, variant="cov", batch=BATCH.get("llada"))
+    am = cur.float().argmax(dim=1)
+    n = cur.shape[0]
+    for r in range(0, n - 1, 3):
+        if am[r + 1] != am[r]:
+            cur[r, am[r + 1]] = float("-inf")
+    g = api.step_stats(cur)
+    torch.cuda.synchronize()
+    o = oracle.step_stats(host(cur))
+    R = dict(synth.RULES["llada"], k_max=128, tau_low=0.5)
+    out = _cap_case(cur, ri, so, g, o, R, None, "llada/cov masked vocabulary")
+    D = f64(out["dmat"])[0]
+    assert np.isneginf(D).any(), "no -inf conflict score among the candidates"
