@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from _parity import assert_close, host
+from _parity import assert_close, f64, host
 from diffusion_lm_unmask_amd import api, synth
 
 pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("poisoned_outputs")]
@@ -365,3 +365,28 @@ def test_null_row_index_is_the_identity(name):
     for k in ("commit", "n_commit", "cand", "dmat"):
         _same(c1[k], c2[k], f"{name} cap {k}")
     assert int(host(c1["cand"][0] >= 0).sum()) > 1      # several candidates gathered
+
+
+def test_fused_thousands_of_tiny_sequences():
+    # 3000 sequences of 2 masked rows (6000 rows, a ragged 257-token
+    # vocabulary, with the previous step): every role launches one workgroup
+    # per sequence (or per block of rows), far more workgroups than compute
+    # units.  Every rule bitwise equal to its entry point, the statistics
+    # against the oracle, and Fast-dLLM and DepCap decisions the oracle's rule
+    # on the fused statistics
+    B, rows, V = 3000, 2, 257
+    spec = synth.Spec("tinyseqs", 31, B, rows, V, torch.bfloat16, 2.0, 0.6, 12.0, 0.5, n_lh=2,
+                      seq_len=rows + 4, attn_sigma=2.0, attn_dtype=torch.bfloat16)
+    cur, prev, so, ri = synth.logits(spec, DEV)
+    pos, offs = synth.gen_positions(spec, DEV)
+    attn = synth.attention(spec, DEV)
+    parts = dict(fast=dict(eligible=None, tau=0.6),
+                 depcap=dict(lam=1.2, l_min=1, l_max=4),
+                 cap=dict(eligible=None, tau_low=0.3, tau_high=0.95, gamma=-16.0, k_max=2),
+                 dapd=dict(attn=attn, masked_pos=pos, m_max=rows, tau=0.02))
+    f = _check(cur, prev, offs, ri, **parts, tag="3000 sequences of 2 rows")
+    so_h = host(offs).numpy()
+    commit_o, _ = oracle.fastdllm_select(f64(f["conf"]), so_h, float(np.float32(0.6)), None)
+    assert np.array_equal(host(f["fast"][0]).numpy(), commit_o)
+    L_o, _ = oracle.depcap_boundary(f64(f["kl"]), f64(f["entropy"]), so_h, 4, 1, 1.2)
+    assert host(f["depcap"][0]).tolist() == list(L_o)
