@@ -643,3 +643,47 @@ def test_cap_with_masked_vocabulary_entries():
     out = _cap_case(cur, ri, so, g, o, R, None, "llada/cov masked vocabulary")
     D = f64(out["dmat"])[0]
     assert np.isneginf(D).any(), "no -inf conflict score among the candidates"
+
+
+@pytest.mark.parametrize("M,contiguous", [(100, True), (64, False)])
+def test_dapd_attention_beyond_2_31_elements(M, contiguous):
+    # one [1, 1, 50000, 50000] bf16 map (2.5e9 elements, 5 GB) whose masked
+    # positions sit at the end, so every read is past element 2^31.  Only the
+    # masked block is written (nothing else is read); the oracle takes that
+    # block compacted to positions 0..M-1, which defines the same graph.
+    # Contiguous positions take the vector loads, spread ones the scalar
+    # loads.  The fused step's tiles read the same maps: bitwise the call's
+    S = 50000
+    attn = torch.empty(1, 1, S, S, device=DEV, dtype=torch.bfloat16)
+    g = torch.Generator().manual_seed(M)
+    if contiguous:
+        pos_h = torch.arange(S - M, S, dtype=torch.int32)
+    else:
+        pos_h = (S - 1 - 97 * torch.arange(M - 1, -1, -1, dtype=torch.int32)).to(torch.int32)
+    block = torch.softmax(torch.randn(M, M, generator=g) * 3.0, dim=1).to(torch.bfloat16)
+    pos = pos_h.to(DEV)
+    attn[0, 0, pos.long()[:, None], pos.long()[None, :]] = block.to(DEV)
+    offs = torch.tensor([0, M], device=DEV, dtype=torch.int32)
+    conf_h = torch.rand(M, generator=g) * 0.5 + 0.5
+    conf = conf_h.to(DEV)
+    tau = 0.02
+    out = api.dapd_select(attn, pos, offs, conf, tau, m_max=M, want_degree=True,
+                          want_key=True, want_sym=True)
+    torch.cuda.synchronize()
+    ref = oracle.dapd_select(block[None, None].contiguous(), np.arange(M, dtype=np.int32),
+                             np.array([0, M], np.int32), conf_h.double().numpy(),
+                             float(np.float32(tau)), m_max=M)
+    assert_close(out["sym"], ref["sym"], f"2^31 M={M} sym")
+    assert_close(out["degree"], ref["degree"], f"2^31 M={M} degree")
+    t32 = float(np.float32(tau))
+    take = oracle.dapd_greedy(f64(out["sym"])[0][:M, :M], t32, f64(out["key"]))
+    assert np.array_equal(host(out["commit"]).numpy(), take), "decision-only"
+    assert np.array_equal(host(out["commit"]).numpy(), ref["commit"]), "end to end"
+    logits = torch.randn(M, 64, generator=g).to(torch.bfloat16).to(DEV)
+    st = api.step_stats(logits)
+    f = api.decide_step(logits, None, offs, dapd=dict(attn=attn, masked_pos=pos, m_max=M, tau=tau))
+    c = api.dapd_select(attn, pos, offs, st["conf"], tau, m_max=M)
+    torch.cuda.synchronize()
+    assert torch.equal(f["dapd"][0], c["commit"]) and torch.equal(f["dapd"][1], c["n_commit"])
+    del attn
+    torch.cuda.empty_cache()
