@@ -9,8 +9,10 @@
 
 namespace dlmh {
 
+// row_index may be NULL (row r itself); its values are not read on the host.
 inline int check_stats(const void* logits, const void* prev, int dtype, int64_t vocab,
-                       int64_t ld, const int64_t* row_index, int64_t n_rows, const void* conf,
+                       int64_t ld, [[maybe_unused]] const int64_t* row_index, int64_t n_rows,
+                       const void* conf,
                        const void* argmax, const void* entropy, const void* kl, const void* lse) {
   if (!logits || !conf || !argmax || !entropy || !lse) return DLM_ERR_ARG;
   if ((prev == nullptr) != (kl == nullptr)) return DLM_ERR_ARG;
@@ -42,7 +44,8 @@ inline int check_depcap(const void* kl, const void* entropy, const void* seq_off
 }
 
 inline int check_cap(const void* logits, int dtype, int64_t vocab, int64_t ld,
-                     const void* row_index, const void* seq_offsets, int32_t n_seq,
+                     [[maybe_unused]] const void* row_index, const void* seq_offsets,
+                     int32_t n_seq,
                      const void* conf, const void* argmax, const void* lse, float tau_low,
                      float tau_high, float gamma, int32_t k_max, const void* commit,
                      const void* n_commit) {
