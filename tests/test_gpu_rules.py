@@ -687,3 +687,45 @@ def test_dapd_attention_beyond_2_31_elements(M, contiguous):
     assert torch.equal(f["dapd"][0], c["commit"]) and torch.equal(f["dapd"][1], c["n_commit"])
     del attn
     torch.cuda.empty_cache()
+
+
+def test_rule_parameters_at_their_extremes():
+    # thresholds and weights at infinities and outside [0, 1]: the rules'
+    # comparisons must fall the same way on both sides (Fast-dLLM: tau -inf
+    # commits every eligible row, +inf only the fallback; DepCap: lambda
+    # negative or huge; CAP: gamma +-inf (every pair or no pair conflicts),
+    # every candidate forced or none, an empty pool; DAPD: tau 0 (every
+    # pair an edge: a complete graph), 1 and -1)
+    cur, prev, so, ri, g, o = _stats("llada", "cov")
+    n = cur.shape[0]
+    block = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    block[:64] = 1
+    for tau in (float("-inf"), float("inf"), 0.0, 1.0):
+        _fastdllm_case(g["conf"], o["conf"], so, tau, block, f"fast tau={tau}")
+    R = synth.RULES["llada"]
+    _depcap_case(g, o, so, dict(R, lam=-1.0), "depcap lam=-1")
+    # lambda 1e30: scores near -1e30, equal to fp64 rounding (relative), and
+    # the same boundaries
+    L_g, S_g = api.depcap_boundary(g["kl"], g["entropy"], so, lam=1e30, l_min=R["l_min"],
+                                   l_max=R["l_max"])
+    torch.cuda.synchronize()
+    L_o, S_o = oracle.depcap_boundary(f64(g["kl"]), f64(g["entropy"]), host(so).numpy(),
+                                      R["l_max"], R["l_min"], 1e30)
+    assert host(L_g).tolist() == list(L_o)
+    sg, so_ = f64(S_g), np.asarray(S_o)
+    fin = np.isfinite(so_)
+    assert np.array_equal(np.isnan(sg), np.isnan(so_))
+    assert np.all(np.abs(sg[fin] - so_[fin]) <= 1e-12 * np.abs(so_[fin]))
+    for gamma, t_high, t_low in ((float("-inf"), 0.95, 0.5), (float("inf"), 0.95, 0.5),
+                                 (-16.0, 0.0, 0.5), (-16.0, 2.0, 0.5), (-16.0, 0.95, 2.0),
+                                 (-16.0, 0.95, 0.0)):
+        _cap_case(cur, ri, so, g, o, dict(R, gamma=gamma, tau_high=t_high, tau_low=t_low,
+                                          k_max=64), None,
+                  f"cap gamma={gamma} tau_high={t_high} tau_low={t_low}")
+    attn = synth.attention("llada", DEV, batch=1)
+    pos, offs = synth.gen_positions("llada", DEV, batch=1)
+    for tau in (0.0, 1.0, -1.0):
+        out = _dapd_case(attn, pos, offs, g["conf"], np.asarray(o["conf"]), tau, n,
+                         f"dapd tau={tau}")
+        k = int(host(out["n_commit"])[0])
+        assert (k == 1) if tau <= 0.0 else (k == n), (tau, k)
