@@ -338,3 +338,68 @@ def test_every_rule_with_all_sequences_empty():
                            gen_len=host(gen_len).numpy())
     assert host(r["n_commit"]).tolist() == [0, 0, 0]
     assert np.array_equal(host(r["stage"]).numpy(), ref["stage"])
+
+
+def test_schedule_parameters_at_their_extremes():
+    # factor decoding with f <= 0 (no n satisfies the bound: the fallback),
+    # a tiny f, f = 1e30 and +inf (every eligible row); top-K with the largest
+    # k; a fixed block longer than any generation.  Bit-exact against the
+    # oracle, with the over-long sequence reported
+    so, conf, el = _inputs(19)
+    conf_g, so_g, el_g = (torch.from_numpy(x).to(DEV) for x in (conf, so, el))
+    for f in (0.0, -1.0, 1e-30, 1e30, float("inf")):
+        f32 = float(np.float32(f))
+        c_g, n_g, ce_g = (host(x).numpy() for x in api.factor_select(conf_g, so_g, f,
+                                                                      eligible=el_g))
+        c_o, n_o, ce_o = oracle.factor_select(conf.astype(np.float64), so, f32, eligible=el)
+        for b, m in enumerate(LENS):
+            lo, hi = so[b], so[b + 1]
+            if m > 1024:
+                continue
+            assert np.array_equal(c_g[lo:hi], c_o[lo:hi]), f"f={f} seq {b}"
+            assert n_g[b] == n_o[b] and ce_g[b] == ce_o[b], f"f={f} seq {b}"
+        _check_over_long(c_g, n_g, so)
+    k = 2 ** 31 - 1
+    c_g, n_g = (host(x).numpy() for x in api.topk_select(conf_g, so_g, k, eligible=el_g))
+    c_o, n_o = oracle.topk_select(conf.astype(np.float64), so, k, eligible=el)
+    for b, m in enumerate(LENS):
+        if m <= 1024:
+            lo, hi = so[b], so[b + 1]
+            assert np.array_equal(c_g[lo:hi], c_o[lo:hi]) and n_g[b] == n_o[b], f"k max seq {b}"
+    _check_over_long(c_g, n_g, so)
+    pos = np.concatenate([np.arange(m) * 3 + 7 for m in LENS]).astype(np.int32)
+    for L in (2 ** 30, 2 ** 31 - 1):
+        e_g = api.fixed_block_eligible(torch.from_numpy(pos).to(DEV), so_g, L)
+        e_o = oracle.fixed_block_eligible(pos, so, L)
+        assert np.array_equal(host(e_g).numpy(), e_o), L
+
+
+def test_dapd_step_policy_at_its_extremes():
+    # the late-stage switch and threshold at their limits: late_frac 0 or
+    # below (no sequence is late), 1, a large value and +inf (every sequence
+    # with masks left is late), late_tau -inf (every row passes), +inf (only
+    # the fallback) and 0.  Stage per sequence and commits against the oracle
+    spec = synth.Spec("scatx", 13, 3, 40, 512, torch.bfloat16, 2.0, 0.6, 12.0, None,
+                      n_lh=6, seq_len=100, attn_sigma=3.0)
+    attn = synth.attention(spec, DEV)
+    gen = torch.Generator().manual_seed(5)
+    pos = torch.cat([torch.randperm(100, generator=gen)[:40].sort().values for _ in range(3)])
+    pos = pos[:77].to(device=DEV, dtype=torch.int32).contiguous()
+    so = torch.tensor([0, 40, 40, 77], device=DEV, dtype=torch.int32)
+    conf = torch.rand(77, generator=gen).to(DEV)
+    conf[50] = 1.0
+    gen_len = torch.tensor([60, 10, 100], device=DEV, dtype=torch.int32)
+    so_h, conf_h = host(so).numpy(), host(conf).numpy().astype(np.float64)
+    for lf, lt in ((0.0, 0.9), (-1.0, 0.9), (1.0, 0.9), (1e30, 0.9), (float("inf"), 0.9),
+                   (float("inf"), float("-inf")), (float("inf"), float("inf")),
+                   (float("inf"), 0.0)):
+        out = api.dapd_step(attn, pos, so, conf, 0.02, gen_len=gen_len, late_frac=lf,
+                            late_tau=lt, m_max=45)
+        torch.cuda.synchronize()
+        ref = oracle.dapd_step(host(attn), host(pos).numpy(), so_h, conf_h,
+                               float(np.float32(0.02)), gen_len=host(gen_len).numpy(),
+                               late_frac=float(np.float32(lf)), late_tau=float(np.float32(lt)))
+        tag = f"late_frac={lf} late_tau={lt}"
+        assert np.array_equal(host(out["stage"]).numpy(), ref["stage"]), tag
+        assert np.array_equal(host(out["commit"]).numpy(), ref["commit"]), tag
+        assert np.array_equal(host(out["n_commit"]).numpy(), ref["n_commit"]), tag
