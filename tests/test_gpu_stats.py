@@ -386,3 +386,29 @@ def test_extreme_finite_logits(dtype, V):
         assert np.array_equal(host(out["argmax"]).numpy(), ref["argmax"]), f"{tag}argmax"
         if prev is not None:
             assert np.all(host(out["kl"]).numpy() == 0.0), f"{tag}KL with prev == cur"
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_non_finite_padding_beyond_a_ragged_vocabulary(dtype):
+    # rows padded past a vocabulary that is not a multiple of the 16-byte
+    # chunk, the padding holding NaN and +-inf: nothing past `vocab` may be
+    # read into the statistics (a leak would turn them NaN or inf), on the
+    # split, unsplit and fused paths
+    V, ld = 3001, 3024
+    g = torch.Generator().manual_seed(3001)
+    cur = torch.randn(40, ld, generator=g) * 2.0
+    prev = cur + torch.randn(40, ld, generator=g) * 0.5
+    cur[:, V:] = float("nan")
+    cur[::3, V + 1] = float("inf")
+    prev[:, V:] = float("-inf")
+    prev[1::3, V + 2] = float("nan")
+    cur, prev = cur.to(dtype).to(DEV), prev.to(dtype).to(DEV)
+    out, _ = _compare(cur, prev, vocab=V, tag="nan padding ")
+    _compare(cur, prev, vocab=V, tag="nan padding unsplit ", split=False)
+    for k in ("conf", "entropy", "kl", "lse"):
+        assert bool(torch.isfinite(out[k]).all()), k
+    fused = api.decide_step(cur, prev, vocab=V)
+    solo = api.step_stats(cur, prev, vocab=V, split=False)
+    torch.cuda.synchronize()
+    for k in ("conf", "argmax", "entropy", "kl", "lse"):
+        assert torch.equal(fused[k].view(torch.int32), solo[k].view(torch.int32)), k
