@@ -390,3 +390,42 @@ def test_fused_thousands_of_tiny_sequences():
     assert np.array_equal(host(f["fast"][0]).numpy(), commit_o)
     L_o, _ = oracle.depcap_boundary(f64(f["kl"]), f64(f["entropy"]), so_h, 4, 1, 1.2)
     assert host(f["depcap"][0]).tolist() == list(L_o)
+
+
+def test_two_streams_at_once_match_one_at_a_time():
+    # the library keeps no device state between calls other than the
+    # documented static DAPD workspace: two streams (default priority)
+    # running fused steps with every rule at the same time, each with its own
+    # inputs, outputs and workspaces, give bitwise the results of the same
+    # calls made one at a time
+    runs = []
+    for seed in (1, 2):
+        spec = synth.Spec(f"twostream{seed}", 40 + seed, 3, 48, 1500, torch.bfloat16, 2.0, 0.6,
+                          12.0, 0.5, n_lh=3, seq_len=56, attn_sigma=2.5)
+        cur, prev, so, ri = synth.logits(spec, DEV)
+        pos, offs = synth.gen_positions(spec, DEV)
+        attn = synth.attention(spec, DEV)
+        ws = torch.empty(api.dapd_workspace_bytes(3, 48), device=DEV, dtype=torch.uint8)
+        parts = dict(fast=dict(eligible=None, tau=0.7), depcap=dict(lam=1.2, l_min=2, l_max=32),
+                     cap=dict(eligible=None, tau_low=0.4, tau_high=0.95, gamma=-16.0, k_max=16),
+                     dapd=dict(attn=attn, masked_pos=pos, m_max=48, tau=0.02, workspace=ws))
+        runs.append((cur, prev, offs, parts))
+    torch.cuda.synchronize()
+    alone = []
+    for cur, prev, offs, parts in runs:
+        alone.append(api.decide_step(cur, prev, offs, **parts))
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=DEV) for _ in runs]
+    together = [None, None]
+    for rep in range(10):
+        for k, ((cur, prev, offs, parts), st) in enumerate(zip(runs, streams)):
+            with torch.cuda.stream(st):
+                together[k] = api.decide_step(cur, prev, offs, **parts)
+        torch.cuda.synchronize()
+        for a, t in zip(alone, together):
+            for key in ("conf", "argmax", "entropy", "kl", "lse"):
+                assert torch.equal(a[key].view(torch.int32), t[key].view(torch.int32)), key
+            for part in ("fast", "depcap", "cap", "dapd"):
+                for x, y in zip(a[part], t[part]):
+                    if x is not None:
+                        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), (rep, part)
