@@ -58,9 +58,16 @@ def _check(cur, prev, so, ri, fast=None, depcap=None, cap=None, dapd=None, tag="
         if g[k] is None:
             assert f[k] is None
             continue
-        # 1e-6 absolute plus two fp32 ulps of the value (lse reaches ~20)
+        # 1e-6 absolute plus two fp32 ulps of the value (lse reaches ~20).
+        # KL gets 3e-6: its numerator is formed per segment as
+        # sum e*t - sum e*t_y, whose terms carry |t| up to the lane
+        # reference's margin (8), so the fused step's four chunks per lane and
+        # the call's one or two sum in orders that differ by a few units of
+        # 8 * 2^-24 relative to Z (up to 1.6e-6 over 40 full-vocabulary
+        # seeds; both within 2.7e-6 of the oracle, whose bar is 1e-5)
+        bound = 3e-6 if k == "kl" else 1e-6
         d = float(((f[k].double() - g[k].double()).abs() - 2.4e-7 * g[k].double().abs()).max())
-        assert d <= 1e-6, f"{tag} {k}: fused and the statistics call differ by {d:.2e}"
+        assert d <= bound, f"{tag} {k}: fused and the statistics call differ by {d:.2e}"
     for part in ("fast", "depcap", "cap", "dapd"):
         if part in i:
             for x, y in zip(f[part], i[part]):
@@ -429,3 +436,32 @@ def test_two_streams_at_once_match_one_at_a_time():
                 for x, y in zip(a[part], t[part]):
                     if x is not None:
                         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), (rep, part)
+
+
+@pytest.mark.parametrize("seed", [30000, 30002, 30005, 30015, 30037, 30011])
+def test_fused_random_shapes_full_vocabulary(seed):
+    # random shapes at the workloads' vocabularies (126464, 151936 and two
+    # ragged ones), 1-300 rows per sequence: the 768- and 512-thread rows
+    # and the streaming launch at their real segment counts; every rule
+    # bitwise equal to its entry point, the statistics against the oracle
+    g = np.random.default_rng(seed)
+    B, rows = int(g.integers(1, 3)), int(g.integers(1, 301))
+    V = int((126464, 151936, 126467, 100003)[int(g.integers(0, 4))])
+    dt = (torch.bfloat16, torch.float32)[int(g.random() < 0.2)]
+    has_prev = bool(g.integers(0, 2))
+    spec = synth.Spec(f"big{seed}", seed, B, rows, V, dt, 2.0, float(g.uniform(0.2, 1.0)), 12.0,
+                      0.5 if has_prev else None, n_lh=int(g.integers(1, 5)),
+                      seq_len=rows + int(g.integers(0, 20)), attn_sigma=float(g.uniform(0.5, 3.0)))
+    cur, prev, so, ri = synth.logits(spec, DEV)
+    pos, offs = synth.gen_positions(spec, DEV)
+    attn = synth.attention(spec, DEV)
+    l_min = int(g.integers(1, 9))
+    parts = dict(
+        fast=dict(eligible=None, tau=float(g.uniform(0.3, 0.95))),
+        depcap=dict(lam=float(g.uniform(0.5, 2.0)), l_min=l_min,
+                    l_max=l_min + int(g.integers(0, 120))) if has_prev else None,
+        cap=dict(eligible=None, tau_low=float(g.uniform(0.2, 0.9)), tau_high=0.95, gamma=-16.0,
+                 k_max=int(g.integers(1, 129))),
+        dapd=dict(attn=attn, masked_pos=pos, m_max=rows,
+                  tau=float((0.005, 0.02)[int(g.integers(0, 2))])))
+    _check(cur, prev, offs, ri, **parts, tag=f"full-vocabulary seed {seed}: B {B} rows {rows} V {V}")
